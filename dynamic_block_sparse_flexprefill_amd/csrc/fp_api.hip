@@ -1,0 +1,210 @@
+// C-ABI layer of libfpattn: argument validation, workspace carving and the
+// launch sequence of each call.  No device memory is allocated here and no
+// call synchronises the stream.
+#include <math.h>
+#include <string.h>
+
+#include "fp_internal.hpp"
+
+namespace fp {
+
+static size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+int make_plan(const fp_shape *s, Plan *p) {
+  if (!s || !p) return FP_EINVAL;
+  if (s->S <= 0 || s->b <= 0 || s->Hq <= 0 || s->Hkv <= 0 || s->d <= 0) return FP_EINVAL;
+  if (s->S % s->b != 0 || s->Hq % s->Hkv != 0) return FP_EINVAL;
+  if (s->d != 128 || (s->b != 128 && s->b != 256)) return FP_EUNSUPPORTED;
+  const int N = s->S / s->b, G = s->Hq / s->Hkv;
+  if (N > 8192 || (int64_t)G * s->b > 2048) return FP_EUNSUPPORTED;
+  memset(p, 0, sizeof(*p));
+  p->S = s->S; p->B = s->b; p->Hq = s->Hq; p->Hkv = s->Hkv; p->d = s->d;
+  p->N = N; p->G = G;
+  p->nw32 = (N + 31) / 32;
+  // About two statistics workgroups per compute unit (256 CUs) in total.
+  int nch = (512 + s->Hkv - 1) / s->Hkv;
+  if (nch > N) nch = N;
+  if (nch < 1) nch = 1;
+  p->cpb = (N + nch - 1) / nch;
+  p->nch = (N + p->cpb - 1) / p->cpb;
+  size_t o = 0;
+  const size_t Hq = s->Hq, Hkv = s->Hkv, B = s->b;
+  p->off_part = o;   o = align_up(o + sizeof(float2) * Hq * B * p->nch);
+  p->off_rowml = o;  o = align_up(o + sizeof(float2) * Hq * B);
+  p->off_lo = o;     o = align_up(o + sizeof(float) * Hq * N);
+  p->off_hi = o;     o = align_up(o + sizeof(float) * Hq * N);
+  p->off_kbar = o;   o = align_up(o + sizeof(float) * Hkv * N * 128);
+  p->off_sel = o;    o = align_up(o + sizeof(uint32_t) * Hq * 2 * p->nw32);
+  p->off_qabits = o; o = align_up(o + sizeof(uint32_t) * Hq * (size_t)N * p->nw32);
+  p->off_jwork = o;  o = align_up(o + sizeof(int32_t) * Hkv * N);
+  p->total = o;
+  return FP_OK;
+}
+
+Work carve(const Plan &p, void *ws) {
+  char *b = (char *)ws;
+  Work w;
+  w.part = (float2 *)(b + p.off_part);
+  w.rowml = (float2 *)(b + p.off_rowml);
+  w.lo = (float *)(b + p.off_lo);
+  w.hi = (float *)(b + p.off_hi);
+  w.kbar = (float *)(b + p.off_kbar);
+  w.sel = (uint32_t *)(b + p.off_sel);
+  w.qabits = (uint32_t *)(b + p.off_qabits);
+  w.jwork = (int32_t *)(b + p.off_jwork);
+  return w;
+}
+
+}  // namespace fp
+
+using namespace fp;
+
+static int check_params(float gamma, float tau) {
+  if (!(gamma > 0.0f) || !(gamma <= 1.0f)) return FP_EINVAL;  // also rejects NaN
+  if (!(tau >= 0.0f)) return FP_EINVAL;
+  return FP_OK;
+}
+
+static int check_out(const Plan &p, const fp_index_out *o, bool need_pattern) {
+  if (!o || !o->row_ptr || !o->col_idx || !o->job_ptr || !o->job_blk || !o->job_mask ||
+      !o->job_order || !o->status)
+    return FP_EINVAL;
+  if (need_pattern && (!o->pattern || !o->jsd)) return FP_EINVAL;
+  if (o->col_cap < (int64_t)p.Hq * p.N || o->job_cap < (int64_t)p.Hkv * p.N) return FP_EINVAL;
+  if (o->col_cap > INT32_MAX || o->job_cap > INT32_MAX) return FP_EINVAL;
+  return FP_OK;
+}
+
+#define FP_LAUNCH(call)                          \
+  do {                                           \
+    if ((call) != hipSuccess) return FP_EHIP;    \
+  } while (0)
+
+extern "C" {
+
+int fp_version(void) { return 100; }
+
+const char *fp_strerror(int code) {
+  switch (code) {
+    case FP_OK: return "ok";
+    case FP_EINVAL: return "invalid argument (null pointer, S % b != 0, Hq % Hkv != 0, gamma not in (0,1], tau < 0 or NaN, or a capacity below one entry per row)";
+    case FP_EUNSUPPORTED: return "unsupported shape (needs d = 128, b in {128, 256}, S/b <= 8192, (Hq/Hkv)*b <= 2048)";
+    case FP_EWORKSPACE: return "workspace smaller than fp_workspace_bytes()";
+    case FP_ECAPACITY: return "CSR capacity exceeded (device status)";
+    case FP_EHIP: return "HIP launch or query failed";
+    case FP_EJOBCAPACITY: return "job-list capacity exceeded (device status)";
+    case FP_ETIMEOUT: return "a bounded device-side wait gave up (device status)";
+    default: return "unknown fpattn error code";
+  }
+}
+
+int fp_workspace_bytes(const fp_shape *shape, int variant, size_t *bytes) {
+  if (!bytes || (variant != 0 && variant != 1)) return FP_EINVAL;
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  *bytes = p.total;
+  return FP_OK;
+}
+
+int64_t fp_csr_capacity(const fp_shape *shape) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  return (int64_t)p.Hq * p.N * (p.N + 1) / 2;
+}
+
+int64_t fp_job_capacity(const fp_shape *shape) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  return (int64_t)p.Hkv * p.N * (p.N + 1) / 2;
+}
+
+static int index_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
+                        const void *K, const float *sK, float gamma, float tau,
+                        fp_index_out *out, void *ws, size_t ws_bytes, void *stream) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if (!Q || !K || (i8 && (!sQ || !sK))) return FP_EINVAL;
+  if ((rc = check_params(gamma, tau))) return rc;
+  if ((rc = check_out(p, out, true))) return rc;
+  if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  Work w = carve(p, ws);
+  FP_LAUNCH(launch_status_init(out->status, st));
+  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, st));
+  FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st));
+  FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st));
+  FP_LAUNCH(launch_rows_to_csr(p, out, w, st));
+  FP_LAUNCH(launch_jobs(p, out, w, st));
+  return FP_OK;
+}
+
+int fp_index(const fp_shape *shape, const void *Q, const void *K, float gamma, float tau,
+             fp_index_out *out, void *ws, size_t ws_bytes, void *stream) {
+  return index_common(shape, false, Q, nullptr, K, nullptr, gamma, tau, out, ws, ws_bytes,
+                      stream);
+}
+
+int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ, const int8_t *K8,
+                const float *sK, float gamma, float tau, fp_index_out *out, void *ws,
+                size_t ws_bytes, void *stream) {
+  return index_common(shape, true, Q8, sQ, K8, sK, gamma, tau, out, ws, ws_bytes, stream);
+}
+
+int fp_build_jobs(const fp_shape *shape, fp_index_out *io, void *ws, size_t ws_bytes,
+                  void *stream) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if ((rc = check_out(p, io, false))) return rc;
+  if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  Work w = carve(p, ws);
+  FP_LAUNCH(launch_status_init(io->status, st));
+  FP_LAUNCH(launch_jobs(p, io, w, st));
+  return FP_OK;
+}
+
+static int attn_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
+                       const void *K, const float *sK, const void *V, const float *sV,
+                       const fp_index_out *csr, void *O, void *ws, size_t ws_bytes,
+                       void *stream) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if (!Q || !K || !V || !O || (i8 && (!sQ || !sK || !sV))) return FP_EINVAL;
+  if (!csr || !csr->row_ptr || !csr->col_idx || !csr->job_ptr || !csr->job_blk ||
+      !csr->job_mask || !csr->job_order)
+    return FP_EINVAL;
+  if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
+  FP_LAUNCH(launch_attn(p, i8, Q, sQ, K, sK, V, sV, csr, O, (hipStream_t)stream));
+  return FP_OK;
+}
+
+int fp_attn(const fp_shape *shape, const void *Q, const void *K, const void *V,
+            const fp_index_out *csr, void *O, void *ws, size_t ws_bytes, void *stream) {
+  return attn_common(shape, false, Q, nullptr, K, nullptr, V, nullptr, csr, O, ws, ws_bytes,
+                     stream);
+}
+
+int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ, const int8_t *K8,
+               const float *sK, const int8_t *V8, const float *sV, const fp_index_out *csr,
+               void *O, void *ws, size_t ws_bytes, void *stream) {
+  return attn_common(shape, true, Q8, sQ, K8, sK, V8, sV, csr, O, ws, ws_bytes, stream);
+}
+
+int fp_probe_qk_i8(const fp_shape *shape, const int8_t *Q8, const int8_t *K8, int h, int i,
+                   int j, int32_t *out, void *stream) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if (!Q8 || !K8 || !out) return FP_EINVAL;
+  if (h < 0 || h >= p.Hq || i < 0 || i >= p.N || j < 0 || j >= p.N) return FP_EINVAL;
+  FP_LAUNCH(launch_probe_qk_i8(p, Q8, K8, h, i, j, out, (hipStream_t)stream));
+  return FP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Device helpers shared by the gfx950 kernels of libfpattn: vector types,
+// matrix-core (MFMA) wrappers, bf16 conversion and wave / workgroup
+// reductions.  gfx950 only (wave64, 32x32 MFMA tiles).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kD = 128;                 // head dimension
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -3.0e38f;     // finite "minus infinity" for running maxima
+
+// ---------------------------------------------------------------- MFMA
+// 32x32x16 bf16 -> fp32.  Operand A: lane l holds row (l % 32) and 8
+// consecutive k values of half (l / 32); B likewise with column (l % 32).
+// Result: acc[r] is row 8*(r/4) + 4*(l/32) + (r%4), column l % 32.
+__device__ __forceinline__ f32x16 mfma_bf16(const u32x4 a, const u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 32x32x32 int8 -> int32, same lane roles with 16 int8 k values per lane.
+__device__ __forceinline__ i32x16 mfma_i8(const u32x4 a, const u32x4 b, i32x16 c) {
+  return __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a),
+                                               __builtin_bit_cast(i32x4, b), c, 0, 0, 0);
+}
+
+// Row index (within a 32x32 tile) of accumulator element r on lane `lane`.
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- reductions
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+// Workgroup-wide sum / max; `red` is LDS scratch of at least (blockDim/64)
+// elements.  Every thread gets the result.  The order of additions is fixed
+// (wave butterflies, then waves in index order), so results are reproducible.
+template <typename T>
+__device__ __forceinline__ T block_sum(T x, T *red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  x = wave_sum(x);
+  __syncthreads();
+  if (lane == 0) red[w] = x;
+  __syncthreads();
+  T s = red[0];
+  for (int i = 1; i < nw; ++i) s += red[i];
+  return s;
+}
+__device__ __forceinline__ float block_max(float x, float *red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  x = wave_max(x);
+  __syncthreads();
+  if (lane == 0) red[w] = x;
+  __syncthreads();
+  float s = red[0];
+  for (int i = 1; i < nw; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+__device__ __forceinline__ int block_sum_int(int x, int *red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  x = wave_sum_int(x);
+  __syncthreads();
+  if (lane == 0) red[w] = x;
+  __syncthreads();
+  int s = red[0];
+  for (int i = 1; i < nw; ++i) s += red[i];
+  return s;
+}
+
+}  // namespace fp

@@ -1,0 +1,70 @@
+// Host-side plan (shape checks and workspace carving) and the launchers each
+// kernel file exports to the C-ABI layer.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fpattn.h"
+
+namespace fp {
+
+// Everything the launchers need about one problem, derived from fp_shape.
+struct Plan {
+  int S, B, Hq, Hkv, d, N, G;
+  int nw32;          // 32-bit words per row bitmask: ceil(N / 32)
+  int nch;           // key-block chunks per KV group in the statistics pass
+  int cpb;           // key blocks per chunk: ceil(N / nch)
+  // workspace layout (byte offsets from the workspace base)
+  size_t off_part;   // float2 [Hq*B*nch]  per-chunk row (max, sum) partials
+  size_t off_rowml;  // float2 [Hq*B]      per-row (max, sum) of the last block
+  size_t off_lo;     // float  [Hq*N]      lower-split block mass
+  size_t off_hi;     // float  [Hq*N]      upper-split block mass
+  size_t off_kbar;   // float  [Hkv*N*d]   mean-pooled key blocks
+  size_t off_sel;    // u32    [Hq*2*nw32] vertical / slash selections (bit sets)
+  size_t off_qabits; // u32    [Hq*N*nw32] query-aware row bit sets
+  size_t off_jwork;  // int32  [Hkv*N]     work per grouped job
+  size_t total;
+};
+
+// Validates the shape (FP_EINVAL / FP_EUNSUPPORTED) and fills *p.
+int make_plan(const fp_shape *s, Plan *p);
+
+// Typed views of the workspace.
+struct Work {
+  float2 *part, *rowml;
+  float *lo, *hi, *kbar;
+  uint32_t *sel, *qabits;
+  int32_t *jwork;
+};
+Work carve(const Plan &p, void *ws);
+
+// ---- launchers: each returns hipSuccess or the launch error.
+// Statistics of the last query block against every key block
+// (two passes over K: row max / sum, then block mass).
+hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ,
+                           const void *K, const float *sK, const Work &w, hipStream_t st);
+// Per head: pooled estimate, divergence, pattern, vertical / slash selection.
+hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,
+                              float gamma, float tau, const fp_index_out *out,
+                              const Work &w, hipStream_t st);
+// Query-aware rows: pooled queries of every block against pooled keys.
+hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
+                        const uint8_t *pattern, const Work &w, hipStream_t st);
+// Bit-set rows -> CSR (count, scan, write).
+hipError_t launch_rows_to_csr(const Plan &p, const fp_index_out *out, const Work &w,
+                              hipStream_t st);
+// CSR -> grouped-query job list and its work order.
+hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st);
+// status[0] = 0
+hipError_t launch_status_init(int32_t *status, hipStream_t st);
+// Block-sparse attention over the CSR rows.
+hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
+                       const float *sK, const void *V, const float *sV, const fp_index_out *csr,
+                       void *O, hipStream_t st);
+// One int8 score tile through the attention / statistics tile code.
+hipError_t launch_probe_qk_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
+                              int j, int32_t *out, hipStream_t st);
+
+}  // namespace fp

@@ -1,0 +1,151 @@
+// Per-head finalisation of sparse-index generation.
+//
+// Flex-Prefill's pattern decision, as the explainer ("FPGA24成果：FAST-Prefill
+// 稀疏注意力加速器", yunpan.plus) section 1.2 and the re-telling
+// ("FPGA加速动态稀疏注意力技术解析与优化", maplevalley.com.cn) section 1.1
+// describe it: the last query block is the representative query; a
+// Jensen-Shannon divergence decides per head between the query-aware and the
+// vertical-slash pattern (threshold tau, typically 0.1).  Read here as:
+//   p  = softmax_j(sigma * mean(Q_last) . mean(K_j))   pooled estimate
+//   v  = vertical block mass,  sl = slash block mass (from the statistics pass)
+//   D  = JSD(p, v) with the natural log; query-aware iff D < tau.
+// For vertical-slash heads the key-block columns Sel(v, gamma) and the
+// diagonal offsets Sel(sl, gamma) are chosen here (explainer section 3.1,
+// cumulative threshold gamma); the rows are expanded later.
+//
+// One workgroup per query head; every per-head vector of length N lives in LDS.
+#include "fp_common.hpp"
+#include "fp_internal.hpp"
+#include "fp_select.hpp"
+
+namespace fp {
+namespace {
+
+struct FinArgs {
+  const uint8_t *Q;
+  const float *sQ;
+  int S, N, B, G, nw32;
+  float sigma, gamma, tau;
+  const float *lo, *hi, *kbar;
+  uint8_t *pattern;
+  float *jsd, *stats;
+  uint32_t *sel;
+};
+
+constexpr int kFinThreads = 256;
+
+template <bool I8>
+__global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int N = a.N, B = a.B, S = a.S;
+  float *ev = smem;                 // [N] logits, then softmax weights
+  float *vv = ev + N;               // [N] vertical mass
+  float *sv = vv + N;               // [N] slash mass
+  float *qb = sv + N;               // [2][128] partial sums, then mean query
+  uint32_t *msk = (uint32_t *)(qb + 256);   // [nw32]
+  __shared__ double redd[16];
+  __shared__ int redi[16];
+  __shared__ float redf[16];
+  const int tid = threadIdx.x, h = blockIdx.x, g = h / a.G;
+
+  // Mean of the last query block (two halves of the rows, then combined).
+  {
+    const int dd = tid & 127, half = tid >> 7;
+    float s = 0.0f;
+    for (int r = half * (B / 2); r < (half + 1) * (B / 2); ++r) {
+      const size_t tok = (size_t)h * S + (S - B) + r;
+      if (!I8) s += bf16_to_f32(((const uint16_t *)a.Q)[tok * 128 + dd]);
+      else s += a.sQ[tok] * (float)((const int8_t *)a.Q)[tok * 128 + dd];
+    }
+    qb[half * 128 + dd] = s;
+  }
+  __syncthreads();
+  if (tid < 128) qb[tid] = (qb[tid] + qb[128 + tid]) / (float)B;
+  __syncthreads();
+
+  // Pooled logits against every mean-pooled key block.
+  for (int j = tid; j < N; j += kFinThreads) {
+    const float4 *kr = (const float4 *)(a.kbar + ((size_t)g * N + j) * 128);
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) {
+      const float4 k4 = kr[c];
+      acc += qb[4 * c] * k4.x + qb[4 * c + 1] * k4.y + qb[4 * c + 2] * k4.z + qb[4 * c + 3] * k4.w;
+    }
+    ev[j] = a.sigma * acc;
+  }
+  float mx = kNegBig;
+  for (int j = tid; j < N; j += kFinThreads) mx = fmaxf(mx, ev[j]);
+  mx = block_max(mx, redf);
+  double zpart = 0.0;
+  for (int j = tid; j < N; j += kFinThreads) {
+    const float w = expf(ev[j] - mx);
+    ev[j] = w;
+    zpart += (double)w;
+  }
+  const double Z = block_sum(zpart, redd);
+
+  // Vertical and slash mass; divergence.
+  const float *lo = a.lo + (size_t)h * N, *hi = a.hi + (size_t)h * N;
+  double dpart = 0.0;
+  for (int j = tid; j < N; j += kFinThreads) {
+    const float p = (float)((double)ev[j] / Z);
+    ev[j] = p;
+    const float v = lo[j] + hi[j];
+    vv[j] = v;
+    sv[j] = lo[N - 1 - j] + (j <= N - 2 ? hi[N - 2 - j] : 0.0f);
+    const double pd = p, vd = v, m = 0.5 * (pd + vd);
+    if (pd > 0.0) dpart += pd * log(pd / m);
+    if (vd > 0.0) dpart += vd * log(vd / m);
+  }
+  const double D = 0.5 * block_sum(dpart, redd);
+  const bool qa = D < (double)a.tau;
+  if (tid == 0) {
+    a.jsd[h] = (float)D;
+    a.pattern[h] = qa ? FP_PATTERN_QUERY_AWARE : FP_PATTERN_VERTICAL_SLASH;
+  }
+  if (a.stats) {
+    const size_t HN = (size_t)gridDim.x * N;
+    for (int j = tid; j < N; j += kFinThreads) {
+      a.stats[(size_t)h * N + j] = vv[j];
+      a.stats[HN + (size_t)h * N + j] = sv[j];
+      a.stats[2 * HN + (size_t)h * N + j] = ev[j];
+    }
+  }
+
+  // Vertical-slash heads: select columns and diagonal offsets.
+  uint32_t *out = a.sel + (size_t)h * 2 * a.nw32;
+  for (int which = 0; which < 2; ++which) {
+    if (!qa) {
+      block_select(which == 0 ? vv : sv, N, a.gamma, msk, redd, redi);
+      for (int w = tid; w < a.nw32; w += kFinThreads) out[which * a.nw32 + w] = msk[w];
+      __syncthreads();
+    } else {
+      for (int w = tid; w < a.nw32; w += kFinThreads) out[which * a.nw32 + w] = 0u;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,
+                              float gamma, float tau, const fp_index_out *out, const Work &w,
+                              hipStream_t st) {
+  FinArgs a;
+  a.Q = (const uint8_t *)Q;
+  a.sQ = sQ;
+  a.S = p.S; a.N = p.N; a.B = p.B; a.G = p.G; a.nw32 = p.nw32;
+  a.sigma = 1.0f / sqrtf((float)p.d);
+  a.gamma = gamma; a.tau = tau;
+  a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
+  a.pattern = out->pattern; a.jsd = out->jsd; a.stats = out->stats;
+  a.sel = w.sel;
+  const size_t lds = sizeof(float) * (3 * (size_t)p.N + 256) + sizeof(uint32_t) * p.nw32;
+  if (i8)
+    hipLaunchKernelGGL(k_ig_finalize<true>, dim3(p.Hq), dim3(kFinThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL(k_ig_finalize<false>, dim3(p.Hq), dim3(kFinThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace fp

@@ -1,0 +1,279 @@
+// Last-block statistics for sparse-index generation.
+//
+// Explainer ("FPGA24成果：FAST-Prefill稀疏注意力加速器", yunpan.plus) section
+// 3.1: key blocks stream from HBM in increasing block order, the last query
+// block Q_last is multiplied against each one, and only compact per-head
+// block statistics are kept -- vertical mass (attention summed along key
+// columns) and slash mass (summed along diagonals).  Section 2.1 describes the
+// b x S intermediate this avoids; nothing of that size is written here.
+//
+// The attention is the causal row softmax of section 1.1 for the b rows
+// t_r = S - b + r of the last block.  With L_r the row's softmax denominator,
+// the per-head outputs are, for each key block j,
+//   lo[j] = (1/b) sum_r sum_{c <= r} exp(s_r[jb+c] - M_r) / L_r
+//   hi[j] = (1/b) sum_r sum_{c >  r} exp(s_r[jb+c] - M_r) / L_r
+// so that vertical mass v[j] = lo[j] + hi[j], and the slash mass of offset
+// block o (token diagonal t_r - k pooled by b) is lo[N-1-o] + hi[N-2-o].
+// Every key block is also mean-pooled into kbar[g][j][:] for the pooled
+// estimate of Flex-Prefill's pattern test (explainer section 1.2).
+//
+// This version streams K twice: pass 1 gathers each row's running maximum
+// and exponential sum per chunk of key blocks, a combine step merges the
+// chunks, and pass 2 streams K again to bin the normalised attention.
+//
+// Work split: one workgroup per (KV group g, contiguous chunk of key blocks);
+// all G query heads of the group share each staged key block.  Each wave owns
+// TPW tiles of 32 last-block query rows and keeps their Q fragments in
+// registers; scores are computed transposed (keys x queries) on the 32x32x16
+// bf16 (or 32x32x32 int8) matrix cores so that every lane holds one query row.
+#include "fp_common.hpp"
+#include "fp_internal.hpp"
+
+namespace fp {
+namespace {
+
+struct StatArgs {
+  const uint8_t *Q;   // bf16 or int8 [Hq, S, 128]
+  const float *sQ;    // int8 only: [Hq, S]
+  const uint8_t *K;   // bf16 or int8 [Hkv, S, 128]
+  const float *sK;    // int8 only: [Hkv, S]
+  int S, N, G, nch, cpb;
+  float c2;           // (1/sqrt(d)) * log2(e)
+  float2 *part;       // [Hq*B*nch] (max, sum) per row and chunk (log2 domain)
+  float2 *rowml;      // [Hq*B] merged (max, sum)
+  float *lo, *hi;     // [Hq*N]
+  float *kbar;        // [Hkv*N*128]
+};
+
+template <bool I8> struct Tile;
+template <> struct Tile<false> {   // bf16: 8 k-steps of 16, 272-byte LDS rows
+  static constexpr int KS = 8, RowBytes = 256, Stride = 272;
+};
+template <> struct Tile<true> {    // int8: 4 k-steps of 32, 144-byte LDS rows
+  static constexpr int KS = 4, RowBytes = 128, Stride = 144;
+};
+
+// Copy key block j of KV head g into LDS (rows padded to Tile::Stride bytes).
+template <int B, bool I8>
+__device__ __forceinline__ void stage_k(const StatArgs &a, int g, int j, uint8_t *ks, float *sk) {
+  constexpr int CPR = Tile<I8>::RowBytes / 16;   // 16-byte chunks per row
+  const uint8_t *src = a.K + ((size_t)g * a.S + (size_t)j * B) * Tile<I8>::RowBytes;
+  for (int c = threadIdx.x; c < B * CPR; c += blockDim.x) {
+    const int row = c / CPR, col = c % CPR;
+    u32x4 v = *(const u32x4 *)(src + (size_t)row * Tile<I8>::RowBytes + col * 16);
+    *(u32x4 *)(ks + row * Tile<I8>::Stride + col * 16) = v;
+  }
+  if (I8) {
+    for (int r = threadIdx.x; r < B; r += blockDim.x) sk[r] = a.sK[(size_t)g * a.S + (size_t)j * B + r];
+  }
+}
+
+// Scores of one 32-key tile (kt) against one 32-query tile: x[r] in log2 units.
+template <bool I8>
+__device__ __forceinline__ void tile_scores(const uint8_t *ks, const float *sk, const u32x4 *qf,
+                                            float qscale, int kt, float c2, float x[16]) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t *arow = ks + (kt * 32 + (lane & 31)) * Tile<I8>::Stride + 16 * (lane >> 5);
+  if (!I8) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc = mfma_bf16(*(const u32x4 *)(arow + 32 * s), qf[s], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = acc[r] * c2;
+  } else {
+    i32x16 acc = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = mfma_i8(*(const u32x4 *)(arow + 32 * s), qf[s], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      x[r] = (float)acc[r] * (c2 * qscale) * sk[kt * 32 + acc_row(r, lane)];
+  }
+}
+
+template <int B, int TPW, bool I8, int PASS>
+__global__ void __launch_bounds__(1024) k_ig_stats(StatArgs a) {
+  constexpr int QT = B / 32;                 // query tiles per head
+  __shared__ __attribute__((aligned(16))) uint8_t ks[B * Tile<I8>::Stride];
+  __shared__ float sk[I8 ? B : 1];
+  __shared__ float red[64 * 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int G = a.G, S = a.S, N = a.N;
+  const int ntiles = G * QT;
+  const int j0 = chunk * a.cpb, j1 = min(N, j0 + a.cpb);
+
+  // Q fragments of this wave's tiles (rows of the last query block).
+  u32x4 qf[TPW][Tile<I8>::KS];
+  float qscale[TPW], ml_m[TPW], ml_l[TPW], wrow[TPW];
+  int qrow[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave * TPW + u;
+    const int tt = t < ntiles ? t : 0;
+    const int hh = tt / QT, row = (tt % QT) * 32 + (lane & 31);
+    const int h = g * G + hh;
+    qrow[u] = row;
+    const size_t tok = (size_t)h * S + (S - B) + row;
+    const uint8_t *qp = a.Q + tok * Tile<I8>::RowBytes + 16 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < Tile<I8>::KS; ++s) qf[u][s] = *(const u32x4 *)(qp + 32 * s);
+    qscale[u] = I8 ? a.sQ[tok] : 1.0f;
+    ml_m[u] = kNegBig;
+    ml_l[u] = 0.0f;
+    wrow[u] = 0.0f;
+    if (PASS == 2) {
+      const float2 ml = a.rowml[(size_t)h * B + row];
+      ml_m[u] = ml.x;
+      wrow[u] = 1.0f / ((float)B * ml.y);
+    }
+  }
+
+  for (int j = j0; j < j1; ++j) {
+    __syncthreads();
+    stage_k<B, I8>(a, g, j, ks, sk);
+    __syncthreads();
+    const bool diag = (j == N - 1);
+
+    if (PASS == 2) {
+      // Mean-pooled key block (fp32, rows summed in order).
+      for (int dd = threadIdx.x; dd < 128; dd += blockDim.x) {
+        float s = 0.0f;
+        for (int r = 0; r < B; ++r) {
+          float kv;
+          if (!I8) kv = bf16_to_f32(*(const uint16_t *)(ks + r * Tile<I8>::Stride + 2 * dd));
+          else kv = sk[r] * (float)(int8_t)ks[r * Tile<I8>::Stride + dd];
+          s += kv;
+        }
+        a.kbar[((size_t)g * N + j) * 128 + dd] = s / (float)B;
+      }
+    }
+
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave * TPW + u;
+      if (t >= ntiles) continue;
+      float lo_acc = 0.0f, hi_acc = 0.0f;
+      for (int kt = 0; kt < QT; ++kt) {
+        float x[16];
+        tile_scores<I8>(ks, sk, qf[u], qscale[u], kt, a.c2, x);
+        if (PASS == 1) {
+          float mx = kNegBig;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = kt * 32 + acc_row(r, lane);
+            if (diag && c > qrow[u]) x[r] = kNegBig;
+            mx = fmaxf(mx, x[r]);
+          }
+          const float mnew = fmaxf(ml_m[u], mx);
+          float sum = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum += (x[r] == kNegBig) ? 0.0f : exp2f(x[r] - mnew);
+          ml_l[u] = ml_l[u] * exp2f(ml_m[u] - mnew) + sum;
+          ml_m[u] = mnew;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int c = kt * 32 + acc_row(r, lane);
+            const float e = exp2f(x[r] - ml_m[u]);
+            if (c <= qrow[u]) lo_acc += e;
+            else if (!diag) hi_acc += e;
+          }
+        }
+      }
+      if (PASS == 2) {
+        lo_acc = wave_sum(lo_acc * wrow[u]);
+        hi_acc = wave_sum(hi_acc * wrow[u]);
+        if (lane == 0) {
+          red[2 * t] = lo_acc;
+          red[2 * t + 1] = hi_acc;
+        }
+      }
+    }
+    if (PASS == 2) {
+      __syncthreads();
+      if (threadIdx.x < G) {
+        const int hh = threadIdx.x;
+        float l = 0.0f, hsum = 0.0f;
+        for (int q = 0; q < QT; ++q) {
+          l += red[2 * (hh * QT + q)];
+          hsum += red[2 * (hh * QT + q) + 1];
+        }
+        const size_t o = (size_t)(g * G + hh) * N + j;
+        a.lo[o] = l;
+        a.hi[o] = hsum;
+      }
+    }
+  }
+
+  if (PASS == 1) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave * TPW + u;
+      float m = ml_m[u], l = ml_l[u];
+      const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
+      const float M = fmaxf(m, mo);
+      const float L = l * exp2f(m - M) + lo * exp2f(mo - M);
+      if (t < ntiles && lane < 32) {
+        const int h = g * G + t / QT;
+        a.part[((size_t)h * B + qrow[u]) * a.nch + chunk] = make_float2(M, L);
+      }
+    }
+  }
+}
+
+// Merge the per-chunk (max, sum) of every last-block row, chunks in order.
+__global__ void k_ig_combine(const float2 *part, float2 *rowml, int rows, int nch) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const float2 *p = part + (size_t)r * nch;
+  float M = kNegBig;
+  for (int c = 0; c < nch; ++c) M = fmaxf(M, p[c].x);
+  float L = 0.0f;
+  for (int c = 0; c < nch; ++c) L += p[c].y * exp2f(p[c].x - M);
+  rowml[r] = make_float2(M, L);
+}
+
+template <int B, int TPW, bool I8>
+hipError_t run(const Plan &p, const StatArgs &a, hipStream_t st) {
+  const int nwaves = (p.G * B / 32 + TPW - 1) / TPW;
+  dim3 grid(p.nch, p.Hkv), block(64 * nwaves);
+  hipLaunchKernelGGL((k_ig_stats<B, TPW, I8, 1>), grid, block, 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = p.Hq * B;
+  hipLaunchKernelGGL(k_ig_combine, dim3((rows + 255) / 256), dim3(256), 0, st, a.part, a.rowml,
+                     rows, p.nch);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL((k_ig_stats<B, TPW, I8, 2>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+template <bool I8>
+hipError_t dispatch(const Plan &p, const StatArgs &a, hipStream_t st) {
+  const int tiles = p.G * p.B / 32;      // at most 64 (G*b <= 2048)
+  if (p.B == 128) {
+    if (tiles <= 16) return run<128, 1, I8>(p, a, st);
+    if (tiles <= 32) return run<128, 2, I8>(p, a, st);
+    return run<128, 4, I8>(p, a, st);
+  }
+  if (tiles <= 16) return run<256, 1, I8>(p, a, st);
+  if (tiles <= 32) return run<256, 2, I8>(p, a, st);
+  return run<256, 4, I8>(p, a, st);
+}
+
+}  // namespace
+
+hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
+                           const float *sK, const Work &w, hipStream_t st) {
+  StatArgs a;
+  a.Q = (const uint8_t *)Q;
+  a.sQ = sQ;
+  a.K = (const uint8_t *)K;
+  a.sK = sK;
+  a.S = p.S; a.N = p.N; a.G = p.G; a.nch = p.nch; a.cpb = p.cpb;
+  a.c2 = kLog2e / sqrtf((float)p.d);
+  a.part = w.part; a.rowml = w.rowml; a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
+  return i8 ? dispatch<true>(p, a, st) : dispatch<false>(p, a, st);
+}
+
+}  // namespace fp

@@ -34,6 +34,7 @@ from dataclasses import dataclass, field, replace
 from typing import Dict, Optional
 
 import numpy as np
+import torch
 
 VS_QUERY_OFFSET = 8.0   # shared query offset along u_g for VS groups
 VS_SPIKE_GAIN = 4.0     # sink keys get += 4 * mean query of the group
@@ -88,6 +89,13 @@ def bf16_bits_from_f32(x: np.ndarray) -> np.ndarray:
     u = x.view(np.uint32)
     bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
     return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def _bf16_bits_fast(x: np.ndarray) -> np.ndarray:
+    """Same rounding as bf16_bits_from_f32 (round-half-to-even), multi-threaded through torch's
+    float32 -> bfloat16 cast; used for the large tensors of a layer."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 def f32_from_bf16_bits(u16: np.ndarray) -> np.ndarray:
@@ -210,8 +218,8 @@ def make(cfg, seed: int = 0) -> Layer:
                     src = rng.choice(i, size=min(QA_SOURCES, i), replace=False)
                     q[h, i * b:(i + 1) * b] += c[src].sum(axis=0)
 
-    qb = bf16_bits_from_f32(q)
+    qb = _bf16_bits_fast(q)
     del q
-    kb = bf16_bits_from_f32(k)
-    vb = bf16_bits_from_f32(v)
+    kb = _bf16_bits_fast(k)
+    vb = _bf16_bits_fast(v)
     return Layer(cfg=cfg, seed=seed, q=qb, k=kb, v=vb, planted=planted, spikes=spikes)

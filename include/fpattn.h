@@ -1,0 +1,227 @@
+/*
+ * fpattn.h -- C ABI of the dynamic block-sparse prefill attention library
+ * (libfpattn.so, HIP kernels for AMD gfx950 / MI355X).
+ *
+ * The method is the one the FAST-Prefill write-ups describe for Flex-Prefill:
+ *   [E] "FPGA24成果：FAST-Prefill稀疏注意力加速器，长上下文LLM推理提速2.5倍"
+ *       (yunpan.plus explainer), sections 1.1, 1.2, 2.1, 3.1-3.3, 4.2;
+ *   [R] "FPGA加速动态稀疏注意力技术解析与优化" (maplevalley.com.cn re-telling),
+ *       sections 1.1, 2.2, 3.2, 3.3.
+ * Two stages, each one call:
+ *   fp_index  -- sparse-index generation ([E] 3.1): the last query block is
+ *                scored against every key block in increasing block order;
+ *                per head, vertical (column) and slash (diagonal) block mass
+ *                and a pooled-query x pooled-key estimate are accumulated; a
+ *                Jensen-Shannon divergence against tau picks the
+ *                query-aware or the vertical-slash pattern ([E] 1.2, [R] 1.1);
+ *                blocks are taken in descending score until the cumulative
+ *                mass reaches gamma ([E] 3.1), block 0 and the diagonal block
+ *                are always kept, and the result is a CSR of key blocks per
+ *                (head, query block) plus a grouped-query job list ([E] 3.2).
+ *   fp_attn   -- block-sparse causal attention over that CSR ([E] 1.1, 1.2
+ *                figure 3): each query block attends only to its listed key
+ *                blocks, with the causal mask inside the diagonal block.
+ * The *_i8 variants are the W8A8 form ([E] 3.3 and 4.2, [R] 3.3): Q and K
+ * (and V) arrive as int8 with one fp32 scale per (head, token); Q.K^T is an
+ * int8 product with int32 accumulation, P.V runs in bf16.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers named as device pointers must point to device memory of the
+ *    current HIP device; "host" marks host memory.  Layouts are dense
+ *    row-major.  Q is [Hq, S, d], K and V are [Hkv, S, d] (head-major, one
+ *    sequence); query head h reads KV head h / (Hq / Hkv).
+ *  - The caller owns every buffer.  The library allocates nothing on the
+ *    device and keeps no state between calls apart from a cached
+ *    device-property query.  Scratch memory comes in through `ws`, of at
+ *    least fp_workspace_bytes() bytes; concurrent calls need separate
+ *    workspaces.
+ *  - Every call validates its arguments on the host, then only enqueues work
+ *    on `stream` (a hipStream_t; NULL = the default stream) and returns
+ *    without synchronising.  Outputs are valid once that stream has reached
+ *    the point of the call; inputs must stay alive until then.
+ *  - Return value: FP_OK (0) or a negative FP_E* code.  When a code is
+ *    returned nothing was enqueued.  Data-dependent failures (CSR or job
+ *    capacity exceeded) cannot be known on the host: the kernels set bits in
+ *    the device status word (fp_index_out.status) and stop writing past the
+ *    capacity; read it after the stream synchronises.
+ *  - Identical inputs give bit-identical outputs (no floating-point atomics).
+ *  - Supported shapes: d = 128; b in {128, 256}; S a positive multiple of b
+ *    with S / b <= 8192; Hq a multiple of Hkv; G * b <= 2048 where
+ *    G = Hq / Hkv; gamma in (0, 1]; tau >= 0.
+ */
+#ifndef FPATTN_H
+#define FPATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FP_OK            0
+#define FP_EINVAL       (-1) /* null pointer, S % b != 0, Hq % Hkv != 0, gamma not in (0,1], tau < 0 or NaN */
+#define FP_EUNSUPPORTED (-2) /* d != 128, b not in {128,256}, N > 8192, G*b > 2048 */
+#define FP_EWORKSPACE   (-3) /* workspace smaller than fp_workspace_bytes() */
+#define FP_ECAPACITY    (-4) /* (device status bit 1) CSR capacity exceeded */
+#define FP_EHIP         (-5) /* a HIP launch or query failed */
+#define FP_EJOBCAPACITY (-6) /* (device status bit 2) job-list capacity exceeded */
+#define FP_ETIMEOUT     (-7) /* (device status bit 3) a bounded device-side wait gave up */
+
+/* Device status word bits (fp_index_out.status[0]); 0 = success. */
+#define FP_STATUS_CSR_OVERFLOW 1u
+#define FP_STATUS_JOB_OVERFLOW 2u
+#define FP_STATUS_WAIT_TIMEOUT 4u
+
+/* Pattern codes written to fp_index_out.pattern ([E] 1.2, [R] 1.1). */
+#define FP_PATTERN_VERTICAL_SLASH 0
+#define FP_PATTERN_QUERY_AWARE    1
+
+/* Problem shape (host struct).  N = S / b blocks. */
+typedef struct fp_shape {
+  int32_t S;    /* tokens in the sequence                 */
+  int32_t b;    /* block size in tokens ([E] 1.2: 128/256) */
+  int32_t Hq;   /* query heads                            */
+  int32_t Hkv;  /* key/value heads                        */
+  int32_t d;    /* head dimension (must be 128)           */
+} fp_shape;
+
+/*
+ * Index output (host struct of device pointers).  Row r = h * N + i is the
+ * key-block set J(h, i) of query block i of head h, columns ascending; job
+ * (g, i), index g * N + i, is the union over the G query heads of KV group g
+ * of J(h, i), each block carrying a bit mask of the heads that use it (bit
+ * h - g*G).  job_order lists the job indices by decreasing work
+ * sum_h |J(h, i)| (ties: lower index first).
+ */
+typedef struct fp_index_out {
+  int32_t  *row_ptr;    /* device [Hq*N + 1]                                    */
+  int32_t  *col_idx;    /* device [col_cap]                                     */
+  int64_t   col_cap;    /* host: capacity of col_idx (fp_csr_capacity() is the
+                           worst case, gamma = 1)                               */
+  int32_t  *job_ptr;    /* device [Hkv*N + 1]                                   */
+  int32_t  *job_blk;    /* device [job_cap] key block of each job entry         */
+  uint32_t *job_mask;   /* device [job_cap] head mask of each job entry         */
+  int64_t   job_cap;    /* host: capacity of job_blk / job_mask
+                           (fp_job_capacity() is the worst case)                */
+  int32_t  *job_order;  /* device [Hkv*N]                                       */
+  uint8_t  *pattern;    /* device [Hq], FP_PATTERN_*  (NULL allowed in
+                           fp_build_jobs only)                                  */
+  float    *jsd;        /* device [Hq] Jensen-Shannon divergence D_h (natural
+                           log, no square root)  (NULL allowed in fp_build_jobs) */
+  float    *stats;      /* device [3][Hq][N] or NULL: vertical mass v, slash
+                           mass sl and pooled estimate p of every head          */
+  int32_t  *status;     /* device [1] status word, FP_STATUS_* bits, written by
+                           every call that fills this struct (set to 0 first)   */
+} fp_index_out;
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int fp_version(void);
+
+/* Static text for an FP_* code (never NULL). */
+const char *fp_strerror(int code);
+
+/*
+ * Scratch bytes that fp_index / fp_index_i8 (variant 0 / 1), fp_build_jobs
+ * and fp_attn / fp_attn_i8 need for this shape.  One workspace of the size
+ * returned for variant 1 serves every call.  Writes *bytes (host).
+ */
+int fp_workspace_bytes(const fp_shape *shape, int variant, size_t *bytes);
+
+/* Worst-case CSR entries Hq * N * (N + 1) / 2 (every causal block kept);
+ * negative FP_E* code on an invalid shape. */
+int64_t fp_csr_capacity(const fp_shape *shape);
+
+/* Worst-case job entries Hkv * N * (N + 1) / 2; negative FP_E* on error. */
+int64_t fp_job_capacity(const fp_shape *shape);
+
+/*
+ * Sparse-index generation, bf16 inputs ([E] 3.1, 1.2; [R] 1.1, 3.2).
+ *   Q: device bf16 [Hq, S, d];  K: device bf16 [Hkv, S, d].
+ *   gamma: cumulative-mass threshold in (0, 1] (gamma = 1 keeps every causal
+ *          block); tau: divergence threshold (>= 0), D_h < tau selects the
+ *          query-aware pattern.
+ * Definitions (sigma = 1/sqrt(d), t_r = S - b + r for the b rows of the last
+ * query block, softmax over keys k <= t_r):
+ *   v[j]  = (1/b) sum_r sum_{k in block j} a_r[k]             (vertical mass)
+ *   sl[o] = (1/b) sum_r sum_{k <= t_r, (t_r - k) / b = o} a_r[k] (slash mass)
+ *   p     = softmax_j(sigma * mean(Q_last) . mean(K_j))       (pooled estimate)
+ *   D     = JSD(p, v);  query-aware iff D < tau.
+ *   Sel(x, gamma): fewest indices in descending value (ties: lower index
+ *   first) whose sum reaches gamma * sum(x).
+ *   vertical-slash rows: J(h,i) = {j in Sel(v) : j <= i}
+ *                        u {i - o : o in Sel(sl), o <= i} u {0, i};
+ *   query-aware rows:    J(h,i) = Sel(softmax_{j<=i}(sigma * mean(Q_i) .
+ *                        mean(K_j))) u {0, i}.
+ * Fills every field of *out (device writes only); out->stats may be NULL.
+ * K is read from HBM once, in increasing block order; nothing of size
+ * Hq x S is written to memory.  Errors: FP_EINVAL, FP_EUNSUPPORTED,
+ * FP_EWORKSPACE, FP_EHIP; capacity overflow through out->status.
+ */
+int fp_index(const fp_shape *shape, const void *Q, const void *K,
+             float gamma, float tau, fp_index_out *out,
+             void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * W8A8 sparse-index generation ([E] 3.3, 4.2; [R] 3.3).
+ *   Q8: device int8 [Hq, S, d], sQ: device fp32 [Hq, S];
+ *   K8: device int8 [Hkv, S, d], sK: device fp32 [Hkv, S].
+ * Scores are sigma * sQ[t] * sK[k] * (Q8[t] . K8[k]) with the integer dot
+ * product exact (int8 x int8 -> int32); pooled vectors use the dequantised
+ * values s * x8.  Otherwise as fp_index.
+ */
+int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
+                const int8_t *K8, const float *sK, float gamma, float tau,
+                fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Rebuild the grouped-query job list (job_ptr, job_blk, job_mask, job_order)
+ * from a CSR already in io->row_ptr / io->col_idx (rows sorted ascending,
+ * every column <= its query block).  fp_index calls this itself; it is
+ * exported so that a CSR from elsewhere can drive fp_attn ([E] 3.2: the
+ * sparse index set is turned into a compact job list).  Writes io->status.
+ */
+int fp_build_jobs(const fp_shape *shape, fp_index_out *io,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Block-sparse causal attention, bf16 ([E] 1.1 and 1.2 figure 3).
+ *   Q: device bf16 [Hq, S, d]; K, V: device bf16 [Hkv, S, d];
+ *   csr: the fields row_ptr, col_idx, job_ptr, job_blk, job_mask, job_order
+ *        of an fp_index / fp_build_jobs result (read only);
+ *   O: device bf16 [Hq, S, d], every element written.
+ * For query token t of block i of head h: O[h,t] = sum over keys k <= t whose
+ * block is in J(h,i) of softmax_k(sigma * Q[h,t] . K[g,k]) * V[g,k]; fp32
+ * softmax and accumulation, one rounding to bf16 at the end.
+ * Errors: FP_EINVAL, FP_EUNSUPPORTED, FP_EWORKSPACE, FP_EHIP.
+ */
+int fp_attn(const fp_shape *shape, const void *Q, const void *K, const void *V,
+            const fp_index_out *csr, void *O,
+            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * W8A8 block-sparse attention ([E] 3.3, 4.2; [R] 3.3).  Scores use the exact
+ * int8 dot product scaled by sigma * sQ * sK; P.V uses bf16 P against the
+ * int8 values of V (exact in bf16) with the per-token scale sV folded into P.
+ *   V8: device int8 [Hkv, S, d], sV: device fp32 [Hkv, S]; O: device bf16.
+ */
+int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
+               const int8_t *K8, const float *sK, const int8_t *V8,
+               const float *sV, const fp_index_out *csr, void *O,
+               void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Test hook for the W8A8 score product: out[c][r] = Q8[h, i*b + r] .
+ * K8[h / G, j*b + c] (exact int32) for r, c in [0, b), computed with the same
+ * int8 matrix-core tile code that fp_index_i8 and fp_attn_i8 use.
+ *   out: device int32 [b, b] (key-major: out[c * b + r]).
+ */
+int fp_probe_qk_i8(const fp_shape *shape, const int8_t *Q8, const int8_t *K8,
+                   int h, int i, int j, int32_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FPATTN_H */

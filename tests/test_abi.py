@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dynamic_block_sparse_flexprefill_amd as fpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fpattn.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ("fp_index", "fp_index_i8", "fp_attn", "fp_attn_i8", "fp_build_jobs",
+              "fp_workspace_bytes", "fp_csr_capacity", "fp_job_capacity", "fp_strerror",
+              "fp_version", "fp_probe_qk_i8"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = fpa.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_version_and_strerror():
+    assert fpa.lib().fp_version() >= 100
+    for code in range(0, -8, -1):
+        assert isinstance(fpa.strerror(code), str) and fpa.strerror(code)
+    assert "unknown" in fpa.strerror(-99)
+
+
+@pytest.mark.parametrize("S,b,Hq,Hkv,d,code", [
+    (2048, 128, 4, 2, 128, fpa.FP_OK),
+    (2000, 128, 4, 2, 128, fpa.FP_EINVAL),        # S % b
+    (2048, 128, 5, 2, 128, fpa.FP_EINVAL),        # Hq % Hkv
+    (0, 128, 4, 2, 128, fpa.FP_EINVAL),
+    (2048, 128, 4, 2, 64, fpa.FP_EUNSUPPORTED),   # d
+    (2048, 64, 4, 2, 128, fpa.FP_EUNSUPPORTED),   # b
+    (128 * 8193, 128, 4, 2, 128, fpa.FP_EUNSUPPORTED),  # N > 8192
+    (4096, 256, 16, 1, 128, fpa.FP_EUNSUPPORTED),  # G * b > 2048
+    (4096, 128, 16, 1, 128, fpa.FP_OK),            # G * b = 2048
+])
+def test_shape_validation(S, b, Hq, Hkv, d, code):
+    sh = fpa.shape_of(S, b, Hq, Hkv, d)
+    n = ctypes.c_size_t(0)
+    rc = fpa.lib().fp_workspace_bytes(ctypes.byref(sh), 0, ctypes.byref(n))
+    assert rc == code
+    if code == fpa.FP_OK:
+        assert n.value > 0
+        N = S // b
+        assert fpa.csr_capacity(sh) == Hq * N * (N + 1) // 2
+        assert fpa.job_capacity(sh) == Hkv * N * (N + 1) // 2
+    else:
+        assert fpa.csr_capacity(sh) == code
+
+
+def _dummy_out(sh, col_cap=None):
+    N = sh.S // sh.b
+    o = fpa.FpIndexOut()
+    for f in ("row_ptr", "col_idx", "job_ptr", "job_blk", "job_mask", "job_order", "pattern", "jsd", "status"):
+        setattr(o, f, 0x1000)   # never dereferenced: every case below fails validation first
+    o.col_cap = sh.Hq * N * (N + 1) // 2 if col_cap is None else col_cap
+    o.job_cap = sh.Hkv * N * (N + 1) // 2
+    o.stats = None
+    return o
+
+
+@pytest.mark.parametrize("gamma,tau,ok", [(0.0, 0.1, False), (1.5, 0.1, False), (float("nan"), 0.1, False),
+                                          (0.9, -0.1, False), (0.9, float("nan"), False)])
+def test_index_rejects_bad_parameters(gamma, tau, ok):
+    sh = fpa.shape_of(2048, 128, 4, 2)
+    o = _dummy_out(sh)
+    rc = fpa.lib().fp_index(ctypes.byref(sh), ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1000),
+                            gamma, tau, ctypes.byref(o), ctypes.c_void_p(0x1000), 1 << 30, None)
+    assert rc == fpa.FP_EINVAL
+
+
+def test_index_rejects_null_and_small_workspace():
+    sh = fpa.shape_of(2048, 128, 4, 2)
+    L = fpa.lib()
+    o = _dummy_out(sh)
+    P = ctypes.c_void_p(0x1000)
+    assert L.fp_index(ctypes.byref(sh), None, P, 0.9, 0.1, ctypes.byref(o), P, 1 << 30, None) == fpa.FP_EINVAL
+    assert L.fp_index(ctypes.byref(sh), P, P, 0.9, 0.1, None, P, 1 << 30, None) == fpa.FP_EINVAL
+    assert L.fp_index(ctypes.byref(sh), P, P, 0.9, 0.1, ctypes.byref(o), None, 1 << 30, None) == fpa.FP_EINVAL
+    assert L.fp_index(ctypes.byref(sh), P, P, 0.9, 0.1, ctypes.byref(o), P, 16, None) == fpa.FP_EWORKSPACE
+    small = _dummy_out(sh, col_cap=10)   # fewer entries than rows
+    assert L.fp_index(ctypes.byref(sh), P, P, 0.9, 0.1, ctypes.byref(small), P, 1 << 30, None) == fpa.FP_EINVAL
+    o.status = None
+    assert L.fp_index(ctypes.byref(sh), P, P, 0.9, 0.1, ctypes.byref(o), P, 1 << 30, None) == fpa.FP_EINVAL
+    bad = fpa.shape_of(2048, 128, 4, 2, 64)
+    assert L.fp_index(ctypes.byref(bad), P, P, 0.9, 0.1, ctypes.byref(o), P, 1 << 30, None) == fpa.FP_EUNSUPPORTED
+
+
+def test_attn_and_probe_reject_bad_arguments():
+    sh = fpa.shape_of(2048, 128, 4, 2)
+    L = fpa.lib()
+    o = _dummy_out(sh)
+    P = ctypes.c_void_p(0x1000)
+    assert L.fp_attn(ctypes.byref(sh), P, P, None, ctypes.byref(o), P, P, 1 << 30, None) == fpa.FP_EINVAL
+    assert L.fp_attn(ctypes.byref(sh), P, P, P, ctypes.byref(o), P, P, 8, None) == fpa.FP_EWORKSPACE
+    assert L.fp_attn_i8(ctypes.byref(sh), P, None, P, P, P, P, ctypes.byref(o), P, P, 1 << 30, None) == fpa.FP_EINVAL
+    assert L.fp_probe_qk_i8(ctypes.byref(sh), P, P, 4, 0, 0, P, None) == fpa.FP_EINVAL   # h out of range
+    assert L.fp_probe_qk_i8(ctypes.byref(sh), P, P, 0, 16, 0, P, None) == fpa.FP_EINVAL  # i out of range
+    o2 = _dummy_out(sh)
+    o2.job_ptr = None
+    assert L.fp_build_jobs(ctypes.byref(sh), ctypes.byref(o2), P, 1 << 30, None) == fpa.FP_EINVAL
+
+
+def test_workspace_grows_with_shape():
+    a = fpa.workspace_bytes(fpa.shape_of(2048, 128, 4, 2))
+    b = fpa.workspace_bytes(fpa.shape_of(131072, 128, 24, 8))
+    assert b > a > 0
+    # nothing of size Hq x S x b: the 128K workspace stays far below the b x S score matrix of one head
+    assert b < 128 * 131072 * 4
