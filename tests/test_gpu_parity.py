@@ -194,8 +194,12 @@ def test_index_deterministic_and_end_to_end():
     Oa = fpa.attn(Qd, Kd, Vd, a)
     Ob = fpa.attn(Qd, Kd, Vd, b_)
     torch.cuda.synchronize()
+    nnz, njob = a.nnz, int(a.job_ptr[-1].item())
+    lens = {"col_idx": nnz, "job_blk": njob, "job_mask": njob}   # capacity tails are never written
     for f in ("row_ptr", "col_idx", "job_ptr", "job_blk", "job_mask", "job_order", "pattern", "jsd", "stats"):
-        assert torch.equal(getattr(a, f), getattr(b_, f)), f
+        x, y = getattr(a, f), getattr(b_, f)
+        n = lens.get(f, x.numel())
+        assert torch.equal(x.flatten()[:n], y.flatten()[:n]), f
     assert torch.equal(Oa.view(torch.int16), Ob.view(torch.int16))
     # the device CSR drives attention to the oracle's output on that CSR
     rp, ci = P.gpu_rows(a)
