@@ -1,23 +1,29 @@
-// Block-sparse causal attention over a CSR of key blocks.
+// Block-sparse causal attention over the grouped-query job list.
 //
 // The explainer ("FPGA24成果：FAST-Prefill稀疏注意力加速器", yunpan.plus)
 // section 1.1 gives the attention softmax(Q K^T / sqrt(d_k)) V; section 1.2
 // (figure 3) restricts each query block to the key/value blocks its sparse
 // index names.  For query token t of block i and head h, the keys are those
 // k <= t whose block is in J(h, i); the softmax runs over exactly those keys.
-// The softmax is taken block by block with a running maximum (the re-telling
-// "FPGA加速动态稀疏注意力技术解析与优化", section 3.3, normalises attention
-// scores block-wise to avoid overflow).
+// The softmax is taken chunk by chunk against a running reference maximum
+// (the re-telling "FPGA加速动态稀疏注意力技术解析与优化", section 3.3,
+// normalises attention scores block-wise to avoid overflow).
 //
 // W8A8 (explainer sections 3.3 and 4.2): Q.K^T on the int8 matrix cores with
 // int32 accumulation, scaled by sigma * sQ[t] * sK[k]; P.V in bf16 with the
 // int8 values of V (exact in bf16) and sV folded into P.
 //
-// Kernel layout: one workgroup per CSR row (h, i), one wave per 32 queries.
-// Each key block is staged in LDS once per workgroup: K row-major, V
-// transposed.  Scores are computed transposed, S^T = K Q^T, on the 32x32
-// matrix cores, so every lane owns one query row; its softmax weights are
-// already in the operand layout of the next product O^T += V^T P^T.
+// Kernel layout.  The explainer's section 2.2 notes that grouped-query heads
+// re-fetch the same K/V blocks; section 3.2 schedules sparse attention from a
+// compact job list.  Here one workgroup runs one job (KV group g, query block
+// i) -- the union of the G heads' key blocks -- or a share of its query tiles:
+// each key block is staged in LDS once (128 keys at a time) and used by every
+// head of the group whose mask bit is set.  One wave owns one (head, 32-query
+// tile).  The next 128-key chunk is loaded into registers while the current
+// one is computed.  Scores are computed transposed, S^T = K Q^T, on the
+// 32x32x16 matrix cores so that every lane owns one query row; its softmax
+// weights are then already the operand of O^T += V^T P^T (V is transposed
+// while staged).  Jobs run longest first (job_order).
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 
@@ -27,62 +33,93 @@ namespace {
 struct AttnArgs {
   const uint8_t *Q, *K, *V;
   const float *sQ, *sK, *sV;
-  const int32_t *row_ptr, *col_idx;
+  const int32_t *job_ptr, *job_blk, *job_order;
+  const uint32_t *job_mask;
   uint16_t *O;
-  int S, N, Hq, G;
+  int S, N, B, G, qpw, parts;
   float c2;
 };
 
-template <int B, bool I8> struct AttnLds {
-  static constexpr int KStride = I8 ? 144 : 272;   // bytes per staged key row
-  static constexpr int VStride = B + 4;             // bf16 elements per transposed V row
-  static constexpr int KBytes = B * KStride;
-  static constexpr int VBytes = 128 * VStride * 2;
+constexpr int kChunk = 128;                  // keys staged per step
+constexpr int kVStride = kChunk + 4;         // bf16 elements per transposed V row
+constexpr float kRescale = 8.0f;             // lazy-rescale headroom (log2 units)
+
+template <bool I8> struct KL {
+  static constexpr int RB = I8 ? 128 : 256;            // global bytes per key row
+  static constexpr int Stride = I8 ? 144 : 272;        // LDS bytes per key row (padded)
+  static constexpr int KPieces = kChunk * RB / 16;     // 16-byte pieces of a K chunk
+  static constexpr int VItems = (kChunk / 2) * (RB / 16);  // (key pair, 16-byte column)
 };
 
-// Stage key block j of KV head g: K rows (padded) and V transposed to [d][key] bf16.
-template <int B, bool I8>
-__device__ __forceinline__ void stage_kv(const uint8_t *K, const uint8_t *V, const float *sK,
-                                         const float *sV, int S, int g, int j, uint8_t *ks,
-                                         uint16_t *vt, float *sk, float *sv) {
-  using L = AttnLds<B, I8>;
-  constexpr int RB = I8 ? 128 : 256;                 // bytes per global row
-  constexpr int CPR = RB / 16;
-  const size_t row0 = (size_t)g * S + (size_t)j * B;
-  const uint8_t *kb = K + row0 * RB;
-  for (int c = threadIdx.x; c < B * CPR; c += blockDim.x) {
-    const int r = c / CPR, col = c % CPR;
-    *(u32x4 *)(ks + r * L::KStride + col * 16) = *(const u32x4 *)(kb + (size_t)r * RB + col * 16);
-  }
-  const uint8_t *vb = V + row0 * RB;
-  uint32_t *vt32 = (uint32_t *)vt;
-  for (int it = threadIdx.x; it < (B / 2) * CPR; it += blockDim.x) {
-    const int dc = it % CPR, kp = it / CPR;
-    const u32x4 a = *(const u32x4 *)(vb + (size_t)(2 * kp) * RB + dc * 16);
-    const u32x4 b = *(const u32x4 *)(vb + (size_t)(2 * kp + 1) * RB + dc * 16);
-    if (!I8) {
+// Register-staged copy of one 128-key chunk of K and V.
+template <int NT, bool I8>
+struct Stage {
+  using L = KL<I8>;
+  static constexpr int KP = (L::KPieces + NT - 1) / NT;
+  static constexpr int VP = (L::VItems + NT - 1) / NT;
+  u32x4 kr[KP], va[VP], vb[VP];
+  float sk, sv;
+
+  __device__ __forceinline__ void load(const AttnArgs &a, size_t row0) {
+    const int tid = threadIdx.x;
+    const uint8_t *kb = a.K + row0 * L::RB, *vbp = a.V + row0 * L::RB;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (a[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t hi = (b[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        vt32[((dc * 8 + e) * L::VStride + 2 * kp) >> 1] = lo | (hi << 16);
-      }
-    } else {
+    for (int u = 0; u < KP; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < L::KPieces) kr[u] = *(const u32x4 *)(kb + (size_t)idx * 16);
+    }
+    constexpr int CPR = L::RB / 16;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float lo = (float)(int8_t)((a[e >> 2] >> (8 * (e & 3))) & 0xffu);
-        const float hi = (float)(int8_t)((b[e >> 2] >> (8 * (e & 3))) & 0xffu);
-        vt32[((dc * 16 + e) * L::VStride + 2 * kp) >> 1] = pack_bf16x2(lo, hi);
+    for (int u = 0; u < VP; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < L::VItems) {
+        const int dc = idx % CPR, kp = idx / CPR;
+        va[u] = *(const u32x4 *)(vbp + (size_t)(2 * kp) * L::RB + dc * 16);
+        vb[u] = *(const u32x4 *)(vbp + (size_t)(2 * kp + 1) * L::RB + dc * 16);
       }
     }
-  }
-  if (I8) {
-    for (int r = threadIdx.x; r < B; r += blockDim.x) {
-      sk[r] = sK[row0 + r];
-      sv[r] = sV[row0 + r];
+    if (I8 && tid < kChunk) {
+      sk = a.sK[row0 + tid];
+      sv = a.sV[row0 + tid];
     }
   }
-}
+
+  __device__ __forceinline__ void store(uint8_t *ks, uint32_t *vt32, float *sks, float *svs) const {
+    const int tid = threadIdx.x;
+    constexpr int CPR = L::RB / 16;
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < L::KPieces) *(u32x4 *)(ks + (idx / CPR) * L::Stride + (idx % CPR) * 16) = kr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < VP; ++u) {
+      const int idx = tid + u * NT;
+      if (idx < L::VItems) {
+        const int dc = idx % CPR, kp = idx / CPR;
+        if (!I8) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t lo = (va[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t hi = (vb[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            vt32[((dc * 8 + e) * kVStride >> 1) + kp] = lo | (hi << 16);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float lo = (float)(int8_t)((va[u][e >> 2] >> (8 * (e & 3))) & 0xffu);
+            const float hi = (float)(int8_t)((vb[u][e >> 2] >> (8 * (e & 3))) & 0xffu);
+            vt32[((dc * 16 + e) * kVStride >> 1) + kp] = pack_bf16x2(lo, hi);
+          }
+        }
+      }
+    }
+    if (I8 && tid < kChunk) {
+      sks[tid] = sk;
+      svs[tid] = sv;
+    }
+  }
+};
 
 // Q fragments (operand B of S^T = K Q^T) for query token `tok` of this lane.
 template <bool I8>
@@ -99,41 +136,42 @@ __device__ __forceinline__ void load_q(const uint8_t *Q, size_t tok, u32x4 qf[8]
   }
 }
 
-// Raw scores of key tile (32 keys starting at key0) against this wave's 32 queries.
+// Raw scores of 32 staged keys (rows key0..key0+31 of ks) against the wave's
+// 32 queries: transposed tile, acc[r] <-> key key0 + acc_row(r), query lane%32.
 template <bool I8>
-__device__ __forceinline__ void raw_scores(const uint8_t *ks, int kstride, int key0,
-                                           const u32x4 qf[8], f32x16 &accf, i32x16 &acci) {
+__device__ __forceinline__ void raw_scores(const uint8_t *ks, int key0, const u32x4 qf[8],
+                                           float x[16]) {
   const int lane = threadIdx.x & 63;
-  const uint8_t *arow = ks + (key0 + (lane & 31)) * kstride + 16 * (lane >> 5);
+  const uint8_t *arow = ks + (key0 + (lane & 31)) * KL<I8>::Stride + 16 * (lane >> 5);
   if (!I8) {
-    accf = f32x16{};
+    f32x16 acc = {};
 #pragma unroll
-    for (int s = 0; s < 8; ++s) accf = mfma_bf16(*(const u32x4 *)(arow + 32 * s), qf[s], accf);
+    for (int s = 0; s < 8; ++s) acc = mfma_bf16(*(const u32x4 *)(arow + 32 * s), qf[s], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = acc[r];
   } else {
-    acci = i32x16{};
+    i32x16 acc = {};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acci = mfma_i8(*(const u32x4 *)(arow + 32 * s), qf[s], acci);
+    for (int s = 0; s < 4; ++s) acc = mfma_i8(*(const u32x4 *)(arow + 32 * s), qf[s], acc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = (float)acc[r];
   }
 }
 
-template <int B, bool I8>
-__global__ void __launch_bounds__(2 * B) k_attn_rows(AttnArgs a) {
-  using L = AttnLds<B, I8>;
-  __shared__ __attribute__((aligned(16))) uint8_t ks[L::KBytes];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[128 * L::VStride];
-  __shared__ float sk[I8 ? B : 1], sv[I8 ? B : 1];
+template <int NT, bool I8>
+__global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[kChunk * KL<I8>::Stride];
+  __shared__ __attribute__((aligned(16))) uint32_t vt32[128 * kVStride / 2];
+  __shared__ __attribute__((aligned(16))) float sks[I8 ? kChunk : 4], svs[I8 ? kChunk : 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
-  const int N = a.N, S = a.S;
-
-  // Workgroup -> row, keeping consecutive rows (the heads of one query
-  // block) on the same XCD: the hardware deals workgroups round-robin to 8.
-  const int nblk = gridDim.x;
-  int L8 = blockIdx.x;
-  if ((nblk & 7) == 0) L8 = (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int i = N - 1 - L8 / a.Hq, h = L8 % a.Hq, g = h / a.G;
-  const int row = h * N + i;
-  const int qr = wave * 32 + (lane & 31);
-  const size_t tok = (size_t)h * S + (size_t)i * B + qr;
+  const int N = a.N, S = a.S, B = a.B;
+  const int job = a.job_order[blockIdx.x / a.parts], part = blockIdx.x % a.parts;
+  const int g = job / N, i = job % N;
+  const int hh = wave / a.qpw, qt = part * a.qpw + wave % a.qpw;
+  const int h = g * a.G + hh;
+  const int qtok0 = i * B + qt * 32;                 // first query token of this wave
+  const int qtok = qtok0 + (lane & 31);
+  const size_t tok = (size_t)h * S + qtok;
 
   u32x4 qf[8];
   load_q<I8>(a.Q, tok, qf);
@@ -142,76 +180,101 @@ __global__ void __launch_bounds__(2 * B) k_attn_rows(AttnArgs a) {
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m = kNegBig, l = 0.0f;
+  float m = -1e30f, l = 0.0f;                        // reference max (log2 units), partial sum
 
-  const int p0 = a.row_ptr[row], p1 = a.row_ptr[row + 1];
-  for (int p = p0; p < p1; ++p) {
-    const int j = a.col_idx[p];
-    if (j < 0 || j >= N) continue;   // not a key block of this sequence (same for every thread)
+  const int p0 = a.job_ptr[job], p1 = a.job_ptr[job + 1];
+  const int nck = B / kChunk;
+  const int total = (p1 - p0) * nck;
+  Stage<NT, I8> st;
+  auto chunk_row0 = [&](int c, int &j, int &kc) -> bool {
+    j = a.job_blk[p0 + c / nck];
+    kc = c % nck;
+    return j >= 0 && j < N;
+  };
+  {
+    int j, kc;
+    if (total > 0 && chunk_row0(0, j, kc)) st.load(a, (size_t)g * S + (size_t)j * B + kc * kChunk);
+  }
+  for (int c = 0; c < total; ++c) {
+    int j, kc;
+    const bool valid = chunk_row0(c, j, kc);
+    const uint32_t mask = a.job_mask[p0 + c / nck];
     __syncthreads();
-    stage_kv<B, I8>(a.K, a.V, a.sK, a.sV, S, g, j, ks, vt, sk, sv);
+    st.store(ks, vt32, sks, svs);
     __syncthreads();
-    const int lim = qr + (i - j) * B;   // keys c > lim of this block are in the future
+    if (c + 1 < total) {
+      int j2, kc2;
+      if (chunk_row0(c + 1, j2, kc2)) st.load(a, (size_t)g * S + (size_t)j2 * B + kc2 * kChunk);
+    }
+    const int key0 = j * B + kc * kChunk;            // token index of the chunk's first key
+    if (!valid || !((mask >> hh) & 1u) || key0 > qtok0 + 31) continue;
+    const bool diag = key0 + kChunk - 1 > qtok0;     // some keys lie after some queries
+    const uint16_t *vt = (const uint16_t *)vt32;
 #pragma unroll 1
-    for (int kc = 0; kc < B / 128; ++kc) {
-      float x[4][16];
+    for (int kt = 0; kt < kChunk / 32; ++kt) {
+      const int kb = kt * 32;
+      float x[16];
+      raw_scores<I8>(ks, kb, qf, x);
+      if (I8) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        f32x16 accf;
-        i32x16 acci;
-        raw_scores<I8>(ks, L::KStride, kc * 128 + kt * 32, qf, accf, acci);
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 s4 = *(const f32x4 *)(sks + kb + 8 * q + 4 * hf);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = kc * 128 + kt * 32 + acc_row(r, lane);
-          float v = I8 ? (float)acci[r] * qscale * sk[c] : accf[r] * qscale;
-          x[kt][r] = (c > lim) ? kNegBig : v;
+          for (int e = 0; e < 4; ++e) x[4 * q + e] *= s4[e];
         }
       }
-      float mx = kNegBig;
+      if (diag) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, x[kt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mnew = fmaxf(m, mx);
-      const float alpha = exp2f(m - mnew);
-      float rs = 0.0f;
-      u32x4 pf[4][2];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        float pv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = (x[kt][r] == kNegBig) ? 0.0f : exp2f(x[kt][r] - mnew);
-          rs += e;
-          pv[r] = I8 ? e * sv[kc * 128 + kt * 32 + acc_row(r, lane)] : e;
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          pf[kt][s] = u32x4{pack_bf16x2(pv[8 * s + 0], pv[8 * s + 1]), pack_bf16x2(pv[8 * s + 2], pv[8 * s + 3]),
-                            pack_bf16x2(pv[8 * s + 4], pv[8 * s + 5]), pack_bf16x2(pv[8 * s + 6], pv[8 * s + 7])};
+        for (int r = 0; r < 16; ++r)
+          if (key0 + kb + acc_row(r, lane) > qtok) x[r] = -INFINITY;
       }
-      rs += __shfl_xor(rs, 32, 64);
-      l = l * alpha + rs;
-      m = mnew;
+      float mx = x[0];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qscale;
+      const bool grow = mx > m + kRescale;
+      if (__any(grow)) {
+        const float mnew = grow ? mx : m;
+        const float alpha = fast_exp2(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      }
+      float pv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pv[r] = fast_exp2(fmaf(x[r], qscale, -m));
+        l += pv[r];
+      }
+      if (I8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 s4 = *(const f32x4 *)(svs + kb + 8 * q + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pv[4 * q + e] *= s4[e];
+        }
+      }
+      u32x4 pf[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        pf[s2] = u32x4{pack_bf16x2(pv[8 * s2 + 0], pv[8 * s2 + 1]), pack_bf16x2(pv[8 * s2 + 2], pv[8 * s2 + 3]),
+                       pack_bf16x2(pv[8 * s2 + 4], pv[8 * s2 + 5]), pack_bf16x2(pv[8 * s2 + 6], pv[8 * s2 + 7])};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t *vrow = vt + (dt * 32 + (lane & 31)) * L::VStride + kc * 128 + 4 * hf;
+        const uint16_t *vrow = vt + (dt * 32 + (lane & 31)) * kVStride + kb + 4 * hf;
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            const uint16_t *q = vrow + kt * 32 + 16 * s;
-            const u32x2 v0 = *(const u32x2 *)q;
-            const u32x2 v1 = *(const u32x2 *)(q + 8);
-            o[dt] = mfma_bf16(u32x4{v0[0], v0[1], v1[0], v1[1]}, pf[kt][s], o[dt]);
-          }
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const uint16_t *q = vrow + 16 * s2;
+          const u32x2 v0 = *(const u32x2 *)q;
+          const u32x2 v1 = *(const u32x2 *)(q + 8);
+          o[dt] = mfma_bf16(u32x4{v0[0], v0[1], v1[0], v1[1]}, pf[s2], o[dt]);
+        }
       }
     }
   }
 
+  l += __shfl_xor(l, 32, 64);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   uint16_t *orow = a.O + tok * 128;
 #pragma unroll
@@ -229,31 +292,39 @@ __global__ void __launch_bounds__(2 * B) k_attn_rows(AttnArgs a) {
 template <int B>
 __global__ void __launch_bounds__(2 * B) k_probe_qk_i8(const uint8_t *Q, const uint8_t *K, int S,
                                                        int h, int g, int i, int j, int32_t *out) {
-  using L = AttnLds<B, true>;
-  __shared__ __attribute__((aligned(16))) uint8_t ks[L::KBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ks[B * KL<true>::Stride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint8_t *kb = K + ((size_t)g * S + (size_t)j * B) * 128;
   for (int c = threadIdx.x; c < B * 8; c += blockDim.x) {
     const int r = c / 8, col = c % 8;
-    *(u32x4 *)(ks + r * L::KStride + col * 16) = *(const u32x4 *)(kb + (size_t)r * 128 + col * 16);
+    *(u32x4 *)(ks + r * KL<true>::Stride + col * 16) = *(const u32x4 *)(kb + (size_t)r * 128 + col * 16);
   }
   __syncthreads();
   const int qr = wave * 32 + (lane & 31);
   u32x4 qf[8];
   load_q<true>(Q, (size_t)h * S + (size_t)i * B + qr, qf);
   for (int kt = 0; kt < B / 32; ++kt) {
-    f32x16 accf;
-    i32x16 acci;
-    raw_scores<true>(ks, L::KStride, kt * 32, qf, accf, acci);
+    float x[16];
+    raw_scores<true>(ks, kt * 32, qf, x);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[(size_t)(kt * 32 + acc_row(r, lane)) * B + qr] = acci[r];
+    for (int r = 0; r < 16; ++r) out[(size_t)(kt * 32 + acc_row(r, lane)) * B + qr] = (int32_t)x[r];
   }
 }
 
-template <int B, bool I8>
+template <int NT, bool I8>
 hipError_t run_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_rows<B, I8>), dim3(p.Hq * p.N), dim3(2 * B), 0, st, a);
+  hipLaunchKernelGGL((k_attn_jobs<NT, I8>), dim3(p.Hkv * p.N * a.parts), dim3(NT), 0, st, a);
   return hipGetLastError();
+}
+
+template <bool I8>
+hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
+  switch (64 * p.G * a.qpw) {
+    case 256: return run_attn<256, I8>(p, a, st);
+    case 512: return run_attn<512, I8>(p, a, st);
+    case 768: return run_attn<768, I8>(p, a, st);
+    default: return run_attn<1024, I8>(p, a, st);
+  }
 }
 
 }  // namespace
@@ -264,12 +335,19 @@ hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, c
   AttnArgs a;
   a.Q = (const uint8_t *)Q; a.K = (const uint8_t *)K; a.V = (const uint8_t *)V;
   a.sQ = sQ; a.sK = sK; a.sV = sV;
-  a.row_ptr = csr->row_ptr; a.col_idx = csr->col_idx;
+  a.job_ptr = csr->job_ptr; a.job_blk = csr->job_blk; a.job_order = csr->job_order;
+  a.job_mask = csr->job_mask;
   a.O = (uint16_t *)O;
-  a.S = p.S; a.N = p.N; a.Hq = p.Hq; a.G = p.G;
+  a.S = p.S; a.N = p.N; a.B = p.B; a.G = p.G;
   a.c2 = kLog2e / sqrtf((float)p.d);
-  if (p.B == 128) return i8 ? run_attn<128, true>(p, a, st) : run_attn<128, false>(p, a, st);
-  return i8 ? run_attn<256, true>(p, a, st) : run_attn<256, false>(p, a, st);
+  // query tiles per workgroup: the largest divisor of b/32 keeping G * qpw <= 12 waves
+  const int qtiles = p.B / 32;
+  int qpw = 1;
+  for (int d = 1; d <= qtiles; d <<= 1)
+    if (qtiles % d == 0 && p.G * d <= 12) qpw = d;
+  a.qpw = qpw;
+  a.parts = qtiles / qpw;
+  return i8 ? dispatch_attn<true>(p, a, st) : dispatch_attn<false>(p, a, st);
 }
 
 hipError_t launch_probe_qk_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
