@@ -6,21 +6,29 @@
 // (h, i) becomes CSR row h*N + i (key blocks ascending); the job of (KV group
 // g, query block i) is the union of the G rows of that group's query heads,
 // each entry carrying the bit mask of heads that use the block (the heads of
-// a group share K/V, which is what the staged blocks are reused for), and
-// jobs are ordered by decreasing work so the longest start first.
+// a group share K/V, which is what staged blocks are reused for), and jobs
+// are ordered by decreasing work so the longest start first.
 //
-// Vertical-slash rows are expanded here from the two selections:
+// Every row is handled as a bit set over key blocks.  Vertical-slash rows are
+// expanded on the fly from the two selections,
 //   J(h, i) = {j in V : j <= i} u {i - o : o in Sl, o <= i} u {0, i};
-// query-aware rows arrive as bit sets.
+// query-aware rows (and, in fp_build_jobs, every row of a given CSR) come
+// from the row bit-set buffer.  One wave handles one job: lanes own 32-bit
+// words of the rows, popcounts give the counts, OR gives the union.  Counts
+// are turned into offsets by one scan launch (rows and jobs side by side),
+// then a second pass over the same words writes columns and job entries.
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 
 namespace fp {
 namespace {
 
-__global__ void k_status_init(int32_t *status) { status[0] = 0; }
+__global__ void k_status_init(int32_t *status, unsigned int *bar) {
+  status[0] = 0;
+  if (bar) bar[0] = 0u;
+}
 
-// Bits j..j+31 (j may be negative) of a bit set of nw words; absent bits are 0.
+// Bits o..o+31 (o may be negative) of a bit set of nw words; absent bits are 0.
 __device__ __forceinline__ uint32_t bits32(const uint32_t *m, int nw, int o) {
   const int k = o >> 5, sh = o & 31;
   const uint32_t lo = (k >= 0 && k < nw) ? m[k] : 0u;
@@ -37,27 +45,27 @@ __device__ __forceinline__ uint32_t causal_mask_word(int i, int w) {
   return b == 31 ? 0xffffffffu : ((1u << (b + 1)) - 1u);
 }
 
-struct RowArgs {
-  int N, nw32, Hq;
-  const uint8_t *pattern;
-  const uint32_t *sel;     // [Hq][2][nw32]
-  const uint32_t *qabits;  // [Hq][N][nw32]
-  int32_t *row_ptr;
-  int32_t *col_idx;
-  int64_t cap;
-  int32_t *status;
+struct JobArgs {
+  int N, G, Hkv, nw32;
+  const uint8_t *pattern;   // NULL: every row comes from rowbits
+  const uint32_t *sel;      // [Hq][2][nw32]
+  const uint32_t *rowbits;  // [Hq][N][nw32]
+  int32_t *row_ptr, *col_idx;
+  int32_t *job_ptr, *job_blk;
+  uint32_t *job_mask;
+  int32_t *jwork;
 };
 
 // Word w of the bit set of row (h, i).
-__device__ __forceinline__ uint32_t row_word(const RowArgs &a, int h, int i, int w, bool qa) {
+__device__ __forceinline__ uint32_t row_word(const JobArgs &a, int h, int i, int w) {
   uint32_t word;
-  if (qa) {
-    word = a.qabits[((size_t)h * a.N + i) * a.nw32 + w];
+  if (!a.pattern || a.pattern[h] == FP_PATTERN_QUERY_AWARE) {
+    word = a.rowbits[((size_t)h * a.N + i) * a.nw32 + w];
   } else {
     const uint32_t *vm = a.sel + (size_t)h * 2 * a.nw32;
     const uint32_t *sm = vm + a.nw32;
-    // column j = 32w + k is on slash offset o = i - j; offsets for k = 31..0
-    // are the 32 consecutive bits starting at i - 32w - 31, bit-reversed.
+    // column j = 32w + k lies on slash offset o = i - j; the offsets for
+    // k = 31..0 are the 32 consecutive bits from i - 32w - 31, bit-reversed.
     const uint32_t s = __builtin_bitreverse32(bits32(sm, a.nw32, i - 32 * w - 31));
     word = vm[w] | s;
     if (w == 0) word |= 1u;
@@ -66,120 +74,165 @@ __device__ __forceinline__ uint32_t row_word(const RowArgs &a, int h, int i, int
   return word & causal_mask_word(i, w);
 }
 
-__global__ void k_rows_count(RowArgs a) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= a.Hq * a.N) return;
-  const int h = r / a.N, i = r % a.N;
-  const bool qa = a.pattern[h] == FP_PATTERN_QUERY_AWARE;
-  int cnt = 0;
-  for (int w = 0; w <= (i >> 5); ++w) cnt += __popc(row_word(a, h, i, w, qa));
-  a.row_ptr[r + 1] = cnt;
-}
+constexpr int kMaxG = 16;
+constexpr int kJobWaves = 4;
 
-__global__ void k_rows_write(RowArgs a) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= a.Hq * a.N) return;
-  const int h = r / a.N, i = r % a.N;
-  const bool qa = a.pattern[h] == FP_PATTERN_QUERY_AWARE;
-  int pos = a.row_ptr[r];
-  const int end = a.row_ptr[r + 1];
-  for (int w = 0; w <= (i >> 5) && pos < end; ++w) {
-    uint32_t m = row_word(a, h, i, w, qa);
-    while (m && pos < end) {
-      const int b = __ffs(m) - 1;
-      m &= m - 1u;
-      a.col_idx[pos++] = 32 * w + b;
-    }
-  }
-}
-
-// In-place scan: a[1..n] hold counts; afterwards a[k] = sum of the first k
-// counts, clamped to cap (a[0] = 0).  A total above cap sets `bit` in status.
-constexpr int kScanThreads = 1024;
-__global__ void __launch_bounds__(kScanThreads) k_scan_counts(int32_t *a, int n, int64_t cap,
-                                                              int32_t *status, uint32_t bit) {
-  __shared__ long long wsum[kScanThreads / 64];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int seg = (n + kScanThreads - 1) / kScanThreads;
-  const int beg = 1 + tid * seg, end = min(n + 1, beg + seg);
-  long long local = 0;
-  for (int k = beg; k < end; ++k) local += a[k];
-  // inclusive wave scan
-  long long x = local;
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const long long y = __shfl_up(x, o, 64);
+    const int y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  long long base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  long long run = base + x - local;     // exclusive prefix of this segment
-  for (int k = beg; k < end; ++k) {
-    run += a[k];
-    a[k] = (int32_t)(run < cap ? run : cap);
+  return x;
+}
+
+// Pass 1 (WRITE = false): row counts (when ROWS) and union counts / work per job.
+// Pass 2 (WRITE = true): columns of the rows (when ROWS) and job entries.
+template <bool ROWS, bool WRITE>
+__global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int job = blockIdx.x * kJobWaves + (threadIdx.x >> 6);
+  if (job >= a.Hkv * a.N) return;
+  const int g = job / a.N, i = job % a.N, G = a.G;
+  const int nwi = (i >> 5) + 1;
+  int rbase[kMaxG];
+  int ucarry = 0, work = 0, ucount = 0;
+  int rcount[kMaxG];
+#pragma unroll
+  for (int hh = 0; hh < kMaxG; ++hh) {
+    rcount[hh] = 0;
+    rbase[hh] = 0;
+    if (WRITE && ROWS && hh < G) rbase[hh] = a.row_ptr[(g * G + hh) * a.N + i];
   }
-  if (tid == 0) a[0] = 0;
-  if (tid == kScanThreads - 1) {
-    long long total = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) total += wsum[w];
-    if (total > cap) atomicOr((unsigned int *)status, bit);
+  const int jb = WRITE ? a.job_ptr[job] : 0, je = WRITE ? a.job_ptr[job + 1] : 0;
+  for (int w0 = 0; w0 < nwi; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t wd[kMaxG];
+    uint32_t U = 0u;
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh) {
+      wd[hh] = (hh < G && w < nwi) ? row_word(a, g * G + hh, i, w) : 0u;
+      U |= wd[hh];
+    }
+    if (!WRITE) {
+#pragma unroll
+      for (int hh = 0; hh < kMaxG; ++hh)
+        if (hh < G) rcount[hh] += wave_sum_int(__popc(wd[hh]));
+      ucount += wave_sum_int(__popc(U));
+    } else {
+      if (ROWS) {
+#pragma unroll
+        for (int hh = 0; hh < kMaxG; ++hh) {
+          if (hh >= G) continue;
+          const int r = (g * G + hh) * a.N + i;
+          const int c = __popc(wd[hh]);
+          const int incl = wave_incl_scan(c);
+          int pos = rbase[hh] + incl - c;
+          const int end = a.row_ptr[r + 1];
+          uint32_t m = wd[hh];
+          while (m && pos < end) {
+            a.col_idx[pos++] = 32 * w + (__ffs(m) - 1);
+            m &= m - 1u;
+          }
+          rbase[hh] += __shfl(incl, 63, 64);
+        }
+      }
+      const int c = __popc(U);
+      const int incl = wave_incl_scan(c);
+      int pos = jb + ucarry + incl - c;
+      uint32_t m = U;
+      while (m && pos < je) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        uint32_t hm = 0u;
+#pragma unroll
+        for (int hh = 0; hh < kMaxG; ++hh) hm |= ((wd[hh] >> b) & 1u) << hh;
+        a.job_blk[pos] = 32 * w + b;
+        a.job_mask[pos] = hm;
+        ++pos;
+      }
+      ucarry += __shfl(incl, 63, 64);
+    }
+  }
+  if (!WRITE && lane == 0) {
+#pragma unroll
+    for (int hh = 0; hh < kMaxG; ++hh) {
+      if (hh >= G) continue;
+      work += rcount[hh];
+      if (ROWS) a.row_ptr[(g * G + hh) * a.N + i + 1] = rcount[hh];
+    }
+    a.job_ptr[job + 1] = ucount;
+    a.jwork[job] = work;
   }
 }
 
-struct JobArgs {
-  int N, G, Hkv;
-  const int32_t *row_ptr, *col_idx;
-  int32_t *job_ptr, *job_blk;
-  uint32_t *job_mask;
-  int32_t *jwork;
+// Bit sets of the rows of a caller-supplied CSR (columns outside [0, i] are
+// dropped: such blocks hold no key a query of block i may attend to).
+__global__ void k_csr_to_bits(const int32_t *row_ptr, const int32_t *col_idx, int64_t ccap, int N,
+                              int nw32, int rows, uint32_t *rowbits) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= rows) return;
+  const int i = r % N;
+  uint32_t *dst = rowbits + (size_t)r * nw32;
+  for (int w = 0; w <= (i >> 5); ++w) dst[w] = 0u;
+  const int64_t e = min((int64_t)row_ptr[r + 1], ccap);
+  for (int64_t p = max((int64_t)row_ptr[r], (int64_t)0); p < e; ++p) {
+    const int j = col_idx[p];
+    if (j >= 0 && j <= i) dst[j >> 5] |= 1u << (j & 31);
+  }
+}
+
+// In-place scans, one array per workgroup: x[1..n] hold counts; afterwards
+// x[k] = sum of the first k counts, clamped to cap (x[0] = 0).  A total above
+// cap sets `bit` in status.  Tiles of 8 elements per thread, loaded coalesced.
+constexpr int kScanThreads = 1024;
+struct ScanJob {
+  int32_t *x;
+  int n;
   int64_t cap;
-  int64_t ccap;   // entries of col_idx
+  uint32_t bit;
 };
-
-constexpr int kMaxG = 16;
-
-// G-way merge of the rows of job (g, i); WRITE selects counting or writing.
-template <bool WRITE>
-__global__ void k_jobs(JobArgs a) {
-  const int job = blockIdx.x * blockDim.x + threadIdx.x;
-  if (job >= a.Hkv * a.N) return;
-  const int g = job / a.N, i = job % a.N;
-  int p[kMaxG], e[kMaxG];
-  int work = 0;
-  for (int hh = 0; hh < a.G; ++hh) {
-    const int r = (g * a.G + hh) * a.N + i;
-    e[hh] = (int)min((int64_t)a.row_ptr[r + 1], a.ccap);
-    p[hh] = min(a.row_ptr[r], e[hh]);
-    work += e[hh] - p[hh];
-  }
-  int cnt = 0;
-  int pos = WRITE ? a.job_ptr[job] : 0;
-  const int end = WRITE ? a.job_ptr[job + 1] : 0;
-  while (true) {
-    int cur = 0x7fffffff;
-    for (int hh = 0; hh < a.G; ++hh)
-      if (p[hh] < e[hh]) cur = min(cur, a.col_idx[p[hh]]);
-    if (cur == 0x7fffffff) break;
-    uint32_t m = 0u;
-    for (int hh = 0; hh < a.G; ++hh)
-      if (p[hh] < e[hh] && a.col_idx[p[hh]] == cur) {
-        m |= 1u << hh;
-        ++p[hh];
-      }
-    if (WRITE) {
-      if (pos >= end) break;
-      a.job_blk[pos] = cur;
-      a.job_mask[pos] = m;
-      ++pos;
-    } else {
-      ++cnt;
+__global__ void __launch_bounds__(kScanThreads) k_scan(ScanJob s0, ScanJob s1, int32_t *status) {
+  const ScanJob s = blockIdx.x == 0 ? s0 : s1;
+  __shared__ long long wsum[kScanThreads / 64];
+  constexpr int E = 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  long long carry = 0;
+  for (int base = 0; base < s.n; base += kScanThreads * E) {
+    int v[E];
+    long long loc = 0;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int k = base + tid * E + u;
+      v[u] = k < s.n ? s.x[1 + k] : 0;
+      loc += v[u];
     }
+    long long x = loc;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const long long y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    long long pre = carry;
+    for (int w = 0; w < wave; ++w) pre += wsum[w];
+    long long tile = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) tile += wsum[w];
+    long long run = pre + x - loc;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int k = base + tid * E + u;
+      run += v[u];
+      if (k < s.n) s.x[1 + k] = (int32_t)(run < s.cap ? run : s.cap);
+    }
+    carry += tile;
   }
-  if (!WRITE) {
-    a.job_ptr[job + 1] = cnt;
-    a.jwork[job] = work;
+  if (tid == 0) {
+    s.x[0] = 0;
+    if (carry > s.cap) atomicOr((unsigned int *)status, s.bit);
   }
 }
 
@@ -220,60 +273,59 @@ __global__ void __launch_bounds__(kSortThreads) k_jobs_order(const int32_t *jwor
   for (int k = tid; k < n; k += kSortThreads) order[k] = (int32_t)(0xffffffffu - (uint32_t)(keys[k] & 0xffffffffull));
 }
 
-}  // namespace
-
-hipError_t launch_status_init(int32_t *status, hipStream_t st) {
-  hipLaunchKernelGGL(k_status_init, dim3(1), dim3(1), 0, st, status);
-  return hipGetLastError();
-}
-
-hipError_t launch_rows_to_csr(const Plan &p, const fp_index_out *out, const Work &w,
-                              hipStream_t st) {
-  RowArgs a;
-  a.N = p.N; a.nw32 = p.nw32; a.Hq = p.Hq;
-  a.pattern = out->pattern; a.sel = w.sel; a.qabits = w.qabits;
-  a.row_ptr = out->row_ptr; a.col_idx = out->col_idx; a.cap = out->col_cap;
-  a.status = out->status;
-  const int rows = p.Hq * p.N;
-  hipLaunchKernelGGL(k_rows_count, dim3((rows + 255) / 256), dim3(256), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(kScanThreads), 0, st, out->row_ptr, rows,
-                     out->col_cap, out->status, (uint32_t)FP_STATUS_CSR_OVERFLOW);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_rows_write, dim3((rows + 255) / 256), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st) {
+hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st, bool rows) {
   JobArgs a;
-  a.N = p.N; a.G = p.G; a.Hkv = p.Hkv;
+  a.N = p.N; a.G = p.G; a.Hkv = p.Hkv; a.nw32 = p.nw32;
+  a.pattern = rows ? io->pattern : nullptr;
+  a.sel = w.sel;
+  a.rowbits = w.rowbits;
   a.row_ptr = io->row_ptr; a.col_idx = io->col_idx;
   a.job_ptr = io->job_ptr; a.job_blk = io->job_blk; a.job_mask = io->job_mask;
   a.jwork = w.jwork;
-  a.cap = io->job_cap;
-  a.ccap = io->col_cap;
-  const int jobs = p.Hkv * p.N;
-  const dim3 grid((jobs + 127) / 128), block(128);
-  hipLaunchKernelGGL(k_jobs<false>, grid, block, 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_counts, dim3(1), dim3(kScanThreads), 0, st, io->job_ptr, jobs,
-                     io->job_cap, io->status, (uint32_t)FP_STATUS_JOB_OVERFLOW);
+  const int jobs = p.Hkv * p.N, rcount = p.Hq * p.N;
+  const dim3 grid((jobs + kJobWaves - 1) / kJobWaves), block(64 * kJobWaves);
+  hipError_t e;
+  if (rows) hipLaunchKernelGGL((k_jobs<true, false>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_jobs<false, false>), grid, block, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_jobs<true>, grid, block, 0, st, a);
+  const ScanJob sj{io->job_ptr, jobs, io->job_cap, (uint32_t)FP_STATUS_JOB_OVERFLOW};
+  const ScanJob sr{io->row_ptr, rcount, io->col_cap, (uint32_t)FP_STATUS_CSR_OVERFLOW};
+  hipLaunchKernelGGL(k_scan, dim3(rows ? 2 : 1), dim3(kScanThreads), 0, st, sj, sr, io->status);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (rows) hipLaunchKernelGGL((k_jobs<true, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_jobs<false, true>), grid, block, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   int P = 1;
   while (P < jobs) P <<= 1;
   const size_t lds = jobs <= kSortMax ? sizeof(unsigned long long) * P : 0;
   if (lds > 0) {
-    e = hipFuncSetAttribute((const void *)k_jobs_order, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)lds);
+    e = hipFuncSetAttribute((const void *)k_jobs_order, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_jobs_order, dim3(1), dim3(kSortThreads), lds, st, w.jwork, jobs, p.N,
-                     p.Hkv, io->job_order);
+  hipLaunchKernelGGL(k_jobs_order, dim3(1), dim3(kSortThreads), lds, st, w.jwork, jobs, p.N, p.Hkv,
+                     io->job_order);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_status_init(int32_t *status, unsigned int *bar, hipStream_t st) {
+  hipLaunchKernelGGL(k_status_init, dim3(1), dim3(1), 0, st, status, bar);
+  return hipGetLastError();
+}
+
+hipError_t launch_rows_and_jobs(const Plan &p, const fp_index_out *out, const Work &w,
+                                hipStream_t st) {
+  return build(p, out, w, st, true);
+}
+
+hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st) {
+  const int rows = p.Hq * p.N;
+  hipLaunchKernelGGL(k_csr_to_bits, dim3((rows + 255) / 256), dim3(256), 0, st, io->row_ptr,
+                     io->col_idx, io->col_cap, p.N, p.nw32, rows, w.rowbits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return build(p, io, w, st, false);
 }
 
 }  // namespace fp

@@ -35,8 +35,10 @@ int make_plan(const fp_shape *s, Plan *p) {
   p->off_hi = o;     o = align_up(o + sizeof(float) * Hq * N);
   p->off_kbar = o;   o = align_up(o + sizeof(float) * Hkv * N * 128);
   p->off_sel = o;    o = align_up(o + sizeof(uint32_t) * Hq * 2 * p->nw32);
-  p->off_qabits = o; o = align_up(o + sizeof(uint32_t) * Hq * (size_t)N * p->nw32);
+  p->off_rowbits = o; o = align_up(o + sizeof(uint32_t) * Hq * (size_t)N * p->nw32);
+  p->off_qbar = o;   o = align_up(o + sizeof(float) * Hq * (size_t)N * 128);
   p->off_jwork = o;  o = align_up(o + sizeof(int32_t) * Hkv * N);
+  p->off_bar = o;    o = align_up(o + 256);
   p->total = o;
   return FP_OK;
 }
@@ -50,8 +52,10 @@ Work carve(const Plan &p, void *ws) {
   w.hi = (float *)(b + p.off_hi);
   w.kbar = (float *)(b + p.off_kbar);
   w.sel = (uint32_t *)(b + p.off_sel);
-  w.qabits = (uint32_t *)(b + p.off_qabits);
+  w.rowbits = (uint32_t *)(b + p.off_rowbits);
+  w.qbar = (float *)(b + p.off_qbar);
   w.jwork = (int32_t *)(b + p.off_jwork);
+  w.bar = (unsigned int *)(b + p.off_bar);
   return w;
 }
 
@@ -133,12 +137,11 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   Work w = carve(p, ws);
-  FP_LAUNCH(launch_status_init(out->status, st));
-  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, st));
+  FP_LAUNCH(launch_status_init(out->status, w.bar, st));
+  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st));
   FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st));
   FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st));
-  FP_LAUNCH(launch_rows_to_csr(p, out, w, st));
-  FP_LAUNCH(launch_jobs(p, out, w, st));
+  FP_LAUNCH(launch_rows_and_jobs(p, out, w, st));
   return FP_OK;
 }
 
@@ -163,7 +166,7 @@ int fp_build_jobs(const fp_shape *shape, fp_index_out *io, void *ws, size_t ws_b
   if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   Work w = carve(p, ws);
-  FP_LAUNCH(launch_status_init(io->status, st));
+  FP_LAUNCH(launch_status_init(io->status, nullptr, st));
   FP_LAUNCH(launch_jobs(p, io, w, st));
   return FP_OK;
 }

@@ -23,8 +23,10 @@ struct Plan {
   size_t off_hi;     // float  [Hq*N]      upper-split block mass
   size_t off_kbar;   // float  [Hkv*N*d]   mean-pooled key blocks
   size_t off_sel;    // u32    [Hq*2*nw32] vertical / slash selections (bit sets)
-  size_t off_qabits; // u32    [Hq*N*nw32] query-aware row bit sets
+  size_t off_rowbits; // u32   [Hq*N*nw32] row bit sets (query-aware rows; every row in fp_build_jobs)
+  size_t off_qbar;   // float  [Hq*N*d]    mean-pooled query blocks (query-aware heads)
   size_t off_jwork;  // int32  [Hkv*N]     work per grouped job
+  size_t off_bar;    // u32    [64]        grid-barrier counter of the single-pass statistics
   size_t total;
 };
 
@@ -35,8 +37,10 @@ int make_plan(const fp_shape *s, Plan *p);
 struct Work {
   float2 *part, *rowml;
   float *lo, *hi, *kbar;
-  uint32_t *sel, *qabits;
+  uint32_t *sel, *rowbits;
+  float *qbar;
   int32_t *jwork;
+  unsigned int *bar;
 };
 Work carve(const Plan &p, void *ws);
 
@@ -44,7 +48,8 @@ Work carve(const Plan &p, void *ws);
 // Statistics of the last query block against every key block
 // (two passes over K: row max / sum, then block mass).
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ,
-                           const void *K, const float *sK, const Work &w, hipStream_t st);
+                           const void *K, const float *sK, const Work &w, int32_t *status,
+                           hipStream_t st);
 // Per head: pooled estimate, divergence, pattern, vertical / slash selection.
 hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,
                               float gamma, float tau, const fp_index_out *out,
@@ -52,13 +57,13 @@ hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float
 // Query-aware rows: pooled queries of every block against pooled keys.
 hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
                         const uint8_t *pattern, const Work &w, hipStream_t st);
-// Bit-set rows -> CSR (count, scan, write).
-hipError_t launch_rows_to_csr(const Plan &p, const fp_index_out *out, const Work &w,
-                              hipStream_t st);
-// CSR -> grouped-query job list and its work order.
+// Row bit sets -> CSR rows, grouped-query job list and its work order.
+hipError_t launch_rows_and_jobs(const Plan &p, const fp_index_out *out, const Work &w,
+                                hipStream_t st);
+// Caller-supplied CSR -> grouped-query job list and its work order.
 hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st);
-// status[0] = 0
-hipError_t launch_status_init(int32_t *status, hipStream_t st);
+// status[0] = 0 and, when bar is not NULL, bar[0] = 0
+hipError_t launch_status_init(int32_t *status, unsigned int *bar, hipStream_t st);
 // Block-sparse attention over the CSR rows.
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,

@@ -4,105 +4,59 @@
 // value with ties broken by lower index first, whose sum is >= gamma * sum(x);
 // gamma >= 1 takes every index.
 //
-// Instead of sorting, the cut value theta = x_(k*) is found exactly by a
-// bisection over the bit patterns of non-negative floats (ordered like the
-// values): theta is the largest value t with sum_{x >= t} x >= gamma * T.
-// Everything above theta is taken, plus the lowest-index ties at theta that
-// are still needed.  Sums are fp64 with a fixed reduction order.
+// One wave does the whole search with fixed-order fp32 sums (lane partials,
+// then a butterfly), so results are reproducible run to run.  Two methods:
+//  * greedy: the maxima are extracted in exactly that order (value descending,
+//    lowest index among equal values) until the running sum reaches gamma*T
+//    -- used when that takes at most kGreedySteps extractions;
+//  * bisection: the cut value theta = x_(k*) is the largest t with
+//    sum_{x >= t} x >= gamma * T, found by bisection over the bit patterns of
+//    non-negative floats (ordered like the values); everything above theta
+//    is taken, plus the lowest-index ties at theta still needed.
 #pragma once
 
 #include "fp_common.hpp"
 
 namespace fp {
 
-__device__ __forceinline__ void set_bit_lds(uint32_t *m, int j) { atomicOr(&m[j >> 5], 1u << (j & 31)); }
-
-// Whole workgroup: x[0..n) in LDS (values >= 0), result bits in lmask (LDS,
-// ceil(n/32) words, cleared here).  redd: LDS double[>= nwaves], redi: int[>= nwaves].
-__device__ void block_select(const float *x, int n, float gamma, uint32_t *lmask, double *redd,
-                             int *redi) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int nw = (n + 31) >> 5;
-  for (int w = tid; w < nw; w += nt) lmask[w] = 0u;
-  double part = 0.0;
-  for (int j = tid; j < n; j += nt) part += (double)x[j];
-  const double T = block_sum(part, redd);   // contains barriers: lmask clear is visible
-  if (gamma >= 1.0f) {
-    for (int j = tid; j < n; j += nt) set_bit_lds(lmask, j);
-    __syncthreads();
-    return;
-  }
-  const double target = (double)gamma * T;
-  if (!(target > 0.0)) {                    // all-zero input: the first index in order is 0
-    if (tid == 0) lmask[0] = 1u;
-    __syncthreads();
-    return;
-  }
-  uint32_t lo = 0u, hi = 0x7f800000u;       // f(lo) >= target > f(hi)
-  while (hi - lo > 1u) {
-    const uint32_t mid = lo + ((hi - lo) >> 1);
-    const float th = __uint_as_float(mid);
-    double s = 0.0;
-    for (int j = tid; j < n; j += nt) s += (x[j] >= th) ? (double)x[j] : 0.0;
-    s = block_sum(s, redd);
-    if (s >= target) lo = mid; else hi = mid;
-  }
-  const float th = __uint_as_float(lo);
-  double a = 0.0;
-  int eq = 0;
-  for (int j = tid; j < n; j += nt) {
-    if (x[j] > th) a += (double)x[j];
-    eq += (x[j] == th) ? 1 : 0;
-  }
-  const double A = block_sum(a, redd);
-  const int neq = block_sum_int(eq, redi);
-  int c = 1;
-  while (c < neq && A + (double)c * (double)th < target) ++c;
-  for (int j = tid; j < n; j += nt)
-    if (x[j] > th || (neq <= c && x[j] == th)) set_bit_lds(lmask, j);
-  if (neq > c && tid == 0) {                // rare: only some ties at the cut are needed
-    int taken = 0;
-    for (int j = 0; j < n && taken < c; ++j)
-      if (x[j] == th) { set_bit_lds(lmask, j); ++taken; }
-  }
-  __syncthreads();
-}
-
-// One wave: x[0..n) in LDS (values >= 0).  Returns, per lane, nothing; the
-// selected bits are OR-ed into words[0 .. ceil(n/32)) (a per-wave LDS array
-// the caller clears).  Elements are visited as j = lane + 64 * k.
-__device__ void wave_select(const float *x, int n, float gamma, uint32_t *words) {
+// x[0..n) in LDS (values >= 0; elements visited as j = lane + 64 k).  Selected
+// bits are OR-ed into words[0 .. ceil(n/32)) (LDS, cleared by the caller).
+__device__ void wave_select_lds(const float *x, int n, float gamma, uint32_t *words) {
   const int lane = threadIdx.x & 63;
-  double part = 0.0;
-  for (int j = lane; j < n; j += 64) part += (double)x[j];
-  const double T = wave_sum(part);
-  if (gamma >= 1.0f || !(gamma * T > 0.0)) {
+  float part = 0.0f, mxl = 0.0f;
+  for (int j = lane; j < n; j += 64) {
+    part += x[j];
+    mxl = fmaxf(mxl, x[j]);
+  }
+  const float T = wave_sum(part);
+  const float target = gamma * T;
+  if (gamma >= 1.0f || !(target > 0.0f)) {   // everything, or an all-zero input (index 0)
     const bool all = gamma >= 1.0f;
     for (int j = lane; j < n; j += 64)
       if (all || j == 0) atomicOr(&words[j >> 5], 1u << (j & 31));
     return;
   }
-  const double target = (double)gamma * T;
-  uint32_t lo = 0u, hi = 0x7f800000u;
+  // f(lo) >= target (f(0) = T), f(hi) = 0 < target (hi is above the maximum)
+  uint32_t lo = 0u, hi = __float_as_uint(wave_max(mxl)) + 1u;
   while (hi - lo > 1u) {
     const uint32_t mid = lo + ((hi - lo) >> 1);
     const float th = __uint_as_float(mid);
-    double s = 0.0;
-    for (int j = lane; j < n; j += 64) s += (x[j] >= th) ? (double)x[j] : 0.0;
+    float s = 0.0f;
+    for (int j = lane; j < n; j += 64) s += (x[j] >= th) ? x[j] : 0.0f;
     s = wave_sum(s);
     if (s >= target) lo = mid; else hi = mid;
   }
   const float th = __uint_as_float(lo);
-  double a = 0.0;
+  float a = 0.0f;
   int eq = 0;
   for (int j = lane; j < n; j += 64) {
-    if (x[j] > th) a += (double)x[j];
+    if (x[j] > th) a += x[j];
     eq += (x[j] == th) ? 1 : 0;
   }
-  const double A = wave_sum(a);
+  const float A = wave_sum(a);
   const int neq = wave_sum_int(eq);
   int c = 1;
-  while (c < neq && A + (double)c * (double)th < target) ++c;
+  while (c < neq && A + (float)c * th < target) ++c;
   int carried = 0;                          // ties taken in index order
   for (int base = 0; base < n; base += 64) {
     const int j = base + lane;
@@ -114,6 +68,108 @@ __device__ void wave_select(const float *x, int n, float gamma, uint32_t *words)
     if (take) atomicOr(&words[j >> 5], 1u << (j & 31));
     carried += __popcll(eqm);
   }
+}
+
+constexpr int kGreedySteps = 24;
+
+__device__ __forceinline__ int wave_min_int(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m, 64));
+  return x;
+}
+
+// n <= 1024: the values live in registers (16 per lane).
+__device__ void wave_select_reg(const float *x, int n, float gamma, uint32_t *words) {
+  constexpr int VPL = 16;
+  const int lane = threadIdx.x & 63;
+  float v[VPL];
+  float part = 0.0f, mxl = 0.0f;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int j = lane + 64 * k;
+    v[k] = j < n ? x[j] : -1.0f;             // -1: not an element
+    if (j < n) {
+      part += v[k];
+      mxl = fmaxf(mxl, v[k]);
+    }
+  }
+  const float T = wave_sum(part);
+  const float target = gamma * T;
+  if (gamma >= 1.0f || !(target > 0.0f)) {
+    const bool all = gamma >= 1.0f;
+    for (int j = lane; j < n; j += 64)
+      if (all || j == 0) atomicOr(&words[j >> 5], 1u << (j & 31));
+    return;
+  }
+  // greedy extraction
+  uint32_t taken = 0u;
+  float cum = 0.0f;
+  bool done = false;
+  for (int step = 0; step < kGreedySteps && step < n; ++step) {
+    float bv = -1.0f;
+    int bk = -1;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+      if (!((taken >> k) & 1u) && v[k] > bv) {
+        bv = v[k];
+        bk = k;
+      }
+    const float M = wave_max(bv);
+    const int jmin = wave_min_int((bk >= 0 && bv == M) ? lane + 64 * bk : 0x7fffffff);
+    if (lane == (jmin & 63)) taken |= 1u << (jmin >> 6);
+    cum += M;
+    if (cum >= target) {
+      done = true;
+      break;
+    }
+  }
+  if (done) {
+#pragma unroll
+    for (int k = 0; k < VPL; ++k)
+      if ((taken >> k) & 1u) {
+        const int j = lane + 64 * k;
+        atomicOr(&words[j >> 5], 1u << (j & 31));
+      }
+    return;
+  }
+  // bisection
+  uint32_t lo = 0u, hi = __float_as_uint(wave_max(mxl)) + 1u;
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    const float th = __uint_as_float(mid);
+    float sacc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPL; ++k) sacc += (v[k] >= th) ? v[k] : 0.0f;   // v = -1 never counts
+    sacc = wave_sum(sacc);
+    if (sacc >= target) lo = mid; else hi = mid;
+  }
+  const float th = __uint_as_float(lo);
+  float a = 0.0f;
+  int eq = 0;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    if (v[k] > th) a += v[k];
+    eq += (v[k] == th) ? 1 : 0;
+  }
+  const float A = wave_sum(a);
+  const int neq = wave_sum_int(eq);
+  int c = 1;
+  while (c < neq && A + (float)c * th < target) ++c;
+  int carried = 0;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int j = lane + 64 * k;
+    const bool is_eq = (v[k] == th);
+    const uint64_t eqm = __ballot(is_eq);
+    const int rank = carried + __popcll(eqm & ((1ull << lane) - 1ull));
+    if (v[k] > th || (is_eq && rank < c)) atomicOr(&words[j >> 5], 1u << (j & 31));
+    carried += __popcll(eqm);
+  }
+}
+
+__device__ __forceinline__ void wave_select(const float *x, int n, float gamma, uint32_t *words) {
+  if (n <= 1024) wave_select_reg(x, n, gamma, words);
+  else wave_select_lds(x, n, gamma, words);
 }
 
 }  // namespace fp

@@ -41,27 +41,47 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
   float *ev = smem;                 // [N] logits, then softmax weights
   float *vv = ev + N;               // [N] vertical mass
   float *sv = vv + N;               // [N] slash mass
-  float *qb = sv + N;               // [2][128] partial sums, then mean query
-  uint32_t *msk = (uint32_t *)(qb + 256);   // [nw32]
+  float *qb = sv + N;               // [128] mean query of the last block
+  float *qpart = qb + 128;          // [32][128] row-group partial sums
+  uint32_t *msk = (uint32_t *)(qpart + 32 * 128);   // [2][nw32]
   __shared__ double redd[16];
-  __shared__ int redi[16];
   __shared__ float redf[16];
   const int tid = threadIdx.x, h = blockIdx.x, g = h / a.G;
 
-  // Mean of the last query block (two halves of the rows, then combined).
+  // Mean of the last query block: 16-byte loads, rows split over RG groups,
+  // group partials combined in order.
   {
-    const int dd = tid & 127, half = tid >> 7;
-    float s = 0.0f;
-    for (int r = half * (B / 2); r < (half + 1) * (B / 2); ++r) {
-      const size_t tok = (size_t)h * S + (S - B) + r;
-      if (!I8) s += bf16_to_f32(((const uint16_t *)a.Q)[tok * 128 + dd]);
-      else s += a.sQ[tok] * (float)((const int8_t *)a.Q)[tok * 128 + dd];
+    constexpr int RB = I8 ? 128 : 256, CPR = RB / 16, EPC = I8 ? 16 : 8, RG = kFinThreads / CPR;
+    const int ch = tid % CPR, rg = tid / CPR;
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+    const size_t tok0 = (size_t)h * S + (S - B);
+#pragma unroll 8
+    for (int r = rg; r < B; r += RG) {
+      const u32x4 v = *(const u32x4 *)(a.Q + (tok0 + r) * RB + ch * 16);
+      if (!I8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] += bf16lo(v[e]);
+          acc[2 * e + 1] += bf16hi(v[e]);
+        }
+      } else {
+        const float sc = a.sQ[tok0 + r];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += sc * (float)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xffu);
+      }
     }
-    qb[half * 128 + dd] = s;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) qpart[rg * 128 + ch * EPC + e] = acc[e];
+    __syncthreads();
+    if (tid < 128) {
+      float sum = 0.0f;
+      for (int q = 0; q < RG; ++q) sum += qpart[q * 128 + tid];
+      qb[tid] = sum / (float)B;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid < 128) qb[tid] = (qb[tid] + qb[128 + tid]) / (float)B;
-  __syncthreads();
 
   // Pooled logits against every mean-pooled key block.
   for (int j = tid; j < N; j += kFinThreads) {
@@ -113,16 +133,14 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
     }
   }
 
-  // Vertical-slash heads: select columns and diagonal offsets.
+  // Vertical-slash heads: wave 0 selects columns, wave 1 diagonal offsets.
   uint32_t *out = a.sel + (size_t)h * 2 * a.nw32;
-  for (int which = 0; which < 2; ++which) {
-    if (!qa) {
-      block_select(which == 0 ? vv : sv, N, a.gamma, msk, redd, redi);
-      for (int w = tid; w < a.nw32; w += kFinThreads) out[which * a.nw32 + w] = msk[w];
-      __syncthreads();
-    } else {
-      for (int w = tid; w < a.nw32; w += kFinThreads) out[which * a.nw32 + w] = 0u;
-    }
+  const int wave = tid >> 6;
+  if (wave < 2) {
+    uint32_t *m = msk + wave * a.nw32;
+    for (int w = tid & 63; w < a.nw32; w += 64) m[w] = 0u;
+    if (!qa) wave_select(wave == 0 ? vv : sv, N, a.gamma, m);
+    for (int w = tid & 63; w < a.nw32; w += 64) out[wave * a.nw32 + w] = m[w];
   }
 }
 
@@ -140,7 +158,10 @@ hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float
   a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
   a.pattern = out->pattern; a.jsd = out->jsd; a.stats = out->stats;
   a.sel = w.sel;
-  const size_t lds = sizeof(float) * (3 * (size_t)p.N + 256) + sizeof(uint32_t) * p.nw32;
+  const size_t lds = sizeof(float) * (3 * (size_t)p.N + 128 + 32 * 128) + sizeof(uint32_t) * 2 * p.nw32;
+  const void *fn = i8 ? (const void *)k_ig_finalize<true> : (const void *)k_ig_finalize<false>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   if (i8)
     hipLaunchKernelGGL(k_ig_finalize<true>, dim3(p.Hq), dim3(kFinThreads), lds, st, a);
   else

@@ -10,10 +10,12 @@
 //   J(h, i) = Sel(softmax_{j<=i}(e), gamma) u {0, i}
 // with Sel the cumulative-mass selection (explainer section 3.1).
 //
-// Only the Q blocks of heads the divergence test labelled query-aware are
-// read.  One workgroup per (head, R consecutive query blocks): the R pooled
-// queries share every pooled-key read; each wave then selects its rows and
-// writes them as bit sets (one bit per key block).
+// Two kernels.  k_pool_q streams the Q blocks of the heads the divergence
+// test labelled query-aware (and only those) and writes their means; it is
+// bound by HBM, so every thread keeps many 16-byte loads in flight.  k_qa_rows
+// scores R consecutive query blocks of one head against the pooled keys (the
+// R pooled queries share every pooled-key read), and each wave then selects
+// its rows and writes them as bit sets (one bit per key block).
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 #include "fp_select.hpp"
@@ -21,83 +23,90 @@
 namespace fp {
 namespace {
 
-struct QaArgs {
-  const uint8_t *Q;
-  const float *sQ;
-  int S, N, B, G, R, nw32;
-  float sigma, gamma;
-  const uint8_t *pattern;
-  const float *kbar;
-  uint32_t *qabits;
-};
-
 constexpr int kQaThreads = 256;
 
-template <bool I8>
-__global__ void __launch_bounds__(kQaThreads) k_ig_qa(QaArgs a) {
+struct PoolArgs {
+  const uint8_t *Q;
+  const float *sQ;
+  int S, N;
+  const uint8_t *pattern;
+  float *qbar;       // [Hq][N][128]
+};
+
+// One thread per (query block, 16-byte column): rows summed in order.
+template <int B, bool I8>
+__global__ void __launch_bounds__(kQaThreads) k_pool_q(PoolArgs a) {
+  const int h = blockIdx.y;
+  if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
+  constexpr int RB = I8 ? 128 : 256, CPR = RB / 16, EPC = I8 ? 16 : 8;
+  constexpr int BPW = kQaThreads / CPR;        // query blocks per workgroup
+  const int blk = blockIdx.x * BPW + threadIdx.x / CPR, ch = threadIdx.x % CPR;
+  if (blk >= a.N) return;
+  const size_t tok0 = (size_t)h * a.S + (size_t)blk * B;
+  const uint8_t *p = a.Q + tok0 * RB + ch * 16;
+  float acc[EPC];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+#pragma unroll 16
+  for (int r = 0; r < B; ++r) {
+    const u32x4 v = *(const u32x4 *)(p + (size_t)r * RB);
+    if (!I8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16lo(v[e]);
+        acc[2 * e + 1] += bf16hi(v[e]);
+      }
+    } else {
+      const float s = a.sQ[tok0 + r];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] += s * (float)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xffu);
+    }
+  }
+  float4 *dst = (float4 *)(a.qbar + ((size_t)h * a.N + blk) * 128 + ch * EPC);
+#pragma unroll
+  for (int e = 0; e < EPC / 4; ++e)
+    dst[e] = make_float4(acc[4 * e] / B, acc[4 * e + 1] / B, acc[4 * e + 2] / B, acc[4 * e + 3] / B);
+}
+
+struct QaArgs {
+  int N, G, R, nw32;
+  float sigma, gamma;
+  const uint8_t *pattern;
+  const float *qbar, *kbar;
+  uint32_t *rowbits;
+};
+
+__global__ void __launch_bounds__(kQaThreads) k_qa_rows(QaArgs a) {
   const int h = blockIdx.y;
   if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int N = a.N, B = a.B, S = a.S, R = a.R;
+  const int N = a.N, R = a.R;
   const int i0 = blockIdx.x * R;
   const int rows = min(R, N - i0);
   const int g = h / a.G;
   float *ev = smem;                       // [R][N] logits / weights
   float *qb = ev + (size_t)R * N;         // [R][128] pooled queries
-  float *tmp = qb + R * 128;              // [32][128] partial sums
-  uint32_t *words = (uint32_t *)(tmp + 32 * 128);   // [4 waves][nw32]
+  uint32_t *words = (uint32_t *)(qb + R * 128);   // [4 waves][nw32]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // 1. Pool each query block (16-byte loads; rows split over thread groups).
-  constexpr int EPC = I8 ? 16 : 8;        // elements per 16-byte chunk
-  constexpr int CPR = 128 / EPC;          // chunks per row
-  constexpr int RG = kQaThreads / CPR;    // row groups
-  const int ch = tid % CPR, rg = tid / CPR;
-  for (int r = 0; r < rows; ++r) {
-    float acc[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
-    const size_t tok0 = (size_t)h * S + (size_t)(i0 + r) * B;
-    for (int row = rg; row < B; row += RG) {
-      const size_t tok = tok0 + row;
-      const u32x4 v = *(const u32x4 *)(a.Q + tok * (I8 ? 128 : 256) + ch * 16);
-      if (!I8) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc[2 * e] += bf16lo(v[e]);
-          acc[2 * e + 1] += bf16hi(v[e]);
-        }
-      } else {
-        const float s = a.sQ[tok];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] += s * (float)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xff);
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) tmp[rg * 128 + ch * EPC + e] = acc[e];
-    __syncthreads();
-    if (tid < 128) {
-      float s = 0.0f;
-      for (int q = 0; q < RG; ++q) s += tmp[q * 128 + tid];
-      qb[r * 128 + tid] = s / (float)B;
-    }
-    __syncthreads();
-  }
+  for (int k = tid; k < rows * 128; k += kQaThreads) qb[k] = a.qbar[((size_t)h * N + i0) * 128 + k];
+  __syncthreads();
 
-  // 2. Pooled logits e[r][j] for j <= i0 + r.
+  // Pooled logits e[r][j] for j <= i0 + r.
   const int jmax = i0 + rows - 1;
   for (int j = tid; j <= jmax; j += kQaThreads) {
     const float4 *kr = (const float4 *)(a.kbar + ((size_t)g * N + j) * 128);
     float acc[8];
 #pragma unroll
     for (int r = 0; r < 8; ++r) acc[r] = 0.0f;
+#pragma unroll 8
     for (int c = 0; c < 32; ++c) {
       const float4 k4 = kr[c];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         if (r < rows) {
-          const float *q = qb + r * 128 + 4 * c;
-          acc[r] += q[0] * k4.x + q[1] * k4.y + q[2] * k4.z + q[3] * k4.w;
+          const float4 q = *(const float4 *)(qb + r * 128 + 4 * c);
+          acc[r] += q.x * k4.x + q.y * k4.y + q.z * k4.z + q.w * k4.w;
         }
       }
     }
@@ -107,7 +116,7 @@ __global__ void __launch_bounds__(kQaThreads) k_ig_qa(QaArgs a) {
   }
   __syncthreads();
 
-  // 3. One wave per row: softmax weights, selection, bit-set row.
+  // One wave per row: softmax weights, selection, bit-set row.
   uint32_t *wd = words + wave * a.nw32;
   for (int r = wave; r < rows; r += kQaThreads / 64) {
     const int i = i0 + r, n = i + 1;
@@ -123,37 +132,46 @@ __global__ void __launch_bounds__(kQaThreads) k_ig_qa(QaArgs a) {
       atomicOr(&wd[0], 1u);
       atomicOr(&wd[i >> 5], 1u << (i & 31));
     }
-    uint32_t *dst = a.qabits + ((size_t)h * N + i) * a.nw32;
+    uint32_t *dst = a.rowbits + ((size_t)h * N + i) * a.nw32;
     for (int w = lane; w < nwr; w += 64) dst[w] = wd[w];
   }
+}
+
+template <int B, bool I8>
+hipError_t run_pool(const Plan &p, const PoolArgs &a, hipStream_t st) {
+  constexpr int BPW = kQaThreads / ((I8 ? 128 : 256) / 16);
+  hipLaunchKernelGGL((k_pool_q<B, I8>), dim3((p.N + BPW - 1) / BPW, p.Hq), dim3(kQaThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
                         const uint8_t *pattern, const Work &w, hipStream_t st) {
+  PoolArgs pa;
+  pa.Q = (const uint8_t *)Q;
+  pa.sQ = sQ;
+  pa.S = p.S; pa.N = p.N;
+  pa.pattern = pattern;
+  pa.qbar = w.qbar;
+  hipError_t e;
+  if (p.B == 128) e = i8 ? run_pool<128, true>(p, pa, st) : run_pool<128, false>(p, pa, st);
+  else e = i8 ? run_pool<256, true>(p, pa, st) : run_pool<256, false>(p, pa, st);
+  if (e != hipSuccess) return e;
+
   QaArgs a;
-  a.Q = (const uint8_t *)Q;
-  a.sQ = sQ;
-  a.S = p.S; a.N = p.N; a.B = p.B; a.G = p.G; a.nw32 = p.nw32;
+  a.N = p.N; a.G = p.G; a.nw32 = p.nw32;
   a.R = p.N >= 2048 ? (p.N >= 4096 ? 2 : 4) : 8;
   a.sigma = 1.0f / sqrtf((float)p.d);
   a.gamma = gamma;
   a.pattern = pattern;
+  a.qbar = w.qbar;
   a.kbar = w.kbar;
-  a.qabits = w.qabits;
-  const size_t lds = sizeof(float) * ((size_t)a.R * p.N + a.R * 128 + 32 * 128) +
-                     sizeof(uint32_t) * 4 * p.nw32;
-  dim3 grid((p.N + a.R - 1) / a.R, p.Hq);
-  if (i8) {
-    hipError_t e = hipFuncSetAttribute((const void *)k_ig_qa<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ig_qa<true>, grid, dim3(kQaThreads), lds, st, a);
-  } else {
-    hipError_t e = hipFuncSetAttribute((const void *)k_ig_qa<false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_ig_qa<false>, grid, dim3(kQaThreads), lds, st, a);
-  }
+  a.rowbits = w.rowbits;
+  const size_t lds = sizeof(float) * ((size_t)a.R * p.N + a.R * 128) + sizeof(uint32_t) * 4 * p.nw32;
+  e = hipFuncSetAttribute((const void *)k_qa_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_qa_rows, dim3((p.N + a.R - 1) / a.R, p.Hq), dim3(kQaThreads), lds, st, a);
   return hipGetLastError();
 }
 

@@ -17,9 +17,12 @@
 // Every key block is also mean-pooled into kbar[g][j][:] for the pooled
 // estimate of Flex-Prefill's pattern test (explainer section 1.2).
 //
-// This version streams K twice: pass 1 gathers each row's running maximum
-// and exponential sum per chunk of key blocks, a combine step merges the
-// chunks, and pass 2 streams K again to bin the normalised attention.
+// Two forms.  The single-pass kernel (k_ig_stats1, below) streams K once and
+// keeps per-(row, block) partials on chip until one grid-wide barrier; it is
+// used whenever those partials fit in LDS with one workgroup per CU.  The
+// fallback streams K twice: pass 1 gathers each row's running maximum and
+// exponential sum per chunk of key blocks, a combine step merges the chunks,
+// and pass 2 streams K again to bin the normalised attention.
 //
 // Work split: one workgroup per (KV group g, contiguous chunk of key blocks);
 // all G query heads of the group share each staged key block.  Each wave owns
@@ -233,6 +236,236 @@ __global__ void k_ig_combine(const float2 *part, float2 *rowml, int rows, int nc
   rowml[r] = make_float2(M, L);
 }
 
+// ------------------------------------------------------------------ single pass
+//
+// K is streamed once.  Each workgroup keeps, for every last-block row of its
+// KV group and every key block of its chunk, the lower / upper split sums
+// exp2(x - m_ref) in LDS, where m_ref is the row's running reference maximum
+// (raised only when a score exceeds it by more than kHeadroom, rescaling the
+// partials already stored).  After one grid-wide barrier the per-chunk
+// (m_ref, sum) pairs of every row are merged in chunk order, identically in
+// every workgroup, and each workgroup normalises its own blocks.  All
+// workgroups must be resident at once (see the launcher below).
+
+constexpr float kHeadroom = 16.0f;
+
+struct Stat1Args {
+  StatArgs s;
+  unsigned int *bar;   // grid barrier counter (zeroed by the status kernel)
+  int32_t *status;
+};
+
+// Every workgroup arrives, then waits until all have; the wait is bounded so
+// every wave exits even if the launch did not keep all workgroups resident.
+__device__ void grid_barrier(unsigned int *bar, unsigned int nblocks, int32_t *status) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    atomicAdd(bar, 1u);
+    unsigned int spins = 0;
+    while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < nblocks) {
+      __builtin_amdgcn_s_sleep(4);
+      if (++spins > (1u << 24)) {
+        atomicOr((unsigned int *)status, (unsigned int)FP_STATUS_WAIT_TIMEOUT);
+        break;
+      }
+    }
+    __threadfence();
+  }
+  __syncthreads();
+}
+
+template <int B, int NT, bool I8>
+struct KStage {
+  static constexpr int RB = Tile<I8>::RowBytes, CPR = RB / 16, PIECES = B * CPR;
+  static constexpr int KP = (PIECES + NT - 1) / NT;
+  u32x4 r[KP];
+  float s;
+  __device__ __forceinline__ void load(const StatArgs &a, int g, int j) {
+    const size_t row0 = (size_t)g * a.S + (size_t)j * B;
+    const uint8_t *src = a.K + row0 * RB;
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int idx = threadIdx.x + u * NT;
+      if (idx < PIECES) r[u] = *(const u32x4 *)(src + (size_t)idx * 16);
+    }
+    if (I8 && threadIdx.x < B) s = a.sK[row0 + threadIdx.x];
+  }
+  __device__ __forceinline__ void store(uint8_t *ks, float *sk) const {
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      const int idx = threadIdx.x + u * NT;
+      if (idx < PIECES) *(u32x4 *)(ks + (idx / CPR) * Tile<I8>::Stride + (idx % CPR) * 16) = r[u];
+    }
+    if (I8 && threadIdx.x < B) sk[threadIdx.x] = s;
+  }
+};
+
+template <int B, int NT, int TPW, bool I8>
+__global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
+  const StatArgs &a = args.s;
+  constexpr int QT = B / 32, NWV = NT / 64, RG = NT / 128;
+  extern __shared__ __attribute__((aligned(16))) float part[];   // [NWV*TPW][cpb][32][2]
+  __shared__ __attribute__((aligned(16))) uint8_t ks[B * Tile<I8>::Stride];
+  __shared__ float sk[I8 ? B : 1];
+  __shared__ float kpart[RG][128];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunk = blockIdx.x, g = blockIdx.y;
+  const int G = a.G, S = a.S, N = a.N, cpb = a.cpb;
+  const int ntiles = G * QT;
+  const int j0 = chunk * cpb, nb = min(N, j0 + cpb) - j0;
+  constexpr int NTL = NWV * TPW;                                  // tile slots
+  float *red = part + (size_t)NTL * cpb * 64;                     // [cpb][NTL][2]
+
+  u32x4 qf[TPW][Tile<I8>::KS];
+  float qscale[TPW], mref[TPW], lsum[TPW];
+  int qrow[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave * TPW + u;
+    const int tt = t < ntiles ? t : 0;
+    const int h = g * G + tt / QT, row = (tt % QT) * 32 + (lane & 31);
+    qrow[u] = row;
+    const size_t tok = (size_t)h * S + (S - B) + row;
+    const uint8_t *qp = a.Q + tok * Tile<I8>::RowBytes + 16 * (lane >> 5);
+#pragma unroll
+    for (int s = 0; s < Tile<I8>::KS; ++s) qf[u][s] = *(const u32x4 *)(qp + 32 * s);
+    qscale[u] = (I8 ? a.sQ[tok] : 1.0f) * a.c2;
+    mref[u] = -1e30f;
+    lsum[u] = 0.0f;
+  }
+
+  KStage<B, NT, I8> stg;
+  if (nb > 0) stg.load(a, g, j0);
+  for (int jj = 0; jj < nb; ++jj) {
+    const int j = j0 + jj;
+    __syncthreads();
+    stg.store(ks, sk);
+    __syncthreads();
+    if (jj + 1 < nb) stg.load(a, g, j + 1);
+    const bool diag = (j == N - 1);
+
+    // mean-pooled key block: RG row groups, then combined in order
+    {
+      const int dd = threadIdx.x & 127, rg = threadIdx.x >> 7;
+      float s = 0.0f;
+      for (int r = rg; r < B; r += RG) {
+        if (!I8) s += bf16_to_f32(*(const uint16_t *)(ks + r * Tile<I8>::Stride + 2 * dd));
+        else s += sk[r] * (float)(int8_t)ks[r * Tile<I8>::Stride + dd];
+      }
+      kpart[rg][dd] = s;
+    }
+
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int t = wave * TPW + u;
+      if (t >= ntiles) continue;
+      float lo_acc = 0.0f, hi_acc = 0.0f;
+      float *prow = part + ((size_t)(wave * TPW + u) * cpb) * 64;   // [cpb][32][2] of this tile
+      const int tq = t % QT;            // this wave's 32 query rows are tq*32 .. tq*32+31
+      for (int kt = 0; kt < QT; ++kt) {
+        if (diag && kt > tq) break;     // keys after every query row of the tile
+        float x[16];
+        tile_scores<I8>(ks, sk, qf[u], 1.0f, kt, 1.0f, x);
+        const bool split = (kt == tq);  // the only key tile holding both c <= r and c > r
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          x[r] *= qscale[u];
+          if (split && diag && kt * 32 + acc_row(r, lane) > qrow[u]) x[r] = -INFINITY;
+          mx = fmaxf(mx, x[r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const bool grow = mx > mref[u] + kHeadroom;
+        if (__any(grow)) {
+          const float mnew = grow ? mx : mref[u];
+          const float alpha = fast_exp2(mref[u] - mnew);
+          lo_acc *= alpha;
+          hi_acc *= alpha;
+          lsum[u] *= alpha;
+          if (grow && lane < 32)
+            for (int q = 0; q < jj; ++q) {
+              prow[q * 64 + 2 * lane] *= alpha;
+              prow[q * 64 + 2 * lane + 1] *= alpha;
+            }
+          mref[u] = mnew;
+        }
+        if (!split) {
+          float e = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e += fast_exp2(x[r] - mref[u]);
+          if (kt < tq) lo_acc += e;
+          else hi_acc += e;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(x[r] - mref[u]);
+            if (kt * 32 + acc_row(r, lane) <= qrow[u]) lo_acc += e;
+            else hi_acc += e;
+          }
+        }
+      }
+      lo_acc += __shfl_xor(lo_acc, 32, 64);
+      hi_acc += __shfl_xor(hi_acc, 32, 64);
+      lsum[u] += lo_acc + hi_acc;
+      if (lane < 32) {
+        prow[jj * 64 + 2 * lane] = lo_acc;
+        prow[jj * 64 + 2 * lane + 1] = hi_acc;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+      float s = 0.0f;
+      for (int q = 0; q < RG; ++q) s += kpart[q][threadIdx.x];
+      a.kbar[((size_t)g * N + j) * 128 + threadIdx.x] = s / (float)B;
+    }
+  }
+
+  // per-chunk (m_ref, sum) of every row, then the grid-wide merge
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave * TPW + u;
+    if (t < ntiles && lane < 32) {
+      const int h = g * G + t / QT;
+      a.part[((size_t)h * B + qrow[u]) * a.nch + chunk] = make_float2(mref[u], lsum[u]);
+    }
+  }
+  grid_barrier(args.bar, gridDim.x * gridDim.y, args.status);
+
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int t = wave * TPW + u;
+    if (t >= ntiles) continue;
+    const int h = g * G + t / QT;
+    const float2 *pp = a.part + ((size_t)h * B + qrow[u]) * a.nch;
+    float M = kNegBig;
+    for (int c = 0; c < a.nch; ++c) M = fmaxf(M, pp[c].x);
+    float L = 0.0f;
+    for (int c = 0; c < a.nch; ++c) L += pp[c].y * exp2f(pp[c].x - M);
+    const float wr = exp2f(mref[u] - M) / ((float)B * L);
+    const float *prow = part + ((size_t)(wave * TPW + u) * cpb) * 64;
+    for (int q = 0; q < nb; ++q) {
+      // lanes 0..31: lower split of their row; lanes 32..63: upper split
+      float v = wr * prow[q * 64 + 2 * (lane & 31) + (lane >> 5)];
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      if ((lane & 31) == 0) red[(q * NTL + t) * 2 + (lane >> 5)] = v;
+    }
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < G * nb; k += NT) {
+    const int hh = k % G, q = k / G;
+    float lo = 0.0f, hi = 0.0f;
+    for (int tq = 0; tq < QT; ++tq) {
+      lo += red[(q * NTL + hh * QT + tq) * 2];
+      hi += red[(q * NTL + hh * QT + tq) * 2 + 1];
+    }
+    const size_t o = (size_t)(g * G + hh) * N + j0 + q;
+    a.lo[o] = lo;
+    a.hi[o] = hi;
+  }
+}
+
 template <int B, int TPW, bool I8>
 hipError_t run(const Plan &p, const StatArgs &a, hipStream_t st) {
   const int nwaves = (p.G * B / 32 + TPW - 1) / TPW;
@@ -261,10 +494,77 @@ hipError_t dispatch(const Plan &p, const StatArgs &a, hipStream_t st) {
   return run<256, 4, I8>(p, a, st);
 }
 
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Single pass when every workgroup (one per CU) can hold its chunk's partials
+// in LDS and all are co-resident; *used tells the caller whether it ran.
+template <int B, int NT, int TPW, bool I8>
+hipError_t run1(const Plan &p, StatArgs a, unsigned int *bar, int32_t *status, hipStream_t st,
+                bool *used) {
+  *used = false;
+  constexpr int NTL = NT / 64 * TPW;
+  const int cus = cu_count();
+  if (cus <= 0) return hipSuccess;
+  int nch = cus / p.Hkv;
+  if (nch > p.N) nch = p.N;
+  if (nch < 1 || nch > p.nch) return hipSuccess;
+  const int cpb = (p.N + nch - 1) / nch;
+  nch = (p.N + cpb - 1) / cpb;
+  const size_t lds = sizeof(float) * ((size_t)NTL * cpb * 64 + (size_t)cpb * NTL * 2);
+  const size_t static_lds = B * Tile<I8>::Stride + 4 * (NT / 128) * 128 + (I8 ? 4 * B : 4);
+  if (lds + static_lds > 160 * 1024) return hipSuccess;
+  const void *fn = (const void *)k_ig_stats1<B, NT, TPW, I8>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1 || (long)nch * p.Hkv > (long)per_cu * cus) return hipSuccess;
+  a.nch = nch;
+  a.cpb = cpb;
+  // The grid (one workgroup per CU, at most per_cu per CU) fits the device at
+  // once, and the launch follows the previous kernel of the stream, so all
+  // workgroups are resident together; the barrier's wait is bounded anyway.
+  Stat1Args args{a, bar, status};
+  hipLaunchKernelGGL((k_ig_stats1<B, NT, TPW, I8>), dim3(nch, p.Hkv), dim3(NT), lds, st, args);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  *used = true;
+  return hipSuccess;
+}
+
+template <bool I8>
+hipError_t dispatch1(const Plan &p, const StatArgs &a, unsigned int *bar, int32_t *status,
+                     hipStream_t st, bool *used) {
+  const int tiles = p.G * p.B / 32;
+  if (p.B == 128) {
+    if (tiles <= 4) return run1<128, 256, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 8) return run1<128, 512, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 12) return run1<128, 768, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 16) return run1<128, 1024, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 32) return run1<128, 1024, 2, I8>(p, a, bar, status, st, used);
+    return run1<128, 1024, 4, I8>(p, a, bar, status, st, used);
+  }
+  if (tiles <= 8) return run1<256, 512, 1, I8>(p, a, bar, status, st, used);
+  if (tiles <= 16) return run1<256, 1024, 1, I8>(p, a, bar, status, st, used);
+  if (tiles <= 32) return run1<256, 1024, 2, I8>(p, a, bar, status, st, used);
+  return run1<256, 1024, 4, I8>(p, a, bar, status, st, used);
+}
+
 }  // namespace
 
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
-                           const float *sK, const Work &w, hipStream_t st) {
+                           const float *sK, const Work &w, int32_t *status, hipStream_t st) {
   StatArgs a;
   a.Q = (const uint8_t *)Q;
   a.sQ = sQ;
@@ -273,6 +573,10 @@ hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *s
   a.S = p.S; a.N = p.N; a.G = p.G; a.nch = p.nch; a.cpb = p.cpb;
   a.c2 = kLog2e / sqrtf((float)p.d);
   a.part = w.part; a.rowml = w.rowml; a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
+  bool used = false;
+  hipError_t e = i8 ? dispatch1<true>(p, a, w.bar, status, st, &used)
+                    : dispatch1<false>(p, a, w.bar, status, st, &used);
+  if (e != hipSuccess || used) return e;
   return i8 ? dispatch<true>(p, a, st) : dispatch<false>(p, a, st);
 }
 
