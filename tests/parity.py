@@ -63,15 +63,19 @@ def gpu_rows(idx):
     return rp, ci
 
 
-def compare_index(idx, ref: oi.IndexResult, gamma: float, tau: float, stats_tol=(1e-3, 1e-6)):
-    """Assert the device index equals the oracle's under the boundary rule; return a summary."""
-    Hq, N = ref.Hq, ref.N
+def compare_index(idx, ref: oi.IndexResult, gamma: float, tau: float, stats_tol=(1e-3, 1e-6), heads=None):
+    """Assert the device index equals the oracle's under the boundary rule; return a summary.
+
+    heads: the query heads ref.heads holds, in order (default: every head)."""
+    Hq, N = idx.shape.Hq, ref.N
+    heads = list(range(Hq)) if heads is None else list(heads)
+    assert len(heads) == len(ref.heads)
     status = int(idx.status.item())
     assert status == 0, f"device status {status}"
     pat = idx.pattern.cpu().numpy()
     jsd = idx.jsd.cpu().numpy()
     summary = {"pattern_mismatch": 0, "row_diffs": 0, "boundary_rows": 0}
-    for h, hd in enumerate(ref.heads):
+    for h, hd in zip(heads, ref.heads):
         assert abs(jsd[h] - hd.D) <= 1e-4 + 1e-3 * abs(hd.D), (h, jsd[h], hd.D)
         if pat[h] != hd.pattern:
             assert abs(hd.D - tau) < RTOL_BOUNDARY * tau, (h, pat[h], hd.pattern, hd.D)
@@ -79,13 +83,13 @@ def compare_index(idx, ref: oi.IndexResult, gamma: float, tau: float, stats_tol=
     if idx.stats is not None:
         st = idx.stats.cpu().numpy().astype(np.float64)
         rt, at = stats_tol
-        for h, hd in enumerate(ref.heads):
+        for h, hd in zip(heads, ref.heads):
             np.testing.assert_allclose(st[0, h], hd.v, rtol=rt, atol=at, err_msg=f"v head {h}")
             np.testing.assert_allclose(st[1, h], hd.sl, rtol=rt, atol=at, err_msg=f"slash head {h}")
             np.testing.assert_allclose(st[2, h], hd.p, rtol=rt, atol=at, err_msg=f"p head {h}")
     rp, ci = gpu_rows(idx)
     assert rp.shape[0] == Hq * N + 1 and rp[0] == 0
-    for h, hd in enumerate(ref.heads):
+    for h, hd in zip(heads, ref.heads):
         if pat[h] != hd.pattern:
             continue   # compared by the caller against an oracle forced to the device's pattern
         if hd.pattern == oi.VS:
