@@ -10,10 +10,23 @@ planted-v1 synthetic Q/K/V, gamma = 0.9, tau = 0.1.
 
 Prints progress on stderr and ONE JSON line on stdout.  Only one GPU is used;
 --gpus above 1 exits with a message.
+
+Measured HBM traffic of the attention kernel (the `traffic` field) comes from
+two rocprofv3 counter passes over this script, scaled by the same counters on
+a copy of known size:
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D -o copy_FETCH_SIZE -- python3 bench.py --copy-calibration
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D -o copy_WRITE_SIZE -- python3 bench.py --copy-calibration
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D -o bench_FETCH_SIZE -- python3 bench.py --steps 1 --warmup 0 --no-cpu
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D -o bench_WRITE_SIZE -- python3 bench.py --steps 1 --warmup 0 --no-cpu
+    python bench.py --traffic-from D        # writes profiles/traffic_<config>.json
+The file records a hash of the attention source; once the kernel changes the
+field reads null until the passes are taken again.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import platform
@@ -33,6 +46,73 @@ CONFIG_TEXT = {
     "8b-64k": "Llama-3-8B-shaped attention layer, S=65536, b=256, Hq=32, Hkv=8, d=128, 3/4 heads vertical-slash",
     "w8a8-128k": "W8A8 Llama-3.2-3B-shaped attention layer, S=131072, b=128, Hq=24, Hkv=8, d=128",
 }
+
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_flexprefill_amd", "csrc", "attn.hip")
+ATTN_KERNEL = "k_attn"
+COPY_BYTES = 1 << 30
+
+
+def attn_source_hash() -> str:
+    return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+
+
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+
+
+def copy_calibration():
+    """A device copy of COPY_BYTES bytes (three times), for scaling the traffic counters."""
+    import torch
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(f"copied {COPY_BYTES} bytes x3", flush=True)
+
+
+def _counter(csv_path: str, name_part: str) -> float:
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(csv_path)) if name_part in r["Kernel_Name"]]
+    if not vals:
+        raise RuntimeError(f"no dispatch of {name_part} in {csv_path}")
+    return sum(vals) / len(vals)
+
+
+def traffic_from(d: str, config: str):
+    """Combine the four counter passes in directory d into profiles/traffic_<config>.json."""
+    f = lambda stem: os.path.join(d, f"{stem}_counter_collection.csv")
+    copy_kib = COPY_BYTES / 1024.0
+    fetch_factor = copy_kib / _counter(f("copy_FETCH_SIZE"), "copyBuffer")
+    write_factor = copy_kib / _counter(f("copy_WRITE_SIZE"), "copyBuffer")
+    fetch = _counter(f("bench_FETCH_SIZE"), ATTN_KERNEL)
+    write = _counter(f("bench_WRITE_SIZE"), ATTN_KERNEL)
+    rec = {"config": config, "kernel": ATTN_KERNEL, "attn_source_sha256": attn_source_hash(),
+           "fetch_size_kib": fetch, "write_size_kib": write,
+           "fetch_factor": fetch_factor, "write_factor": write_factor,
+           "bytes_per_launch": fetch * 1024 * fetch_factor + write * 1024 * write_factor,
+           "commands": [
+               f"rocprofv3 --pmc {c} --output-format csv -d D -o copy_{c} -- python3 bench.py --copy-calibration"
+               for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
+               f"rocprofv3 --pmc {c} --output-format csv -d D -o bench_{c} -- python3 bench.py --steps 1 --warmup 0 --no-cpu --config {config}"
+               for c in ("FETCH_SIZE", "WRITE_SIZE")]}
+    os.makedirs(os.path.dirname(traffic_file(config)), exist_ok=True)
+    json.dump(rec, open(traffic_file(config), "w"), indent=1)
+    print(json.dumps(rec))
+
+
+def measured_traffic(config: str):
+    """HBM bytes per attention launch from the counter passes, or None if stale or absent."""
+    try:
+        rec = json.load(open(traffic_file(config)))
+    except (OSError, ValueError):
+        return None
+    if rec.get("attn_source_sha256") != attn_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def log(*a):
@@ -61,7 +141,15 @@ def main(argv=None):
     ap.add_argument("--config", default="3b-128k", choices=sorted(CONFIG_TEXT))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to sample")
+    ap.add_argument("--copy-calibration", action="store_true", help="run the copy used to scale traffic counters")
+    ap.add_argument("--traffic-from", metavar="DIR", help="write profiles/traffic_<config>.json from counter CSVs")
     args = ap.parse_args(argv)
+    if args.copy_calibration:
+        copy_calibration()
+        return 0
+    if args.traffic_from:
+        traffic_from(args.traffic_from, args.config)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}); the path shards by KV group "
               "with no exchange, so there is no multi-GPU run to time here.", file=sys.stderr)
@@ -167,9 +255,9 @@ def main(argv=None):
         "data": "synthetic (planted-v1 generator, seed 0)",
         "config": {"workload": CONFIG_TEXT[c.name], "name": c.name, "S": c.S, "b": c.b, "Hq": c.Hq,
                    "Hkv": c.Hkv, "d": c.d, "gamma": c.gamma, "tau": c.tau, "seed": 0},
-        "roofline": {"bound": "mfma", "kernel": "k_attn (fp_attn)", "achieved": round(achieved_tf, 2),
+        "roofline": {"bound": "mfma", "kernel": "k_attn_jobs (fp_attn)", "achieved": round(achieved_tf, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved_tf / peak, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(c.name)},
         "roofline_index": {"bound": "hbm", "kernel": "fp_index (all kernels)", "achieved": round(idx_gbs, 1),
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(idx_gbs / PEAK_HBM_GBS, 4),
                            "algorithmic_bytes": ibytes},

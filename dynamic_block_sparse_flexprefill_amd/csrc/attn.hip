@@ -20,7 +20,7 @@
 // each key block is staged in LDS once (128 keys at a time) and used by every
 // head of the group whose mask bit is set.  One wave owns one (head, 32-query
 // tile).  The next 128-key chunk is loaded into registers while the current
-// one is computed.  Scores are computed transposed, S^T = K Q^T, on the
+// one is computed from the other of two LDS buffers.  Scores are computed transposed, S^T = K Q^T, on the
 // 32x32x16 matrix cores so that every lane owns one query row; its softmax
 // weights are then already the operand of O^T += V^T P^T (V is transposed
 // while staged).  Jobs run longest first (job_order).
@@ -41,7 +41,7 @@ struct AttnArgs {
 };
 
 constexpr int kChunk = 128;                  // keys staged per step
-constexpr int kVStride = kChunk + 4;         // bf16 elements per transposed V row
+constexpr int kVStride = kChunk + 8;         // bf16 elements per transposed V row (272 B)
 constexpr float kRescale = 8.0f;             // lazy-rescale headroom (log2 units)
 
 template <bool I8> struct KL {
@@ -51,7 +51,15 @@ template <bool I8> struct KL {
   static constexpr int VItems = (kChunk / 2) * (RB / 16);  // (key pair, 16-byte column)
 };
 
-// Register-staged copy of one 128-key chunk of K and V.
+// K rows are staged in a permuted order: LDS row rho holds key swap23(rho)
+// (bits 2 and 3 of the index exchanged, an involution).  In the transposed
+// score tile a lane then owns, for each 16-key step of the P.V product, 8
+// consecutive keys, so its V^T operand is one 16-byte LDS read.
+__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
+
+// Register-staged copy of one 128-key chunk of K and V.  A wave's V items
+// cover 32 consecutive key pairs x 2 column chunks, so its transposed 4-byte
+// LDS writes (row stride 68 words) hit 64 distinct banks.
 template <int NT, bool I8>
 struct Stage {
   using L = KL<I8>;
@@ -73,7 +81,7 @@ struct Stage {
     for (int u = 0; u < VP; ++u) {
       const int idx = tid + u * NT;
       if (idx < L::VItems) {
-        const int dc = idx % CPR, kp = idx / CPR;
+        const int kp = (idx & 31) | ((idx / (32 * CPR)) << 5), dc = (idx >> 5) % CPR;
         va[u] = *(const u32x4 *)(vbp + (size_t)(2 * kp) * L::RB + dc * 16);
         vb[u] = *(const u32x4 *)(vbp + (size_t)(2 * kp + 1) * L::RB + dc * 16);
       }
@@ -90,20 +98,18 @@ struct Stage {
 #pragma unroll
     for (int u = 0; u < KP; ++u) {
       const int idx = tid + u * NT;
-      if (idx < L::KPieces) *(u32x4 *)(ks + (idx / CPR) * L::Stride + (idx % CPR) * 16) = kr[u];
+      if (idx < L::KPieces) *(u32x4 *)(ks + swap23(idx / CPR) * L::Stride + (idx % CPR) * 16) = kr[u];
     }
 #pragma unroll
     for (int u = 0; u < VP; ++u) {
       const int idx = tid + u * NT;
       if (idx < L::VItems) {
-        const int dc = idx % CPR, kp = idx / CPR;
+        const int kp = (idx & 31) | ((idx / (32 * CPR)) << 5), dc = (idx >> 5) % CPR;
         if (!I8) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = (va[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const uint32_t hi = (vb[u][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            vt32[((dc * 8 + e) * kVStride >> 1) + kp] = lo | (hi << 16);
-          }
+          for (int e = 0; e < 8; ++e)   // {key 2kp, key 2kp+1} of column dc*8+e: one byte permute
+            vt32[((dc * 8 + e) * kVStride >> 1) + kp] =
+                __builtin_amdgcn_perm(vb[u][e >> 1], va[u][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
         } else {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
@@ -160,9 +166,9 @@ __device__ __forceinline__ void raw_scores(const uint8_t *ks, int key0, const u3
 
 template <int NT, bool I8>
 __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[kChunk * KL<I8>::Stride];
-  __shared__ __attribute__((aligned(16))) uint32_t vt32[128 * kVStride / 2];
-  __shared__ __attribute__((aligned(16))) float sks[I8 ? kChunk : 4], svs[I8 ? kChunk : 4];
+  __shared__ __attribute__((aligned(16))) uint8_t ks2[2][kChunk * KL<I8>::Stride];
+  __shared__ __attribute__((aligned(16))) uint32_t vt2[2][128 * kVStride / 2];
+  __shared__ __attribute__((aligned(16))) float sks2[2][I8 ? kChunk : 4], svs2[2][I8 ? kChunk : 4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
   const int N = a.N, S = a.S, B = a.B;
   const int job = a.job_order[blockIdx.x / a.parts], part = blockIdx.x % a.parts;
@@ -186,28 +192,43 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
   const int nck = B / kChunk;
   const int total = (p1 - p0) * nck;
   Stage<NT, I8> st;
+  // Chunks are visited in a rotated order, different per job, so that the
+  // workgroups do not all fetch the same (sink) blocks at the same moment.
+  const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
   auto chunk_row0 = [&](int c, int &j, int &kc) -> bool {
-    j = a.job_blk[p0 + c / nck];
-    kc = c % nck;
+    int cc = c + rot;
+    cc = cc >= total ? cc - total : cc;
+    j = a.job_blk[p0 + cc / nck];
+    kc = cc % nck;
     return j >= 0 && j < N;
   };
+  // Chunk c is computed from LDS buffer c % 2 while chunk c + 1 is written
+  // into the other buffer from registers loaded during chunk c - 1, and the
+  // loads for chunk c + 2 are issued: one barrier per chunk.
   {
     int j, kc;
     if (total > 0 && chunk_row0(0, j, kc)) st.load(a, (size_t)g * S + (size_t)j * B + kc * kChunk);
+    st.store(ks2[0], vt2[0], sks2[0], svs2[0]);
+    if (total > 1 && chunk_row0(1, j, kc)) st.load(a, (size_t)g * S + (size_t)j * B + kc * kChunk);
   }
+  __syncthreads();
   for (int c = 0; c < total; ++c) {
     int j, kc;
     const bool valid = chunk_row0(c, j, kc);
-    const uint32_t mask = a.job_mask[p0 + c / nck];
-    __syncthreads();
-    st.store(ks, vt32, sks, svs);
-    __syncthreads();
+    int cr = c + rot;
+    cr = cr >= total ? cr - total : cr;
+    const uint32_t mask = a.job_mask[p0 + cr / nck];
+    const int buf = c & 1;
     if (c + 1 < total) {
+      st.store(ks2[buf ^ 1], vt2[buf ^ 1], sks2[buf ^ 1], svs2[buf ^ 1]);
       int j2, kc2;
-      if (chunk_row0(c + 1, j2, kc2)) st.load(a, (size_t)g * S + (size_t)j2 * B + kc2 * kChunk);
+      if (c + 2 < total && chunk_row0(c + 2, j2, kc2)) st.load(a, (size_t)g * S + (size_t)j2 * B + kc2 * kChunk);
     }
+    const uint8_t *ks = ks2[buf];
+    const uint32_t *vt32 = vt2[buf];
+    const float *sks = sks2[buf], *svs = svs2[buf];
     const int key0 = j * B + kc * kChunk;            // token index of the chunk's first key
-    if (!valid || !((mask >> hh) & 1u) || key0 > qtok0 + 31) continue;
+    if (valid && ((mask >> hh) & 1u) && key0 <= qtok0 + 31) {
     const bool diag = key0 + kChunk - 1 > qtok0;     // some keys lie after some queries
     const uint16_t *vt = (const uint16_t *)vt32;
 #pragma unroll 1
@@ -215,10 +236,11 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
       const int kb = kt * 32;
       float x[16];
       raw_scores<I8>(ks, kb, qf, x);
+      // accumulator r of this lane holds key kb + key_of(r): rows 8(r/4)+4hf+r%4, permuted
       if (I8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 s4 = *(const f32x4 *)(sks + kb + 8 * q + 4 * hf);
+          const f32x4 s4 = *(const f32x4 *)(sks + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
 #pragma unroll
           for (int e = 0; e < 4; ++e) x[4 * q + e] *= s4[e];
         }
@@ -226,7 +248,7 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
       if (diag) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (key0 + kb + acc_row(r, lane) > qtok) x[r] = -INFINITY;
+          if (key0 + kb + swap23(acc_row(r, lane)) > qtok) x[r] = -INFINITY;
       }
       float mx = x[0];
 #pragma unroll
@@ -250,7 +272,7 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
       if (I8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 s4 = *(const f32x4 *)(svs + kb + 8 * q + 4 * hf);
+          const f32x4 s4 = *(const f32x4 *)(svs + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
 #pragma unroll
           for (int e = 0; e < 4; ++e) pv[4 * q + e] *= s4[e];
         }
@@ -262,16 +284,13 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
                        pack_bf16x2(pv[8 * s2 + 4], pv[8 * s2 + 5]), pack_bf16x2(pv[8 * s2 + 6], pv[8 * s2 + 7])};
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t *vrow = vt + (dt * 32 + (lane & 31)) * kVStride + kb + 4 * hf;
+        const uint16_t *vrow = vt + (dt * 32 + (lane & 31)) * kVStride + kb + 8 * hf;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const uint16_t *q = vrow + 16 * s2;
-          const u32x2 v0 = *(const u32x2 *)q;
-          const u32x2 v1 = *(const u32x2 *)(q + 8);
-          o[dt] = mfma_bf16(u32x4{v0[0], v0[1], v1[0], v1[1]}, pf[s2], o[dt]);
-        }
+        for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma_bf16(*(const u32x4 *)(vrow + 16 * s2), pf[s2], o[dt]);
       }
     }
+    }
+    __syncthreads();
   }
 
   l += __shfl_xor(l, 32, 64);

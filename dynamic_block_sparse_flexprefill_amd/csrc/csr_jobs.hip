@@ -236,24 +236,24 @@ __global__ void __launch_bounds__(kScanThreads) k_scan(ScanJob s0, ScanJob s1, i
   }
 }
 
-// Job order by decreasing work, ties by lower job index (bitonic sort in LDS).
+// Job order by decreasing work, ties by lower job index: every job has the
+// unique key (work << 32) | ~job.  Step 1 sorts each KV group's N keys in LDS
+// (one workgroup per group, bitonic); step 2 places every job at its global
+// rank, i.e. its position in its own group plus, for each other group, the
+// number of larger keys there (binary search).
 constexpr int kSortThreads = 1024;
 constexpr int kSortMax = 16384;
-__global__ void __launch_bounds__(kSortThreads) k_jobs_order(const int32_t *jwork, int n, int N,
-                                                             int Hkv, int32_t *order) {
+__device__ __forceinline__ unsigned long long job_key(const int32_t *jwork, int job) {
+  return ((unsigned long long)(uint32_t)jwork[job] << 32) | (0xffffffffu - (uint32_t)job);
+}
+
+__global__ void __launch_bounds__(kSortThreads) k_sort_group(const int32_t *jwork, int N,
+                                                             unsigned long long *sorted) {
   extern __shared__ unsigned long long keys[];
-  const int tid = threadIdx.x;
-  if (n > kSortMax) {   // too many to sort in LDS: latest query blocks first
-    for (int k = tid; k < n; k += kSortThreads) {
-      const int i = N - 1 - k / Hkv, g = k % Hkv;
-      order[k] = g * N + i;
-    }
-    return;
-  }
+  const int tid = threadIdx.x, g = blockIdx.x;
   int P = 1;
-  while (P < n) P <<= 1;
-  for (int k = tid; k < P; k += kSortThreads)
-    keys[k] = k < n ? (((unsigned long long)(uint32_t)jwork[k] << 32) | (0xffffffffu - (uint32_t)k)) : 0ull;
+  while (P < N) P <<= 1;
+  for (int k = tid; k < P; k += kSortThreads) keys[k] = k < N ? job_key(jwork, g * N + k) : 0ull;
   __syncthreads();
   for (int size = 2; size <= P; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
@@ -270,7 +270,33 @@ __global__ void __launch_bounds__(kSortThreads) k_jobs_order(const int32_t *jwor
       __syncthreads();
     }
   }
-  for (int k = tid; k < n; k += kSortThreads) order[k] = (int32_t)(0xffffffffu - (uint32_t)(keys[k] & 0xffffffffull));
+  for (int k = tid; k < N; k += kSortThreads) sorted[(size_t)g * N + k] = keys[k];
+}
+
+__global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, int32_t *order) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= Hkv * N) return;
+  const int g = e / N, k = e % N;
+  const unsigned long long key = sorted[e];
+  int rank = k;
+  for (int o = 0; o < Hkv; ++o) {
+    if (o == g) continue;
+    const unsigned long long *l = sorted + (size_t)o * N;   // descending
+    int lo = 0, hi = N;                                      // count of entries > key
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (l[mid] > key) lo = mid + 1; else hi = mid;
+    }
+    rank += lo;
+  }
+  order[rank] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+}
+
+// Fallback for N too large to sort a group in LDS: latest query blocks first.
+__global__ void k_order_fallback(int N, int Hkv, int32_t *order) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= Hkv * N) return;
+  order[k] = (k % Hkv) * N + (N - 1 - k / Hkv);
 }
 
 hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st, bool rows) {
@@ -295,15 +321,18 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   if (rows) hipLaunchKernelGGL((k_jobs<true, true>), grid, block, 0, st, a);
   else hipLaunchKernelGGL((k_jobs<false, true>), grid, block, 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  int P = 1;
-  while (P < jobs) P <<= 1;
-  const size_t lds = jobs <= kSortMax ? sizeof(unsigned long long) * P : 0;
-  if (lds > 0) {
-    e = hipFuncSetAttribute((const void *)k_jobs_order, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  if (p.N > kSortMax) {
+    hipLaunchKernelGGL(k_order_fallback, dim3((jobs + 255) / 256), dim3(256), 0, st, p.N, p.Hkv, io->job_order);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_jobs_order, dim3(1), dim3(kSortThreads), lds, st, w.jwork, jobs, p.N, p.Hkv,
-                     io->job_order);
+  int P = 1;
+  while (P < p.N) P <<= 1;
+  const size_t lds = sizeof(unsigned long long) * P;
+  e = hipFuncSetAttribute((const void *)k_sort_group, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_sort_group, dim3(p.Hkv), dim3(kSortThreads), lds, st, w.jwork, p.N, w.jkeys);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_rank_jobs, dim3((jobs + 255) / 256), dim3(256), 0, st, w.jkeys, p.N, p.Hkv, io->job_order);
   return hipGetLastError();
 }
 

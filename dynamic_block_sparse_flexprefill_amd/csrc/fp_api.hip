@@ -39,6 +39,7 @@ int make_plan(const fp_shape *s, Plan *p) {
   p->off_qbar = o;   o = align_up(o + sizeof(float) * Hq * (size_t)N * 128);
   p->off_jwork = o;  o = align_up(o + sizeof(int32_t) * Hkv * N);
   p->off_bar = o;    o = align_up(o + 256);
+  p->off_jkeys = o;  o = align_up(o + sizeof(unsigned long long) * Hkv * N);
   p->total = o;
   return FP_OK;
 }
@@ -56,6 +57,7 @@ Work carve(const Plan &p, void *ws) {
   w.qbar = (float *)(b + p.off_qbar);
   w.jwork = (int32_t *)(b + p.off_jwork);
   w.bar = (unsigned int *)(b + p.off_bar);
+  w.jkeys = (unsigned long long *)(b + p.off_jkeys);
   return w;
 }
 

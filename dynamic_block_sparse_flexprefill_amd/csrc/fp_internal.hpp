@@ -27,6 +27,7 @@ struct Plan {
   size_t off_qbar;   // float  [Hq*N*d]    mean-pooled query blocks (query-aware heads)
   size_t off_jwork;  // int32  [Hkv*N]     work per grouped job
   size_t off_bar;    // u32    [64]        grid-barrier counter of the single-pass statistics
+  size_t off_jkeys;  // u64    [Hkv*N]     per-group sorted job keys
   size_t total;
 };
 
@@ -41,6 +42,7 @@ struct Work {
   float *qbar;
   int32_t *jwork;
   unsigned int *bar;
+  unsigned long long *jkeys;
 };
 Work carve(const Plan &p, void *ws);
 
