@@ -307,6 +307,221 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path with direct-to-LDS staging.  Each 128-key chunk of K and V is
+// copied from global memory into LDS by global_load_lds_dwordx4 (lane L of one
+// instruction fills bytes [16L, 16L+16) of a 1 KiB LDS span, from any global
+// address the lane names), so staging costs no registers and no ALU work.
+//  * K keeps rows of 17 slots of 16 B (272 B: the 32 rows one score tile
+//    reads at one column fall in distinct bank groups); the pad slot receives
+//    a duplicate of the row's last slot.
+//  * V keeps its natural key-major rows of 256 B, the 16 B slot c of key row
+//    r stored at c ^ 4 (r & 3).  The V^T operand of O^T += V^T P^T is read
+//    with the LDS transpose read ds_read_b64_tr_b16: in each 16-lane block,
+//    lane i receives element i % 4 of the 4-element rows addressed by lanes
+//    i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.  Lane 4e + q of a block
+//    addresses key row e, columns 4q .. 4q + 3 of its 16-column slice, so the
+//    block receives 16 columns x 4 consecutive keys, transposed.
+namespace dl {
+constexpr int KSlots = 17;                          // 16 B slots per staged K row
+constexpr int KRow = KSlots * 16;                   // 272 B
+constexpr int KBuf = kChunk * KRow;                 // 34816 B
+constexpr int VBuf = kChunk * 256;                  // 32768 B
+constexpr int KLoads = kChunk * KSlots / 64;        // 34 one-KiB loads
+constexpr int VLoads = VBuf / 1024;                 // 32
+static_assert(kChunk * KSlots % 64 == 0, "K staging must be whole 1 KiB spans");
+}  // namespace dl
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// One direct load: the 64 lanes' 16 B from g fill LDS bytes [lds, lds + 1024).
+// Issued from inline assembly: the compiler then neither tracks the LDS write
+// (so it inserts no wait for it before unrelated LDS reads) nor reuses M0; the
+// caller waits for vmcnt(0) before the barrier that publishes the buffer.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_u8 *)p);
+}
+
+// Issue this wave's share of the direct loads of one chunk (rows from kg/vg).
+__device__ __forceinline__ void dl_issue(const uint8_t *kg, const uint8_t *vg, uint32_t kb, uint32_t vb,
+                                         int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  for (int u = wave; u < dl::KLoads + dl::VLoads; u += nw) {
+    if (u < dl::KLoads) {
+      const int s = 64 * u + lane, row = s / dl::KSlots, c = min(s - row * dl::KSlots, 15);
+      lds_dma16(kg + row * 256 + 16 * c, kb + 1024 * u);
+    } else {
+      const int v = u - dl::KLoads, row = 4 * v + (lane >> 4), c = (lane & 15) ^ (4 * (lane >> 4));
+      lds_dma16(vg + row * 256 + 16 * c, vb + 1024 * v);
+    }
+  }
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as a builtin
+// so that the compiler's own wait placement knows of it.
+constexpr int kWaitVm0 = 0x0f70;
+
+// An LDS byte address the compiler cannot fold constants into (keeps the
+// per-read offsets small enough for the instruction's immediate field).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+__device__ __forceinline__ u32x4 tr_pair(uint32_t addr) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(size_t)addr);
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(size_t)(addr + 8 * 256));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+template <int NT>
+__global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][dl::KBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][dl::VBuf];
+  const int lane = threadIdx.x & 63, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int NW = NT / 64;
+  const int N = a.N, S = a.S, B = a.B;
+  const int job = a.job_order[blockIdx.x / a.parts], part = blockIdx.x % a.parts;
+  const int g = job / N, i = job % N;
+  const int hh = wave / a.qpw, qt = part * a.qpw + wave % a.qpw;
+  const int h = g * a.G + hh;
+  const int qtok0 = i * B + qt * 32;
+  const int qtok = qtok0 + (lane & 31);
+  const size_t tok = (size_t)h * S + qtok;
+
+  u32x4 qf[8];
+  load_q<false>(a.Q, tok, qf);
+  const float qscale = a.c2;
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m = -1e30f, l = 0.0f;
+
+  const int p0 = a.job_ptr[job], p1 = a.job_ptr[job + 1];
+  const int nck = B / kChunk;
+  const int total = (p1 - p0) * nck;
+  // Chunks are visited in a rotated order, different per job, so that the
+  // workgroups do not all fetch the same (sink) blocks at the same moment.
+  const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
+  // Job-list entry of chunk c, fetched two chunks ahead of its use so that no
+  // wait for it falls inside the compute of a chunk.
+  struct Ent { int j, kc; uint32_t mask; };
+  // read through the constant address space: scalar loads, waited on only where used
+  const __attribute__((address_space(4))) int32_t *cblk = (const __attribute__((address_space(4))) int32_t *)a.job_blk;
+  const __attribute__((address_space(4))) uint32_t *cmask = (const __attribute__((address_space(4))) uint32_t *)a.job_mask;
+  auto fetch = [&](int c) -> Ent {
+    if (c >= total) return Ent{-1, 0, 0u};
+    int cr = c + rot;
+    cr = cr >= total ? cr - total : cr;
+    const int e = p0 + cr / nck;
+    return Ent{cblk[e], cr % nck, cmask[e]};
+  };
+  auto issue = [&](const Ent &en, int b) {
+    if (en.j >= 0 && en.j < N) {
+      const size_t row0 = (size_t)g * S + (size_t)en.j * B + en.kc * kChunk;
+      dl_issue(a.K + row0 * 256, a.V + row0 * 256, lds_addr(kbuf[b]), lds_addr(vbuf[b]), wave, NW);
+    }
+  };
+  // per-lane operand offsets: K rows (lane % 32) at column half hf; V^T per 32-column tile
+  const int kl = (lane & 31) * dl::KRow + 16 * hf;
+  const int j16 = lane & 15, bb = (lane >> 4) & 1;
+  int vl[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) vl[dt] = (4 * hf + (j16 >> 2)) * 256 + 64 * (dt ^ (j16 >> 2)) + 32 * bb + 8 * (j16 & 3);
+
+  Ent cur = fetch(0), nxt = fetch(1);
+  issue(cur, 0);
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __syncthreads();
+  for (int c = 0; c < total; ++c) {
+    const int buf = c & 1;
+    issue(nxt, buf ^ 1);                               // chunk c + 1 (no-op past the end)
+    const Ent nn = fetch(c + 2);
+    const int key0 = cur.j * B + cur.kc * kChunk;
+    if (cur.j >= 0 && cur.j < N && ((cur.mask >> hh) & 1u) && key0 <= qtok0 + 31) {
+      const bool diag = key0 + kChunk - 1 > qtok0;
+      const uint32_t kp = opaque(lds_addr(kbuf[buf]) + kl);
+      uint32_t vp[4];
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) vp[dt] = opaque(lds_addr(vbuf[buf]) + vl[dt]);
+#pragma unroll 1
+      for (int kt = 0; kt < kChunk / 32; ++kt) {
+        const int kb = kt * 32;
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s), qf[s], acc);
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = acc[r];
+        if (diag) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key0 + kb + acc_row(r, lane) > qtok) x[r] = -INFINITY;
+        }
+        float mx = x[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qscale;
+        }
+        const bool grow = mx > m + kRescale;
+        if (__any(grow)) {
+          const float mnew = grow ? mx : m;
+          const float alpha = fast_exp2(m - mnew);
+          m = mnew;
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+        }
+        u32x4 pf[2];
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(x[8 * s2 + 2 * w], qscale, -m)),
+                                            fast_exp2(fmaf(x[8 * s2 + 2 * w + 1], qscale, -m)));
+            pf[s2][w] = pw;
+            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
+                                                __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
+          }
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+            o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    cur = nxt;
+    nxt = nn;
+  }
+
+  l += __shfl_xor(l, 32, 64);
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  uint16_t *orow = a.O + tok * 128;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int d0 = dt * 32 + 8 * rq + 4 * hf;
+      const u32x2 w = u32x2{pack_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
+                            pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv)};
+      *(u32x2 *)(orow + d0) = w;
+    }
+}
+
 // out[c * B + r] = Q8[h, i*B + r] . K8[g, j*B + c] through the int8 tile code.
 template <int B>
 __global__ void __launch_bounds__(2 * B) k_probe_qk_i8(const uint8_t *Q, const uint8_t *K, int S,
@@ -336,8 +551,22 @@ hipError_t run_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int NT>
+hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL((k_attn_dl<NT>), dim3(p.Hkv * p.N * a.parts), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
 template <bool I8>
 hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
+  if (!I8) {
+    switch (64 * p.G * a.qpw) {
+      case 256: return run_attn_dl<256>(p, a, st);
+      case 512: return run_attn_dl<512>(p, a, st);
+      case 768: return run_attn_dl<768>(p, a, st);
+      default: return run_attn_dl<1024>(p, a, st);
+    }
+  }
   switch (64 * p.G * a.qpw) {
     case 256: return run_attn<256, I8>(p, a, st);
     case 512: return run_attn<512, I8>(p, a, st);
