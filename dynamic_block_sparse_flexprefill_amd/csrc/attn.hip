@@ -24,6 +24,8 @@
 // 32x32x16 matrix cores so that every lane owns one query row; its softmax
 // weights are then already the operand of O^T += V^T P^T (V is transposed
 // while staged).  Jobs run longest first (job_order).
+#include <algorithm>
+
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 
@@ -43,6 +45,9 @@ struct AttnArgs {
 constexpr int kChunk = 128;                  // keys staged per step
 constexpr int kVStride = kChunk + 8;         // bf16 elements per transposed V row (272 B)
 constexpr float kRescale = 8.0f;             // lazy-rescale headroom (log2 units)
+// Headroom of the bf16 kernel: weights stay below 2^24 before a rescale, so
+// O^T (at most 2^24 times the key count times max |V|) stays far inside fp32.
+constexpr float kRescaleDl = 24.0f;
 
 template <bool I8> struct KL {
   static constexpr int RB = I8 ? 128 : 256;            // global bytes per key row
@@ -253,7 +258,7 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
       float mx = x[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * qscale;
+      mx = fmaxf(mx, xor32(mx)) * qscale;
       const bool grow = mx > m + kRescale;
       if (__any(grow)) {
         const float mnew = grow ? mx : m;
@@ -293,7 +298,7 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
     __syncthreads();
   }
 
-  l += __shfl_xor(l, 32, 64);
+  l += xor32(l);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   uint16_t *orow = a.O + tok * 128;
 #pragma unroll
@@ -381,56 +386,89 @@ __device__ __forceinline__ u32x4 tr_pair(uint32_t addr) {
   return u32x4{l2[0], l2[1], h2[0], h2[1]};
 }
 
+// A load of a value every lane shares, kept on the vector memory path (an
+// opaque VGPR zero in the address): such loads are waited on through vmcnt,
+// which the chunk loop only drains at its barriers.  Scalar loads would share
+// lgkmcnt with the LDS operand reads and stall the first of them.
+template <typename T>
+__device__ __forceinline__ T vload(const T *p) {
+  int z = 0;
+  asm volatile("" : "+v"(z));
+  return p[z];
+}
+__device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// One unit of work: job (KV group g, query block i) in the job order, query
+// tile share `part` of it, its first job-list entry p0, chunk count and the
+// chunk the rotated visiting order starts from.
+struct Unit {
+  int u, g, i, part, p0, total, rot;
+  bool empty;                                  // no job-list entry: one chunk that computes nothing
+};
+
+// Job-list entry of one chunk: key block jv and head mask maskv (as loaded,
+// made scalar where used), 128-key chunk kc of the block, KV group g.
+struct Ent {
+  int jv;
+  uint32_t maskv;
+  int kc, g;
+};
+
+// Persistent form: one workgroup per compute unit takes units in job order
+// (the first two statically, later ones from an atomic counter) and runs one
+// continuous chunk stream across them, so the next unit's first chunk is
+// loaded while the current unit's last chunk is computed.  A workgroup stops
+// at the first unit index past the end; indices only grow, so none is lost.
 template <int NT>
-__global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a) {
+__global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, int nunits, unsigned int *ctr) {
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][dl::KBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][dl::VBuf];
+  __shared__ int s_claim[2];
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int NW = NT / 64;
   const int N = a.N, S = a.S, B = a.B;
-  const int job = a.job_order[blockIdx.x / a.parts], part = blockIdx.x % a.parts;
-  const int g = job / N, i = job % N;
-  const int hh = wave / a.qpw, qt = part * a.qpw + wave % a.qpw;
-  const int h = g * a.G + hh;
-  const int qtok0 = i * B + qt * 32;
-  const int qtok = qtok0 + (lane & 31);
-  const size_t tok = (size_t)h * S + qtok;
-
-  u32x4 qf[8];
-  load_q<false>(a.Q, tok, qf);
+  const int nck = B / kChunk;
+  const int hh = wave / a.qpw;
   const float qscale = a.c2;
 
-  f32x16 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m = -1e30f, l = 0.0f;
-
-  const int p0 = a.job_ptr[job], p1 = a.job_ptr[job + 1];
-  const int nck = B / kChunk;
-  const int total = (p1 - p0) * nck;
-  // Chunks are visited in a rotated order, different per job, so that the
-  // workgroups do not all fetch the same (sink) blocks at the same moment.
-  const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
-  // Job-list entry of chunk c, fetched two chunks ahead of its use so that no
-  // wait for it falls inside the compute of a chunk.
-  struct Ent { int j, kc; uint32_t mask; };
-  // read through the constant address space: scalar loads, waited on only where used
-  const __attribute__((address_space(4))) int32_t *cblk = (const __attribute__((address_space(4))) int32_t *)a.job_blk;
-  const __attribute__((address_space(4))) uint32_t *cmask = (const __attribute__((address_space(4))) uint32_t *)a.job_mask;
-  auto fetch = [&](int c) -> Ent {
-    if (c >= total) return Ent{-1, 0, 0u};
-    int cr = c + rot;
-    cr = cr >= total ? cr - total : cr;
-    const int e = p0 + cr / nck;
-    return Ent{cblk[e], cr % nck, cmask[e]};
+  auto unit_from = [&](int u, const int4 &t) -> Unit {
+    Unit x{u, 0, 0, 0, 0, 0, 0, true};
+    if (u >= nunits) return x;
+    const int job = sgpr(t.x);
+    x.part = u % a.parts;
+    x.g = job / N;
+    x.i = job - x.g * N;
+    x.p0 = sgpr(t.y);
+    x.total = sgpr(t.z);
+    x.rot = sgpr(t.w);
+    x.empty = x.total == 0;
+    if (x.empty) x.total = 1;
+    return x;
+  };
+  auto fetch = [&](const Unit &x, int c) -> Ent {
+    if (c >= x.total || x.empty) return Ent{-1, 0u, 0, 0};
+    int cr = c + x.rot;
+    cr = cr >= x.total ? cr - x.total : cr;
+    const int e = x.p0 + cr / nck;
+    return Ent{vload(a.job_blk + e), vload(a.job_mask + e), cr % nck, x.g};
   };
   auto issue = [&](const Ent &en, int b) {
-    if (en.j >= 0 && en.j < N) {
-      const size_t row0 = (size_t)g * S + (size_t)en.j * B + en.kc * kChunk;
+    const int j = sgpr(en.jv);
+    if (j >= 0 && j < N) {
+      const size_t row0 = (size_t)en.g * S + (size_t)j * B + en.kc * kChunk;
       dl_issue(a.K + row0 * 256, a.V + row0 * 256, lds_addr(kbuf[b]), lds_addr(vbuf[b]), wave, NW);
     }
   };
+
+  if ((int)blockIdx.x >= nunits) return;
+  Unit cur = unit_from(blockIdx.x, vload(utab + blockIdx.x));
+  int nxt_id = blockIdx.x + gridDim.x;                // claimed unit that follows cur
+  Unit nxt{nunits, 0, 0, 0, 0, 0, 0, true};
+  int parity = 0;
+  Ent e0 = fetch(cur, 0), e1 = fetch(cur, 1);
+  issue(e0, 0);
+
   // per-lane operand offsets: K rows (lane % 32) at column half hf; V^T per 32-column tile
   const int kl = (lane & 31) * dl::KRow + 16 * hf;
   const int j16 = lane & 15, bb = (lane >> 4) & 1;
@@ -438,88 +476,132 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) vl[dt] = (4 * hf + (j16 >> 2)) * 256 + 64 * (dt ^ (j16 >> 2)) + 32 * bb + 8 * (j16 & 3);
 
-  Ent cur = fetch(0), nxt = fetch(1);
-  issue(cur, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  __syncthreads();
-  for (int c = 0; c < total; ++c) {
-    const int buf = c & 1;
-    issue(nxt, buf ^ 1);                               // chunk c + 1 (no-op past the end)
-    const Ent nn = fetch(c + 2);
-    const int key0 = cur.j * B + cur.kc * kChunk;
-    if (cur.j >= 0 && cur.j < N && ((cur.mask >> hh) & 1u) && key0 <= qtok0 + 31) {
-      const bool diag = key0 + kChunk - 1 > qtok0;
-      const uint32_t kp = opaque(lds_addr(kbuf[buf]) + kl);
-      uint32_t vp[4];
+  int kk = 0;                                    // chunks streamed so far (LDS buffer parity)
+  while (true) {
+    // unit start: Q fragments, the table entry of the next unit and a claim for the one after it
+    // are all in flight together and waited for once
+    unsigned int claim = 0u;
+    if (threadIdx.x == 0) {
+      int z = 0;                                   // per-lane address: a plain returning atomic, waited below
+      asm volatile("" : "+v"(z));
+      claim = atomicAdd(ctr + z, 1u);
+    }
+    const int4 ntab = vload(utab + min(nxt_id, nunits - 1));   // (ignored past the end)
+    const int qtok0 = cur.i * B + (cur.part * a.qpw + wave % a.qpw) * 32;
+    const int qtok = qtok0 + (lane & 31);
+    const size_t tok = (size_t)(cur.g * a.G + hh) * S + qtok;
+    u32x4 qf[8];
+    load_q<false>(a.Q, tok, qf);
+    f32x16 o[4];
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) vp[dt] = opaque(lds_addr(vbuf[buf]) + vl[dt]);
+    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    float m = -1e30f, l = 0.0f;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    if (threadIdx.x == 0) s_claim[parity] = 2 * gridDim.x + (int)claim;
+    nxt = unit_from(nxt_id, ntab);
+    auto stream = [&](int c) -> Ent { return c < cur.total ? fetch(cur, c) : fetch(nxt, c - cur.total); };
+    if (cur.total == 1) e1 = fetch(nxt, 0);        // the stream's next chunk lies in nxt, unknown until now
+    __syncthreads();
+
+    for (int c = 0; c < cur.total; ++c, ++kk) {
+      const int buf = kk & 1;
+      issue(e1, buf ^ 1);                          // the next chunk of the stream (no-op past its end)
+      const Ent e2 = stream(c + 2);
+      const int j0 = sgpr(e0.jv);
+      const uint32_t mask0 = (uint32_t)sgpr((int)e0.maskv);
+      const int key0 = j0 * B + e0.kc * kChunk;
+      if (j0 >= 0 && j0 < N && ((mask0 >> hh) & 1u) && key0 <= qtok0 + 31) {
+        const bool diag = key0 + kChunk - 1 > qtok0;
+        const uint32_t kp = opaque(lds_addr(kbuf[buf]) + kl);
+        uint32_t vp[4];
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) vp[dt] = opaque(lds_addr(vbuf[buf]) + vl[dt]);
 #pragma unroll 1
-      for (int kt = 0; kt < kChunk / 32; ++kt) {
-        const int kb = kt * 32;
-        f32x16 acc = {};
+        for (int kt = 0; kt < kChunk / 32; ++kt) {
+          const int kb = kt * 32;
+          f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-          acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s), qf[s], acc);
-        float x[16];
+          for (int s = 0; s < 8; ++s)
+            acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s), qf[s], acc);
+          float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = acc[r];
-        if (diag) {
+          for (int r = 0; r < 16; ++r) x[r] = acc[r];
+          if (diag) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key0 + kb + acc_row(r, lane) > qtok) x[r] = -INFINITY;
-        }
-        float mx = x[0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-        {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qscale;
-        }
-        const bool grow = mx > m + kRescale;
-        if (__any(grow)) {
-          const float mnew = grow ? mx : m;
-          const float alpha = fast_exp2(m - mnew);
-          m = mnew;
-          l *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-        }
-        u32x4 pf[2];
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(x[8 * s2 + 2 * w], qscale, -m)),
-                                            fast_exp2(fmaf(x[8 * s2 + 2 * w + 1], qscale, -m)));
-            pf[s2][w] = pw;
-            l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
-                                                __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
+            for (int r = 0; r < 16; ++r)
+              if (key0 + kb + acc_row(r, lane) > qtok) x[r] = -INFINITY;
           }
+          float mx = x[0];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+          {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qscale;
+          }
+          const bool grow = mx > m + kRescaleDl;
+          if (__any(grow)) {
+            const float mnew = grow ? mx : m;
+            const float alpha = fast_exp2(m - mnew);
+            m = mnew;
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+          }
+          u32x4 pf[2];
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2)
-            o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(x[8 * s2 + 2 * w], qscale, -m)),
+                                              fast_exp2(fmaf(x[8 * s2 + 2 * w + 1], qscale, -m)));
+              pf[s2][w] = pw;
+              l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
+                                                  __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
+            }
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+              o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
+        }
       }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      __syncthreads();
+      e0 = e1;
+      e1 = e2;
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    cur = nxt;
-    nxt = nn;
-  }
 
-  l += __shfl_xor(l, 32, 64);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  uint16_t *orow = a.O + tok * 128;
+    l += xor32(l);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    uint16_t *orow = a.O + tok * 128;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = dt * 32 + 8 * rq + 4 * hf;
-      const u32x2 w = u32x2{pack_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
-                            pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv)};
-      *(u32x2 *)(orow + d0) = w;
-    }
+      for (int rq = 0; rq < 4; ++rq) {
+        const int d0 = dt * 32 + 8 * rq + 4 * hf;
+        const u32x2 w = u32x2{pack_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
+                              pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv)};
+        *(u32x2 *)(orow + d0) = w;
+      }
+
+    cur = nxt;                                     // (every unit has a chunk barrier, which published the claim)
+    if (cur.u >= nunits) break;
+    nxt_id = s_claim[parity];
+    parity ^= 1;
+  }
+}
+
+// Unit table {job, first job-list entry, chunks, rotated start} and a zeroed claim counter.
+__global__ void k_attn_prep(const int32_t *job_order, const int32_t *job_ptr, int nunits, int parts,
+                            int nck, int4 *utab, unsigned int *ctr) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u == 0) ctr[0] = 0u;
+  if (u >= nunits) return;
+  const int job = job_order[u / parts];
+  const int p0 = job_ptr[job], total = (job_ptr[job + 1] - p0) * nck;
+  // chunks start at a per-job offset so that workgroups do not all fetch the same (sink) blocks at once
+  const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
+  utab[u] = int4{job, p0, total, rot};
 }
 
 // out[c * B + r] = Q8[h, i*B + r] . K8[g, j*B + c] through the int8 tile code.
@@ -552,19 +634,26 @@ hipError_t run_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
 }
 
 template <int NT>
-hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_dl<NT>), dim3(p.Hkv * p.N * a.parts), dim3(NT), 0, st, a);
+hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
+  const int nunits = p.Hkv * p.N * a.parts;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT>, NT, 0) != hipSuccess) per_cu = 0;
+  const int cus = cu_count();
+  const int grid = std::max(1, std::min(nunits, std::max(1, per_cu) * std::max(1, cus)));
+  hipLaunchKernelGGL(k_attn_prep, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
+                     nunits, a.parts, p.B / kChunk, utab, ctr);
+  hipLaunchKernelGGL((k_attn_dl<NT>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits, ctr);
   return hipGetLastError();
 }
 
 template <bool I8>
-hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
+hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
   if (!I8) {
     switch (64 * p.G * a.qpw) {
-      case 256: return run_attn_dl<256>(p, a, st);
-      case 512: return run_attn_dl<512>(p, a, st);
-      case 768: return run_attn_dl<768>(p, a, st);
-      default: return run_attn_dl<1024>(p, a, st);
+      case 256: return run_attn_dl<256>(p, a, ctr, utab, st);
+      case 512: return run_attn_dl<512>(p, a, ctr, utab, st);
+      case 768: return run_attn_dl<768>(p, a, ctr, utab, st);
+      default: return run_attn_dl<1024>(p, a, ctr, utab, st);
     }
   }
   switch (64 * p.G * a.qpw) {
@@ -579,7 +668,7 @@ hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
 
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,
-                       void *O, hipStream_t st) {
+                       void *O, unsigned int *ctr, int4 *utab, hipStream_t st) {
   AttnArgs a;
   a.Q = (const uint8_t *)Q; a.K = (const uint8_t *)K; a.V = (const uint8_t *)V;
   a.sQ = sQ; a.sK = sK; a.sV = sV;
@@ -595,7 +684,7 @@ hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, c
     if (qtiles % d == 0 && p.G * d <= 12) qpw = d;
   a.qpw = qpw;
   a.parts = qtiles / qpw;
-  return i8 ? dispatch_attn<true>(p, a, st) : dispatch_attn<false>(p, a, st);
+  return i8 ? dispatch_attn<true>(p, a, ctr, utab, st) : dispatch_attn<false>(p, a, ctr, utab, st);
 }
 
 hipError_t launch_probe_qk_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,

@@ -40,6 +40,7 @@ int make_plan(const fp_shape *s, Plan *p) {
   p->off_jwork = o;  o = align_up(o + sizeof(int32_t) * Hkv * N);
   p->off_bar = o;    o = align_up(o + 256);
   p->off_jkeys = o;  o = align_up(o + sizeof(unsigned long long) * Hkv * N);
+  p->off_utab = o;   o = align_up(o + sizeof(int4) * Hkv * N * (B / 32));
   p->total = o;
   return FP_OK;
 }
@@ -58,6 +59,7 @@ Work carve(const Plan &p, void *ws) {
   w.jwork = (int32_t *)(b + p.off_jwork);
   w.bar = (unsigned int *)(b + p.off_bar);
   w.jkeys = (unsigned long long *)(b + p.off_jkeys);
+  w.utab = (int4 *)(b + p.off_utab);
   return w;
 }
 
@@ -185,7 +187,8 @@ static int attn_common(const fp_shape *shape, bool i8, const void *Q, const floa
       !csr->job_mask || !csr->job_order)
     return FP_EINVAL;
   if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
-  FP_LAUNCH(launch_attn(p, i8, Q, sQ, K, sK, V, sV, csr, O, (hipStream_t)stream));
+  const Work w = carve(p, ws);
+  FP_LAUNCH(launch_attn(p, i8, Q, sQ, K, sK, V, sV, csr, O, w.bar + 32, w.utab, (hipStream_t)stream));
   return FP_OK;
 }
 

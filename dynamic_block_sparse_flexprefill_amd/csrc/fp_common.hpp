@@ -65,22 +65,58 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- reductions
+// Butterfly partners without LDS traffic: steps 0-3 are DPP moves inside each
+// 16-lane row (lane ^ 1, lane ^ 2, then the mirrors i <-> 7 - i and
+// i <-> 15 - i, which pair lanes holding equal partial results), step 4 pairs
+// rows 0/1 and 2/3 (v_permlane16_swap), step 5 the two 32-lane halves
+// (v_permlane32_swap).  Each step combines a lane with exactly one partner, so
+// after step k every lane of a 2^(k+1)-lane group holds the same value.
+template <int STEP>
+__device__ __forceinline__ uint32_t bfly_partner(uint32_t v) {
+  if constexpr (STEP == 0) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, true);
+  else if constexpr (STEP == 1) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, true);
+  else if constexpr (STEP == 2) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, true);
+  else if constexpr (STEP == 3) return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, true);
+  else if constexpr (STEP == 4) {
+    const auto s = __builtin_amdgcn_permlane16_swap(v, v, false, false);   // {own or row below, own or row above}
+    return ((threadIdx.x >> 4) & 1) ? s[0] : s[1];
+  } else {
+    const auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return ((threadIdx.x >> 5) & 1) ? s[0] : s[1];
+  }
+}
+template <int STEP, typename T>
+__device__ __forceinline__ T bfly(T x) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, bfly_partner<STEP>(__builtin_bit_cast(uint32_t, x)));
+  } else {
+    static_assert(sizeof(T) == 8, "32- or 64-bit values");
+    const u32x2 w = __builtin_bit_cast(u32x2, x);
+    return __builtin_bit_cast(T, u32x2{bfly_partner<STEP>(w[0]), bfly_partner<STEP>(w[1])});
+  }
+}
+// The value of lane ^ 32.
 template <typename T>
-__device__ __forceinline__ T wave_sum(T x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+__device__ __forceinline__ T xor32(T x) { return bfly<5>(x); }
+
+// Reduction over the first NSTEP butterfly steps (6: the whole wave, 5: each 32-lane half).
+template <int NSTEP, typename T, typename Op>
+__device__ __forceinline__ T bfly_reduce(T x, Op op) {
+  x = op(x, bfly<0>(x));
+  x = op(x, bfly<1>(x));
+  x = op(x, bfly<2>(x));
+  x = op(x, bfly<3>(x));
+  if constexpr (NSTEP > 4) x = op(x, bfly<4>(x));
+  if constexpr (NSTEP > 5) x = op(x, bfly<5>(x));
   return x;
 }
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
-  return x;
-}
-__device__ __forceinline__ int wave_sum_int(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-  return x;
-}
+template <typename T>
+__device__ __forceinline__ T wave_sum(T x) { return bfly_reduce<6>(x, [](T a, T b) { return a + b; }); }
+__device__ __forceinline__ float wave_max(float x) { return bfly_reduce<6>(x, [](float a, float b) { return fmaxf(a, b); }); }
+__device__ __forceinline__ int wave_sum_int(int x) { return bfly_reduce<6>(x, [](int a, int b) { return a + b; }); }
+__device__ __forceinline__ int wave_min_int(int x) { return bfly_reduce<6>(x, [](int a, int b) { return min(a, b); }); }
+// Sum over each 32-lane half.
+__device__ __forceinline__ float half_sum(float x) { return bfly_reduce<5>(x, [](float a, float b) { return a + b; }); }
 
 // Workgroup-wide sum / max; `red` is LDS scratch of at least (blockDim/64)
 // elements.  Every thread gets the result.  The order of additions is fixed

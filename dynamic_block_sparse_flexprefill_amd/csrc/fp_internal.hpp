@@ -26,8 +26,10 @@ struct Plan {
   size_t off_rowbits; // u32   [Hq*N*nw32] row bit sets (query-aware rows; every row in fp_build_jobs)
   size_t off_qbar;   // float  [Hq*N*d]    mean-pooled query blocks (query-aware heads)
   size_t off_jwork;  // int32  [Hkv*N]     work per grouped job
-  size_t off_bar;    // u32    [64]        grid-barrier counter of the single-pass statistics
+  size_t off_bar;    // u32    [64]        [0]: grid-barrier counter of the single-pass statistics;
+                     //                     [32]: unit counter of the persistent attention kernel
   size_t off_jkeys;  // u64    [Hkv*N]     per-group sorted job keys
+  size_t off_utab;   // int4   [Hkv*N*b/32] attention work units {job, first entry, chunks, start}
   size_t total;
 };
 
@@ -43,6 +45,7 @@ struct Work {
   int32_t *jwork;
   unsigned int *bar;
   unsigned long long *jkeys;
+  int4 *utab;
 };
 Work carve(const Plan &p, void *ws);
 
@@ -67,9 +70,11 @@ hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hip
 // status[0] = 0 and, when bar is not NULL, bar[0] = 0
 hipError_t launch_status_init(int32_t *status, unsigned int *bar, hipStream_t st);
 // Block-sparse attention over the CSR rows.
+// compute units of the current device (cached; 0 if the query fails)
+int cu_count();
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,
-                       void *O, hipStream_t st);
+                       void *O, unsigned int *ctr, int4 *utab, hipStream_t st);
 // One int8 score tile through the attention / statistics tile code.
 hipError_t launch_probe_qk_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
                               int j, int32_t *out, hipStream_t st);

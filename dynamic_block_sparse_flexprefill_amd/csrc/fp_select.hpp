@@ -72,12 +72,6 @@ __device__ void wave_select_lds(const float *x, int n, float gamma, uint32_t *wo
 
 constexpr int kGreedySteps = 24;
 
-__device__ __forceinline__ int wave_min_int(int x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = min(x, __shfl_xor(x, m, 64));
-  return x;
-}
-
 // n <= 1024: the values live in registers (16 per lane).
 __device__ void wave_select_reg(const float *x, int n, float gamma, uint32_t *words) {
   constexpr int VPL = 16;

@@ -213,7 +213,7 @@ __global__ void __launch_bounds__(1024) k_ig_stats(StatArgs a) {
     for (int u = 0; u < TPW; ++u) {
       const int t = wave * TPW + u;
       float m = ml_m[u], l = ml_l[u];
-      const float mo = __shfl_xor(m, 32, 64), lo = __shfl_xor(l, 32, 64);
+      const float mo = xor32(m), lo = xor32(l);
       const float M = fmaxf(m, mo);
       const float L = l * exp2f(m - M) + lo * exp2f(mo - M);
       if (t < ntiles && lane < 32) {
@@ -375,7 +375,7 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
           if (split && diag && kt * 32 + acc_row(r, lane) > qrow[u]) x[r] = -INFINITY;
           mx = fmaxf(mx, x[r]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = fmaxf(mx, xor32(mx));
         const bool grow = mx > mref[u] + kHeadroom;
         if (__any(grow)) {
           const float mnew = grow ? mx : mref[u];
@@ -405,8 +405,8 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
           }
         }
       }
-      lo_acc += __shfl_xor(lo_acc, 32, 64);
-      hi_acc += __shfl_xor(hi_acc, 32, 64);
+      lo_acc += xor32(lo_acc);
+      hi_acc += xor32(hi_acc);
       lsum[u] += lo_acc + hi_acc;
       if (lane < 32) {
         prow[jj * 64 + 2 * lane] = lo_acc;
@@ -447,8 +447,7 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     for (int q = 0; q < nb; ++q) {
       // lanes 0..31: lower split of their row; lanes 32..63: upper split
       float v = wr * prow[q * 64 + 2 * (lane & 31) + (lane >> 5)];
-#pragma unroll
-      for (int m = 16; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+      v = half_sum(v);
       if ((lane & 31) == 0) red[(q * NTL + t) * 2 + (lane >> 5)] = v;
     }
   }
@@ -494,17 +493,6 @@ hipError_t dispatch(const Plan &p, const StatArgs &a, hipStream_t st) {
   return run<256, 4, I8>(p, a, st);
 }
 
-int cu_count() {
-  static int cache[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
 
 // Single pass when every workgroup (one per CU) can hold its chunk's partials
 // in LDS and all are co-resident; *used tells the caller whether it ran.
@@ -562,6 +550,18 @@ hipError_t dispatch1(const Plan &p, const StatArgs &a, unsigned int *bar, int32_
 }
 
 }  // namespace
+
+int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                            const float *sK, const Work &w, int32_t *status, hipStream_t st) {
