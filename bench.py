@@ -50,7 +50,8 @@ CONFIG_TEXT = {
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_flexprefill_amd", "csrc", "attn.hip")
-ATTN_KERNEL = "k_attn"
+# the attention kernel whose launches the roofline and traffic figures describe
+ATTN_KERNEL = {False: "k_attn_dl<", True: "k_attn_jobs<"}
 COPY_BYTES = 1 << 30
 
 
@@ -88,9 +89,11 @@ def traffic_from(d: str, config: str):
     copy_kib = COPY_BYTES / 1024.0
     fetch_factor = copy_kib / _counter(f("copy_FETCH_SIZE"), "copyBuffer")
     write_factor = copy_kib / _counter(f("copy_WRITE_SIZE"), "copyBuffer")
-    fetch = _counter(f("bench_FETCH_SIZE"), ATTN_KERNEL)
-    write = _counter(f("bench_WRITE_SIZE"), ATTN_KERNEL)
-    rec = {"config": config, "kernel": ATTN_KERNEL, "attn_source_sha256": attn_source_hash(),
+    import gen
+    kname = ATTN_KERNEL[gen.CONFIGS[config].int8]
+    fetch = _counter(f("bench_FETCH_SIZE"), kname)
+    write = _counter(f("bench_WRITE_SIZE"), kname)
+    rec = {"config": config, "kernel": kname, "attn_source_sha256": attn_source_hash(),
            "fetch_size_kib": fetch, "write_size_kib": write,
            "fetch_factor": fetch_factor, "write_factor": write_factor,
            "bytes_per_launch": fetch * 1024 * fetch_factor + write * 1024 * write_factor,
@@ -255,7 +258,7 @@ def main(argv=None):
         "data": "synthetic (planted-v1 generator, seed 0)",
         "config": {"workload": CONFIG_TEXT[c.name], "name": c.name, "S": c.S, "b": c.b, "Hq": c.Hq,
                    "Hkv": c.Hkv, "d": c.d, "gamma": c.gamma, "tau": c.tau, "seed": 0},
-        "roofline": {"bound": "mfma", "kernel": "k_attn_jobs (fp_attn)", "achieved": round(achieved_tf, 2),
+        "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL[i8].rstrip("<") + " (fp_attn)", "achieved": round(achieved_tf, 2),
                      "peak": peak, "unit": "TFLOP/s", "frac": round(achieved_tf / peak, 4),
                      "traffic": measured_traffic(c.name)},
         "roofline_index": {"bound": "hbm", "kernel": "fp_index (all kernels)", "achieved": round(idx_gbs, 1),
