@@ -76,6 +76,82 @@ struct QaArgs {
   uint32_t *rowbits;
 };
 
+// One wave per row of logits ev[r][0..i0+r]: softmax weights, selection
+// ([E] 3.1 cumulative-gamma rule), block 0 and the diagonal forced in, and the
+// row's bit set written to rowbits.  words: LDS, (blockDim / 64) * nw32 words.
+__device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev, uint32_t *words) {
+  const int N = a.N, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwv = blockDim.x >> 6;
+  uint32_t *wd = words + wave * a.nw32;
+  for (int r = wave; r < rows; r += nwv) {
+    const int i = i0 + r, n = i + 1;
+    float *x = ev + (size_t)r * N;
+    float mx = kNegBig;
+    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, x[j]);
+    mx = wave_max(mx);
+    for (int j = lane; j < n; j += 64) x[j] = expf(x[j] - mx);
+    const int nwr = (i >> 5) + 1;
+    for (int w = lane; w < nwr; w += 64) wd[w] = 0u;
+    wave_select(x, n, a.gamma, wd);
+    if (lane == 0) {
+      atomicOr(&wd[0], 1u);
+      atomicOr(&wd[i >> 5], 1u << (i & 31));
+    }
+    uint32_t *dst = a.rowbits + ((size_t)h * N + i) * a.nw32;
+    for (int w = lane; w < nwr; w += 64) dst[w] = wd[w];
+  }
+}
+
+// Logits of 16 query-aware rows on the fp32 matrix cores (16x16x4): the
+// workgroup's pooled queries are the A operand (lane l: row l % 16, quarter
+// l / 16 of every 16-wide slice of d), each wave sweeps 16-column tiles of K-bar
+// as the B operand, 32 products per tile; rows then select as above.
+// Used while 16 rows of logits fit in LDS (N <= 2048).
+constexpr int kQa16Threads = 512;
+__global__ void __launch_bounds__(kQa16Threads) k_qa_rows16(QaArgs a) {
+  const int h = blockIdx.y;
+  if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int N = a.N;
+  const int i0 = blockIdx.x * 16;
+  const int rows = min(16, N - i0);
+  const int g = h / a.G;
+  float *ev = smem;                                   // [16][N] logits / weights
+  uint32_t *words = (uint32_t *)(ev + (size_t)16 * N);  // [8 waves][nw32]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 4, rl = lane & 15;
+
+  f32x4 qa[8];
+  const float *qrow = a.qbar + ((size_t)h * N + min(i0 + rl, N - 1)) * 128 + 4 * q;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) qa[t] = *(const f32x4 *)(qrow + 16 * t);
+  const int ntile = (i0 + rows - 1) / 16 + 1;         // column tiles covering j <= i0 + rows - 1
+  auto ldk = [&](int jt, f32x4 *kb) {
+    const float *krow = a.kbar + ((size_t)g * N + min(jt * 16 + rl, N - 1)) * 128 + 4 * q;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kb[t] = *(const f32x4 *)(krow + 16 * t);
+  };
+  f32x4 kn[8];
+  if (wave < ntile) ldk(wave, kn);
+  for (int jt = wave; jt < ntile; jt += kQa16Threads / 64) {
+    f32x4 kb[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) kb[t] = kn[t];
+    if (jt + kQa16Threads / 64 < ntile) ldk(jt + kQa16Threads / 64, kn);
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[t][e], kb[t][e], acc, 0, 0, 0);
+    const int col = jt * 16 + rl;                      // acc[r]: row 4q + r, column col
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * q + r;
+      if (row < rows && col <= i0 + row) ev[(size_t)row * N + col] = a.sigma * acc[r];
+    }
+  }
+  __syncthreads();
+  select_rows(a, h, i0, rows, ev, words);
+}
+
 __global__ void __launch_bounds__(kQaThreads) k_qa_rows(QaArgs a) {
   const int h = blockIdx.y;
   if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
@@ -116,25 +192,7 @@ __global__ void __launch_bounds__(kQaThreads) k_qa_rows(QaArgs a) {
   }
   __syncthreads();
 
-  // One wave per row: softmax weights, selection, bit-set row.
-  uint32_t *wd = words + wave * a.nw32;
-  for (int r = wave; r < rows; r += kQaThreads / 64) {
-    const int i = i0 + r, n = i + 1;
-    float *x = ev + (size_t)r * N;
-    float mx = kNegBig;
-    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, x[j]);
-    mx = wave_max(mx);
-    for (int j = lane; j < n; j += 64) x[j] = expf(x[j] - mx);
-    const int nwr = (i >> 5) + 1;
-    for (int w = lane; w < nwr; w += 64) wd[w] = 0u;
-    wave_select(x, n, a.gamma, wd);
-    if (lane == 0) {
-      atomicOr(&wd[0], 1u);
-      atomicOr(&wd[i >> 5], 1u << (i & 31));
-    }
-    uint32_t *dst = a.rowbits + ((size_t)h * N + i) * a.nw32;
-    for (int w = lane; w < nwr; w += 64) dst[w] = wd[w];
-  }
+  select_rows(a, h, i0, rows, ev, words);
 }
 
 template <int B, bool I8>
@@ -168,6 +226,13 @@ hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, 
   a.qbar = w.qbar;
   a.kbar = w.kbar;
   a.rowbits = w.rowbits;
+  if (p.N <= 2048) {
+    const size_t lds = sizeof(float) * (size_t)16 * p.N + sizeof(uint32_t) * 8 * p.nw32;
+    e = hipFuncSetAttribute((const void *)k_qa_rows16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_qa_rows16, dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
+    return hipGetLastError();
+  }
   const size_t lds = sizeof(float) * ((size_t)a.R * p.N + a.R * 128) + sizeof(uint32_t) * 4 * p.nw32;
   e = hipFuncSetAttribute((const void *)k_qa_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -304,7 +304,7 @@ struct KStage {
 template <int B, int NT, int TPW, bool I8>
 __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
   const StatArgs &a = args.s;
-  constexpr int QT = B / 32, NWV = NT / 64, RG = NT / 128;
+  constexpr int QT = B / 32, NWV = NT / 64, RG = NT / 64;
   extern __shared__ __attribute__((aligned(16))) float part[];   // [NWV*TPW][cpb][32][2]
   __shared__ __attribute__((aligned(16))) uint8_t ks[B * Tile<I8>::Stride];
   __shared__ float sk[I8 ? B : 1];
@@ -345,15 +345,36 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     if (jj + 1 < nb) stg.load(a, g, j + 1);
     const bool diag = (j == N - 1);
 
-    // mean-pooled key block: RG row groups, then combined in order
+    // mean-pooled key block: RG row groups of two columns per thread (one 2-column read
+    // per row, rows rg, rg + RG, ... in two interleaved partial sums), combined in order
     {
-      const int dd = threadIdx.x & 127, rg = threadIdx.x >> 7;
-      float s = 0.0f;
-      for (int r = rg; r < B; r += RG) {
-        if (!I8) s += bf16_to_f32(*(const uint16_t *)(ks + r * Tile<I8>::Stride + 2 * dd));
-        else s += sk[r] * (float)(int8_t)ks[r * Tile<I8>::Stride + dd];
+      const int dp = threadIdx.x & 63, rg = threadIdx.x >> 6;
+      float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
+#pragma unroll 4
+      for (int r = rg; r < B; r += 2 * RG) {
+        const int r2 = r + RG;
+        if (!I8) {
+          const uint32_t v = *(const uint32_t *)(ks + r * Tile<I8>::Stride + 4 * dp);
+          s0 += __uint_as_float(v << 16);
+          s1 += __uint_as_float(v & 0xffff0000u);
+          if (r2 < B) {
+            const uint32_t w = *(const uint32_t *)(ks + r2 * Tile<I8>::Stride + 4 * dp);
+            t0 += __uint_as_float(w << 16);
+            t1 += __uint_as_float(w & 0xffff0000u);
+          }
+        } else {
+          const uint32_t v = *(const uint16_t *)(ks + r * Tile<I8>::Stride + 2 * dp);
+          s0 += sk[r] * (float)(int8_t)(v & 0xffu);
+          s1 += sk[r] * (float)(int8_t)(v >> 8);
+          if (r2 < B) {
+            const uint32_t w = *(const uint16_t *)(ks + r2 * Tile<I8>::Stride + 2 * dp);
+            t0 += sk[r2] * (float)(int8_t)(w & 0xffu);
+            t1 += sk[r2] * (float)(int8_t)(w >> 8);
+          }
+        }
       }
-      kpart[rg][dd] = s;
+      kpart[rg][2 * dp] = s0 + t0;
+      kpart[rg][2 * dp + 1] = s1 + t1;
     }
 
 #pragma unroll
@@ -368,14 +389,22 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
         float x[16];
         tile_scores<I8>(ks, sk, qf[u], 1.0f, kt, 1.0f, x);
         const bool split = (kt == tq);  // the only key tile holding both c <= r and c > r
-        float mx = -INFINITY;
+        // raw scores: the scale (>= 0) is applied to the maximum and inside the exponent;
+        // keys after the row (diagonal block) are left out of both
+        float mx;
+        if (split && diag) {
+          asm volatile("" ::: "memory");   // a real branch: the masked form runs for one tile of one block
+          mx = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          x[r] *= qscale[u];
-          if (split && diag && kt * 32 + acc_row(r, lane) > qrow[u]) x[r] = -INFINITY;
-          mx = fmaxf(mx, x[r]);
+          for (int r = 0; r < 16; ++r)
+            if (kt * 32 + acc_row(r, lane) <= qrow[u]) mx = fmaxf(mx, x[r]);
+        } else {
+          mx = x[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
         }
         mx = fmaxf(mx, xor32(mx));
+        mx = mx > -INFINITY ? mx * qscale[u] : -INFINITY;
         const bool grow = mx > mref[u] + kHeadroom;
         if (__any(grow)) {
           const float mnew = grow ? mx : mref[u];
@@ -390,18 +419,19 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
             }
           mref[u] = mnew;
         }
+        const float qs = qscale[u], mneg = -mref[u];
         if (!split) {
           float e = 0.0f;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e += fast_exp2(x[r] - mref[u]);
+          for (int r = 0; r < 16; ++r) e += fast_exp2(fmaf(x[r], qs, mneg));
           if (kt < tq) lo_acc += e;
           else hi_acc += e;
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(x[r] - mref[u]);
+            const float e = fast_exp2(fmaf(x[r], qs, mneg));
             if (kt * 32 + acc_row(r, lane) <= qrow[u]) lo_acc += e;
-            else hi_acc += e;
+            else if (!diag) hi_acc += e;
           }
         }
       }
@@ -509,7 +539,7 @@ hipError_t run1(const Plan &p, StatArgs a, unsigned int *bar, int32_t *status, h
   const int cpb = (p.N + nch - 1) / nch;
   nch = (p.N + cpb - 1) / cpb;
   const size_t lds = sizeof(float) * ((size_t)NTL * cpb * 64 + (size_t)cpb * NTL * 2);
-  const size_t static_lds = B * Tile<I8>::Stride + 4 * (NT / 128) * 128 + (I8 ? 4 * B : 4);
+  const size_t static_lds = B * Tile<I8>::Stride + 4 * (NT / 64) * 128 + (I8 ? 4 * B : 4);
   if (lds + static_lds > 160 * 1024) return hipSuccess;
   const void *fn = (const void *)k_ig_stats1<B, NT, TPW, I8>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
