@@ -10,12 +10,13 @@
 //   J(h, i) = Sel(softmax_{j<=i}(e), gamma) u {0, i}
 // with Sel the cumulative-mass selection (explainer section 3.1).
 //
-// Two kernels.  k_pool_q streams the Q blocks of the heads the divergence
-// test labelled query-aware (and only those) and writes their means; it is
-// bound by HBM, so every thread keeps many 16-byte loads in flight.  k_qa_rows
-// scores R consecutive query blocks of one head against the pooled keys (the
-// R pooled queries share every pooled-key read), and each wave then selects
-// its rows and writes them as bit sets (one bit per key block).
+// k_pool_q streams the Q blocks of the heads the divergence test labelled
+// query-aware (and only those) and writes their means; it is bound by HBM: one
+// wave per query block, each load instruction covering consecutive rows (1 KiB
+// contiguous for bf16), partial column sums combined across lanes at the end.
+// k_qa_rows16 (k_qa_rows for N > 2048) scores consecutive query blocks of one
+// head against the pooled keys, and each wave then selects its rows and writes
+// them as bit sets (one bit per key block).
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 #include "fp_select.hpp"
@@ -39,16 +40,17 @@ __global__ void __launch_bounds__(kQaThreads) k_pool_q(PoolArgs a) {
   const int h = blockIdx.y;
   if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
   constexpr int RB = I8 ? 128 : 256, CPR = RB / 16, EPC = I8 ? 16 : 8;
-  constexpr int BPW = kQaThreads / CPR;        // query blocks per workgroup
-  const int blk = blockIdx.x * BPW + threadIdx.x / CPR, ch = threadIdx.x % CPR;
+  constexpr int RPL = 64 / CPR;                 // rows read together by one wave
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int blk = blockIdx.x * (kQaThreads / 64) + wave, ch = lane % CPR, rr = lane / CPR;
   if (blk >= a.N) return;
   const size_t tok0 = (size_t)h * a.S + (size_t)blk * B;
-  const uint8_t *p = a.Q + tok0 * RB + ch * 16;
+  const uint8_t *p = a.Q + (tok0 + rr) * RB + ch * 16;
   float acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
-#pragma unroll 16
-  for (int r = 0; r < B; ++r) {
+#pragma unroll 8
+  for (int r = 0; r < B; r += RPL) {
     const u32x4 v = *(const u32x4 *)(p + (size_t)r * RB);
     if (!I8) {
 #pragma unroll
@@ -57,15 +59,29 @@ __global__ void __launch_bounds__(kQaThreads) k_pool_q(PoolArgs a) {
         acc[2 * e + 1] += bf16hi(v[e]);
       }
     } else {
-      const float s = a.sQ[tok0 + r];
+      const float s = a.sQ[tok0 + r + rr];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] += s * (float)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xffu);
     }
   }
-  float4 *dst = (float4 *)(a.qbar + ((size_t)h * a.N + blk) * 128 + ch * EPC);
+  // lanes ch, ch + CPR, ... hold partial sums of the same columns
 #pragma unroll
-  for (int e = 0; e < EPC / 4; ++e)
-    dst[e] = make_float4(acc[4 * e] / B, acc[4 * e + 1] / B, acc[4 * e + 2] / B, acc[4 * e + 3] / B);
+  for (int e = 0; e < EPC; ++e) {
+    if (CPR == 16) {
+      acc[e] += bfly<4>(acc[e]);
+      acc[e] += bfly<5>(acc[e]);
+    } else {
+      acc[e] += __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(acc[e]), __float_as_int(acc[e]), 0x128, 0xF, 0xF, true));   // lane (i + 8) mod 16
+      acc[e] += bfly<4>(acc[e]);
+      acc[e] += bfly<5>(acc[e]);
+    }
+  }
+  if (rr == 0) {
+    float4 *dst = (float4 *)(a.qbar + ((size_t)h * a.N + blk) * 128 + ch * EPC);
+#pragma unroll
+    for (int e = 0; e < EPC / 4; ++e)
+      dst[e] = make_float4(acc[4 * e] / B, acc[4 * e + 1] / B, acc[4 * e + 2] / B, acc[4 * e + 3] / B);
+  }
 }
 
 struct QaArgs {
@@ -197,7 +213,7 @@ __global__ void __launch_bounds__(kQaThreads) k_qa_rows(QaArgs a) {
 
 template <int B, bool I8>
 hipError_t run_pool(const Plan &p, const PoolArgs &a, hipStream_t st) {
-  constexpr int BPW = kQaThreads / ((I8 ? 128 : 256) / 16);
+  constexpr int BPW = kQaThreads / 64;
   hipLaunchKernelGGL((k_pool_q<B, I8>), dim3((p.N + BPW - 1) / BPW, p.Hq), dim3(kQaThreads), 0, st, a);
   return hipGetLastError();
 }
