@@ -179,7 +179,8 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
   const int job = a.job_order[blockIdx.x / a.parts], part = blockIdx.x % a.parts;
   const int g = job / N, i = job % N;
   const int hh = wave / a.qpw, qt = part * a.qpw + wave % a.qpw;
-  const int h = g * a.G + hh;
+  const bool live = hh < a.G;                        // else a spare wave: it only stages and waits
+  const int h = g * a.G + (live ? hh : 0);
   const int qtok0 = i * B + qt * 32;                 // first query token of this wave
   const int qtok = qtok0 + (lane & 31);
   const size_t tok = (size_t)h * S + qtok;
@@ -233,7 +234,7 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
     const uint32_t *vt32 = vt2[buf];
     const float *sks = sks2[buf], *svs = svs2[buf];
     const int key0 = j * B + kc * kChunk;            // token index of the chunk's first key
-    if (valid && ((mask >> hh) & 1u) && key0 <= qtok0 + 31) {
+    if (live && valid && ((mask >> hh) & 1u) && key0 <= qtok0 + 31) {
     const bool diag = key0 + kChunk - 1 > qtok0;     // some keys lie after some queries
     const uint16_t *vt = (const uint16_t *)vt32;
 #pragma unroll 1
@@ -298,6 +299,7 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
     __syncthreads();
   }
 
+  if (!live) return;                                 // (no barrier follows)
   l += xor32(l);
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   uint16_t *orow = a.O + tok * 128;
@@ -327,14 +329,17 @@ __global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
 //    i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.  Lane 4e + q of a block
 //    addresses key row e, columns 4q .. 4q + 3 of its 16-column slice, so the
 //    block receives 16 columns x 4 consecutive keys, transposed.
+// keys per staged chunk of the bf16 kernel
+constexpr int kChunkDl = 128;
+
 namespace dl {
 constexpr int KSlots = 17;                          // 16 B slots per staged K row
 constexpr int KRow = KSlots * 16;                   // 272 B
-constexpr int KBuf = kChunk * KRow;                 // 34816 B
-constexpr int VBuf = kChunk * 256;                  // 32768 B
-constexpr int KLoads = kChunk * KSlots / 64;        // 34 one-KiB loads
+constexpr int KBuf = kChunkDl * KRow;                 // 34816 B
+constexpr int VBuf = kChunkDl * 256;                  // 32768 B
+constexpr int KLoads = kChunkDl * KSlots / 64;        // 34 one-KiB loads
 constexpr int VLoads = VBuf / 1024;                 // 32
-static_assert(kChunk * KSlots % 64 == 0, "K staging must be whole 1 KiB spans");
+static_assert(kChunkDl * KSlots % 64 == 0, "K staging must be whole 1 KiB spans");
 }  // namespace dl
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -428,8 +433,9 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int NW = NT / 64;
   const int N = a.N, S = a.S, B = a.B;
-  const int nck = B / kChunk;
+  const int nck = B / kChunkDl;
   const int hh = wave / a.qpw;
+  const bool live = hh < a.G;                    // else a spare wave: it only stages and waits
   const float qscale = a.c2;
 
   auto unit_from = [&](int u, const int4 &t) -> Unit {
@@ -456,7 +462,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   auto issue = [&](const Ent &en, int b) {
     const int j = sgpr(en.jv);
     if (j >= 0 && j < N) {
-      const size_t row0 = (size_t)en.g * S + (size_t)j * B + en.kc * kChunk;
+      const size_t row0 = (size_t)en.g * S + (size_t)j * B + en.kc * kChunkDl;
       dl_issue(a.K + row0 * 256, a.V + row0 * 256, lds_addr(kbuf[b]), lds_addr(vbuf[b]), wave, NW);
     }
   };
@@ -489,7 +495,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     const int4 ntab = vload(utab + min(nxt_id, nunits - 1));   // (ignored past the end)
     const int qtok0 = cur.i * B + (cur.part * a.qpw + wave % a.qpw) * 32;
     const int qtok = qtok0 + (lane & 31);
-    const size_t tok = (size_t)(cur.g * a.G + hh) * S + qtok;
+    const size_t tok = (size_t)(cur.g * a.G + (live ? hh : 0)) * S + qtok;
     u32x4 qf[8];
     load_q<false>(a.Q, tok, qf);
     f32x16 o[4];
@@ -509,15 +515,15 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
       const Ent e2 = stream(c + 2);
       const int j0 = sgpr(e0.jv);
       const uint32_t mask0 = (uint32_t)sgpr((int)e0.maskv);
-      const int key0 = j0 * B + e0.kc * kChunk;
-      if (j0 >= 0 && j0 < N && ((mask0 >> hh) & 1u) && key0 <= qtok0 + 31) {
-        const bool diag = key0 + kChunk - 1 > qtok0;
+      const int key0 = j0 * B + e0.kc * kChunkDl;
+      if (live && j0 >= 0 && j0 < N && ((mask0 >> hh) & 1u) && key0 <= qtok0 + 31) {
+        const bool diag = key0 + kChunkDl - 1 > qtok0;
         const uint32_t kp = opaque(lds_addr(kbuf[buf]) + kl);
         uint32_t vp[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) vp[dt] = opaque(lds_addr(vbuf[buf]) + vl[dt]);
 #pragma unroll 1
-        for (int kt = 0; kt < kChunk / 32; ++kt) {
+        for (int kt = 0; kt < kChunkDl / 32; ++kt) {
           const int kb = kt * 32;
           f32x16 acc = {};
 #pragma unroll
@@ -574,15 +580,17 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     l += xor32(l);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     uint16_t *orow = a.O + tok * 128;
+    if (live) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int d0 = dt * 32 + 8 * rq + 4 * hf;
-        const u32x2 w = u32x2{pack_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
-                              pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv)};
-        *(u32x2 *)(orow + d0) = w;
-      }
+        for (int rq = 0; rq < 4; ++rq) {
+          const int d0 = dt * 32 + 8 * rq + 4 * hf;
+          const u32x2 w = u32x2{pack_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
+                                pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv)};
+          *(u32x2 *)(orow + d0) = w;
+        }
+    }
 
     cur = nxt;                                     // (every unit has a chunk barrier, which published the claim)
     if (cur.u >= nunits) break;
@@ -641,27 +649,24 @@ hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4
   const int cus = cu_count();
   const int grid = std::max(1, std::min(nunits, std::max(1, per_cu) * std::max(1, cus)));
   hipLaunchKernelGGL(k_attn_prep, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
-                     nunits, a.parts, p.B / kChunk, utab, ctr);
+                     nunits, a.parts, p.B / kChunkDl, utab, ctr);
   hipLaunchKernelGGL((k_attn_dl<NT>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits, ctr);
   return hipGetLastError();
 }
 
 template <bool I8>
 hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
+  const int need = 64 * p.G * a.qpw;                 // G * qpw <= 16 (G * b <= 2048)
   if (!I8) {
-    switch (64 * p.G * a.qpw) {
-      case 256: return run_attn_dl<256>(p, a, ctr, utab, st);
-      case 512: return run_attn_dl<512>(p, a, ctr, utab, st);
-      case 768: return run_attn_dl<768>(p, a, ctr, utab, st);
-      default: return run_attn_dl<1024>(p, a, ctr, utab, st);
-    }
+    if (need <= 256) return run_attn_dl<256>(p, a, ctr, utab, st);
+    if (need <= 512) return run_attn_dl<512>(p, a, ctr, utab, st);
+    if (need <= 768) return run_attn_dl<768>(p, a, ctr, utab, st);
+    return run_attn_dl<1024>(p, a, ctr, utab, st);
   }
-  switch (64 * p.G * a.qpw) {
-    case 256: return run_attn<256, I8>(p, a, st);
-    case 512: return run_attn<512, I8>(p, a, st);
-    case 768: return run_attn<768, I8>(p, a, st);
-    default: return run_attn<1024, I8>(p, a, st);
-  }
+  if (need <= 256) return run_attn<256, I8>(p, a, st);
+  if (need <= 512) return run_attn<512, I8>(p, a, st);
+  if (need <= 768) return run_attn<768, I8>(p, a, st);
+  return run_attn<1024, I8>(p, a, st);
 }
 
 }  // namespace
@@ -677,7 +682,8 @@ hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, c
   a.O = (uint16_t *)O;
   a.S = p.S; a.N = p.N; a.B = p.B; a.G = p.G;
   a.c2 = kLog2e / sqrtf((float)p.d);
-  // query tiles per workgroup: the largest divisor of b/32 keeping G * qpw <= 12 waves
+  // query tiles per workgroup: the largest divisor of b/32 keeping G * qpw <= 12 waves; the
+  // workgroup size is the next supported one (256, 512, 768 or 1024 threads), spare waves idle
   const int qtiles = p.B / 32;
   int qpw = 1;
   for (int d = 1; d <= qtiles; d <<= 1)

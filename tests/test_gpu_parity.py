@@ -91,6 +91,8 @@ ATTN_CASES = [
     ("tiny-N37", dict(S=128 * 37), 0.9),
     ("tiny-b256-G4", dict(S=2048, b=256, Hq=8, Hkv=2), 0.95),
     ("tiny-G8", dict(S=1024, Hq=8, Hkv=1), 0.9),
+    ("tiny-G5", dict(S=1024, Hq=10, Hkv=2), 0.9),        # 10 waves per job: two spare waves
+    ("tiny-G7-b256", dict(S=2048, b=256, Hq=7, Hkv=1), 0.9),
 ]
 
 
@@ -100,8 +102,8 @@ def test_attn_bf16_on_oracle_csr(name, kw, gamma):
     _attn_case(cfg(**kw), gamma)
 
 
-@pytest.mark.parametrize("name,kw,gamma", ATTN_CASES[:4] + ATTN_CASES[5:6],
-                         ids=[c[0] + f"-g{c[2]}" for c in ATTN_CASES[:4] + ATTN_CASES[5:6]])
+@pytest.mark.parametrize("name,kw,gamma", ATTN_CASES[:4] + ATTN_CASES[5:6] + ATTN_CASES[7:8],
+                         ids=[c[0] + f"-g{c[2]}" for c in ATTN_CASES[:4] + ATTN_CASES[5:6] + ATTN_CASES[7:8]])
 def test_attn_i8_on_oracle_csr(name, kw, gamma):
     say(f"attn i8 {name} gamma={gamma}")
     _attn_case(cfg(**kw), gamma, i8=True)
@@ -142,6 +144,7 @@ INDEX_CASES = [
     ("tiny-G8", dict(S=2048, Hq=8, Hkv=1), 0.9),
     ("tiny-G16", dict(S=1024, Hq=16, Hkv=1), 0.9),
     ("tiny-N70", dict(S=128 * 70, Hq=4, Hkv=2), 0.9),
+    ("tiny-G5", dict(S=2048, Hq=10, Hkv=2), 0.9),
 ]
 
 
