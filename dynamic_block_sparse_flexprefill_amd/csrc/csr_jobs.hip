@@ -77,15 +77,20 @@ __device__ __forceinline__ uint32_t row_word(const JobArgs &a, int h, int i, int
 constexpr int kMaxG = 16;
 constexpr int kJobWaves = 4;
 
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  return x;
+// Inclusive prefix sum over the wave (32-bit): Hillis-Steele inside each
+// 16-lane row with DPP row shifts (lanes shifted in from outside the row add
+// 0), then the totals of the earlier rows (lanes 15, 31, 47) are added.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+  const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+            t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0) + (row >= 2 ? t1 : 0) + (row >= 3 ? t2 : 0);
 }
+
 
 // Pass 1 (WRITE = false): row counts (when ROWS) and union counts / work per job.
 // Pass 2 (WRITE = true): columns of the rows (when ROWS) and job entries.
@@ -127,7 +132,7 @@ __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
           if (hh >= G) continue;
           const int r = (g * G + hh) * a.N + i;
           const int c = __popc(wd[hh]);
-          const int incl = wave_incl_scan(c);
+          const int incl = wave_scan_incl(c);
           int pos = rbase[hh] + incl - c;
           const int end = a.row_ptr[r + 1];
           uint32_t m = wd[hh];
@@ -135,11 +140,11 @@ __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
             a.col_idx[pos++] = 32 * w + (__ffs(m) - 1);
             m &= m - 1u;
           }
-          rbase[hh] += __shfl(incl, 63, 64);
+          rbase[hh] += __builtin_amdgcn_readlane(incl, 63);
         }
       }
       const int c = __popc(U);
-      const int incl = wave_incl_scan(c);
+      const int incl = wave_scan_incl(c);
       int pos = jb + ucarry + incl - c;
       uint32_t m = U;
       while (m && pos < je) {
@@ -152,7 +157,7 @@ __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
         a.job_mask[pos] = hm;
         ++pos;
       }
-      ucarry += __shfl(incl, 63, 64);
+      ucarry += __builtin_amdgcn_readlane(incl, 63);
     }
   }
   if (!WRITE && lane == 0) {
@@ -193,35 +198,35 @@ struct ScanJob {
   int64_t cap;
   uint32_t bit;
 };
+// In-place exclusive scan of counts x[1..n] into offsets x[0..n] (x[0] = 0),
+// clamped to cap (the overflow is reported through `bit`).  Tiles of
+// kScanThreads * 8 counts; a tile's total fits 32 bits (counts <= N <= 8192),
+// the running carry is 64-bit.
 __global__ void __launch_bounds__(kScanThreads) k_scan(ScanJob s0, ScanJob s1, int32_t *status) {
   const ScanJob s = blockIdx.x == 0 ? s0 : s1;
-  __shared__ long long wsum[kScanThreads / 64];
+  __shared__ int wtot[kScanThreads / 64];
   constexpr int E = 8;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   long long carry = 0;
   for (int base = 0; base < s.n; base += kScanThreads * E) {
     int v[E];
-    long long loc = 0;
+    int loc = 0;
 #pragma unroll
     for (int u = 0; u < E; ++u) {
       const int k = base + tid * E + u;
       v[u] = k < s.n ? s.x[1 + k] : 0;
       loc += v[u];
     }
-    long long x = loc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const long long y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
+    const int incl = wave_scan_incl(loc);
+    if (lane == 63) wtot[wave] = incl;
     __syncthreads();
-    if (lane == 63) wsum[wave] = x;
-    __syncthreads();
-    long long pre = carry;
-    for (int w = 0; w < wave; ++w) pre += wsum[w];
-    long long tile = 0;
-    for (int w = 0; w < kScanThreads / 64; ++w) tile += wsum[w];
-    long long run = pre + x - loc;
+    int t = lane < kScanThreads / 64 ? wtot[lane] : 0;
+    t = wave_scan_incl(t);
+    const int wpre = wave > 0 ? __builtin_amdgcn_readlane(t, wave - 1) : 0;
+    const int tile = __builtin_amdgcn_readlane(t, kScanThreads / 64 - 1);
+    __syncthreads();                               // wtot is rewritten by the next tile
+    long long run = carry + wpre + (incl - loc);
 #pragma unroll
     for (int u = 0; u < E; ++u) {
       const int k = base + tid * E + u;
