@@ -335,14 +335,16 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     lsum[u] = 0.0f;
   }
 
-  KStage<B, NT, I8> stg;
-  if (nb > 0) stg.load(a, g, j0);
-  for (int jj = 0; jj < nb; ++jj) {
+  // K blocks stream through registers two blocks ahead of their use (two stages, alternating)
+  KStage<B, NT, I8> stg0, stg1;
+  if (nb > 0) stg0.load(a, g, j0);
+  if (nb > 1) stg1.load(a, g, j0 + 1);
+  auto block = [&](int jj, KStage<B, NT, I8> &stg) {
     const int j = j0 + jj;
     __syncthreads();
     stg.store(ks, sk);
     __syncthreads();
-    if (jj + 1 < nb) stg.load(a, g, j + 1);
+    if (jj + 2 < nb) stg.load(a, g, j + 2);
     const bool diag = (j == N - 1);
 
     // mean-pooled key block: RG row groups of two columns per thread (one 2-column read
@@ -449,6 +451,10 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
       for (int q = 0; q < RG; ++q) s += kpart[q][threadIdx.x];
       a.kbar[((size_t)g * N + j) * 128 + threadIdx.x] = s / (float)B;
     }
+  };
+  for (int jj = 0; jj < nb; jj += 2) {
+    block(jj, stg0);
+    if (jj + 1 < nb) block(jj + 1, stg1);
   }
 
   // per-chunk (m_ref, sum) of every row, then the grid-wide merge
