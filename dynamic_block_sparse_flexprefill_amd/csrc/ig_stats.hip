@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
   if (nb > 1) stg1.load(a, g, j0 + 1);
   auto block = [&](int jj, KStage<B, NT, I8> &stg) {
     const int j = j0 + jj;
-    __syncthreads();
+    // (the previous block's closing barrier has already retired every read of ks, sk and kpart)
     stg.store(ks, sk);
     __syncthreads();
     if (jj + 2 < nb) stg.load(a, g, j + 2);
