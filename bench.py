@@ -51,7 +51,7 @@ CONFIG_TEXT = {
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_SRC = os.path.join(ROOT, "dynamic_block_sparse_flexprefill_amd", "csrc", "attn.hip")
 # the attention kernel whose launches the roofline and traffic figures describe
-ATTN_KERNEL = {False: "k_attn_dl<", True: "k_attn_jobs<"}
+ATTN_KERNEL = {False: "k_attn_dl<", True: "k_attn_dl<"}
 COPY_BYTES = 1 << 30
 
 

@@ -62,76 +62,6 @@ template <bool I8> struct KL {
 // consecutive keys, so its V^T operand is one 16-byte LDS read.
 __device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
-// Register-staged copy of one 128-key chunk of K and V.  A wave's V items
-// cover 32 consecutive key pairs x 2 column chunks, so its transposed 4-byte
-// LDS writes (row stride 68 words) hit 64 distinct banks.
-template <int NT, bool I8>
-struct Stage {
-  using L = KL<I8>;
-  static constexpr int KP = (L::KPieces + NT - 1) / NT;
-  static constexpr int VP = (L::VItems + NT - 1) / NT;
-  u32x4 kr[KP], va[VP], vb[VP];
-  float sk, sv;
-
-  __device__ __forceinline__ void load(const AttnArgs &a, size_t row0) {
-    const int tid = threadIdx.x;
-    const uint8_t *kb = a.K + row0 * L::RB, *vbp = a.V + row0 * L::RB;
-#pragma unroll
-    for (int u = 0; u < KP; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < L::KPieces) kr[u] = *(const u32x4 *)(kb + (size_t)idx * 16);
-    }
-    constexpr int CPR = L::RB / 16;
-#pragma unroll
-    for (int u = 0; u < VP; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < L::VItems) {
-        const int kp = (idx & 31) | ((idx / (32 * CPR)) << 5), dc = (idx >> 5) % CPR;
-        va[u] = *(const u32x4 *)(vbp + (size_t)(2 * kp) * L::RB + dc * 16);
-        vb[u] = *(const u32x4 *)(vbp + (size_t)(2 * kp + 1) * L::RB + dc * 16);
-      }
-    }
-    if (I8 && tid < kChunk) {
-      sk = a.sK[row0 + tid];
-      sv = a.sV[row0 + tid];
-    }
-  }
-
-  __device__ __forceinline__ void store(uint8_t *ks, uint32_t *vt32, float *sks, float *svs) const {
-    const int tid = threadIdx.x;
-    constexpr int CPR = L::RB / 16;
-#pragma unroll
-    for (int u = 0; u < KP; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < L::KPieces) *(u32x4 *)(ks + swap23(idx / CPR) * L::Stride + (idx % CPR) * 16) = kr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < VP; ++u) {
-      const int idx = tid + u * NT;
-      if (idx < L::VItems) {
-        const int kp = (idx & 31) | ((idx / (32 * CPR)) << 5), dc = (idx >> 5) % CPR;
-        if (!I8) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)   // {key 2kp, key 2kp+1} of column dc*8+e: one byte permute
-            vt32[((dc * 8 + e) * kVStride >> 1) + kp] =
-                __builtin_amdgcn_perm(vb[u][e >> 1], va[u][e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const float lo = (float)(int8_t)((va[u][e >> 2] >> (8 * (e & 3))) & 0xffu);
-            const float hi = (float)(int8_t)((vb[u][e >> 2] >> (8 * (e & 3))) & 0xffu);
-            vt32[((dc * 16 + e) * kVStride >> 1) + kp] = pack_bf16x2(lo, hi);
-          }
-        }
-      }
-    }
-    if (I8 && tid < kChunk) {
-      sks[tid] = sk;
-      svs[tid] = sv;
-    }
-  }
-};
-
 // Q fragments (operand B of S^T = K Q^T) for query token `tok` of this lane.
 template <bool I8>
 __device__ __forceinline__ void load_q(const uint8_t *Q, size_t tok, u32x4 qf[8]) {
@@ -169,151 +99,6 @@ __device__ __forceinline__ void raw_scores(const uint8_t *ks, int key0, const u3
   }
 }
 
-template <int NT, bool I8>
-__global__ void __launch_bounds__(NT) k_attn_jobs(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks2[2][kChunk * KL<I8>::Stride];
-  __shared__ __attribute__((aligned(16))) uint32_t vt2[2][128 * kVStride / 2];
-  __shared__ __attribute__((aligned(16))) float sks2[2][I8 ? kChunk : 4], svs2[2][I8 ? kChunk : 4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, hf = lane >> 5;
-  const int N = a.N, S = a.S, B = a.B;
-  const int job = a.job_order[blockIdx.x / a.parts], part = blockIdx.x % a.parts;
-  const int g = job / N, i = job % N;
-  const int hh = wave / a.qpw, qt = part * a.qpw + wave % a.qpw;
-  const bool live = hh < a.G;                        // else a spare wave: it only stages and waits
-  const int h = g * a.G + (live ? hh : 0);
-  const int qtok0 = i * B + qt * 32;                 // first query token of this wave
-  const int qtok = qtok0 + (lane & 31);
-  const size_t tok = (size_t)h * S + qtok;
-
-  u32x4 qf[8];
-  load_q<I8>(a.Q, tok, qf);
-  const float qscale = I8 ? a.c2 * a.sQ[tok] : a.c2;
-
-  f32x16 o[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  float m = -1e30f, l = 0.0f;                        // reference max (log2 units), partial sum
-
-  const int p0 = a.job_ptr[job], p1 = a.job_ptr[job + 1];
-  const int nck = B / kChunk;
-  const int total = (p1 - p0) * nck;
-  Stage<NT, I8> st;
-  // Chunks are visited in a rotated order, different per job, so that the
-  // workgroups do not all fetch the same (sink) blocks at the same moment.
-  const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
-  auto chunk_row0 = [&](int c, int &j, int &kc) -> bool {
-    int cc = c + rot;
-    cc = cc >= total ? cc - total : cc;
-    j = a.job_blk[p0 + cc / nck];
-    kc = cc % nck;
-    return j >= 0 && j < N;
-  };
-  // Chunk c is computed from LDS buffer c % 2 while chunk c + 1 is written
-  // into the other buffer from registers loaded during chunk c - 1, and the
-  // loads for chunk c + 2 are issued: one barrier per chunk.
-  {
-    int j, kc;
-    if (total > 0 && chunk_row0(0, j, kc)) st.load(a, (size_t)g * S + (size_t)j * B + kc * kChunk);
-    st.store(ks2[0], vt2[0], sks2[0], svs2[0]);
-    if (total > 1 && chunk_row0(1, j, kc)) st.load(a, (size_t)g * S + (size_t)j * B + kc * kChunk);
-  }
-  __syncthreads();
-  for (int c = 0; c < total; ++c) {
-    int j, kc;
-    const bool valid = chunk_row0(c, j, kc);
-    int cr = c + rot;
-    cr = cr >= total ? cr - total : cr;
-    const uint32_t mask = a.job_mask[p0 + cr / nck];
-    const int buf = c & 1;
-    if (c + 1 < total) {
-      st.store(ks2[buf ^ 1], vt2[buf ^ 1], sks2[buf ^ 1], svs2[buf ^ 1]);
-      int j2, kc2;
-      if (c + 2 < total && chunk_row0(c + 2, j2, kc2)) st.load(a, (size_t)g * S + (size_t)j2 * B + kc2 * kChunk);
-    }
-    const uint8_t *ks = ks2[buf];
-    const uint32_t *vt32 = vt2[buf];
-    const float *sks = sks2[buf], *svs = svs2[buf];
-    const int key0 = j * B + kc * kChunk;            // token index of the chunk's first key
-    if (live && valid && ((mask >> hh) & 1u) && key0 <= qtok0 + 31) {
-    const bool diag = key0 + kChunk - 1 > qtok0;     // some keys lie after some queries
-    const uint16_t *vt = (const uint16_t *)vt32;
-#pragma unroll 1
-    for (int kt = 0; kt < kChunk / 32; ++kt) {
-      const int kb = kt * 32;
-      float x[16];
-      raw_scores<I8>(ks, kb, qf, x);
-      // accumulator r of this lane holds key kb + key_of(r): rows 8(r/4)+4hf+r%4, permuted
-      if (I8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 s4 = *(const f32x4 *)(sks + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) x[4 * q + e] *= s4[e];
-        }
-      }
-      if (diag) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (key0 + kb + swap23(acc_row(r, lane)) > qtok) x[r] = -INFINITY;
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, xor32(mx)) * qscale;
-      const bool grow = mx > m + kRescale;
-      if (__any(grow)) {
-        const float mnew = grow ? mx : m;
-        const float alpha = fast_exp2(m - mnew);
-        m = mnew;
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-      }
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[r] = fast_exp2(fmaf(x[r], qscale, -m));
-        l += pv[r];
-      }
-      if (I8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 s4 = *(const f32x4 *)(svs + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pv[4 * q + e] *= s4[e];
-        }
-      }
-      u32x4 pf[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-        pf[s2] = u32x4{pack_bf16x2(pv[8 * s2 + 0], pv[8 * s2 + 1]), pack_bf16x2(pv[8 * s2 + 2], pv[8 * s2 + 3]),
-                       pack_bf16x2(pv[8 * s2 + 4], pv[8 * s2 + 5]), pack_bf16x2(pv[8 * s2 + 6], pv[8 * s2 + 7])};
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t *vrow = vt + (dt * 32 + (lane & 31)) * kVStride + kb + 8 * hf;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma_bf16(*(const u32x4 *)(vrow + 16 * s2), pf[s2], o[dt]);
-      }
-    }
-    }
-    __syncthreads();
-  }
-
-  if (!live) return;                                 // (no barrier follows)
-  l += xor32(l);
-  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  uint16_t *orow = a.O + tok * 128;
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const int d0 = dt * 32 + 8 * rq + 4 * hf;
-      const u32x2 w = u32x2{pack_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
-                            pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv)};
-      *(u32x2 *)(orow + d0) = w;
-    }
-}
-
 // ---------------------------------------------------------------------------
 // bf16 path with direct-to-LDS staging.  Each 128-key chunk of K and V is
 // copied from global memory into LDS by global_load_lds_dwordx4 (lane L of one
@@ -340,6 +125,16 @@ constexpr int VBuf = kChunkDl * 256;                  // 32768 B
 constexpr int KLoads = kChunkDl * KSlots / 64;        // 34 one-KiB loads
 constexpr int VLoads = VBuf / 1024;                 // 32
 static_assert(kChunkDl * KSlots % 64 == 0, "K staging must be whole 1 KiB spans");
+// int8 form: K rows of 128 B staged as 9 slots (144 B); V is staged as int8 and
+// then widened to bf16 and stored transposed (rows of kVStride bf16); one more
+// load carries the chunk's K and V scales.
+constexpr int KSlots8 = 9;
+constexpr int KRow8 = KSlots8 * 16;                 // 144 B
+constexpr int KBuf8 = kChunkDl * KRow8;             // 18432 B
+constexpr int VBuf8 = 128 * kVStride * 2;           // 34816 B (V^T, 128 columns)
+constexpr int KLoads8 = kChunkDl * KSlots8 / 64;    // 18
+static_assert(kChunkDl * KSlots8 % 64 == 0, "K staging must be whole 1 KiB spans");
+static_assert(kChunkDl == 128, "the scale load covers 128 keys");
 }  // namespace dl
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -369,6 +164,56 @@ __device__ __forceinline__ void dl_issue(const uint8_t *kg, const uint8_t *vg, u
     } else {
       const int v = u - dl::KLoads, row = 4 * v + (lane >> 4), c = (lane & 15) ^ (4 * (lane >> 4));
       lds_dma16(vg + row * 256 + 16 * c, vb + 1024 * v);
+    }
+  }
+}
+
+// int8: this wave's share of the direct loads of one chunk: K rows (LDS row
+// rho holding key swap23(rho), see raw_scores), V rows into the staging area,
+// and the scales (sK then sV, 128 each, one load).
+__device__ __forceinline__ void dl_issue8(const uint8_t *kg, const uint8_t *vg, const float *skg, const float *svg,
+                                          uint32_t kb, uint32_t vsb, uint32_t sb, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  for (int u = wave; u < dl::KLoads8 + 17; u += nw) {
+    if (u < dl::KLoads8) {
+      const int s = 64 * u + lane, rho = s / dl::KSlots8, c = min(s - rho * dl::KSlots8, 7);
+      lds_dma16(kg + swap23(rho) * 128 + 16 * c, kb + 1024 * u);
+    } else if (u < dl::KLoads8 + 16) {
+      const int r = 8 * (u - dl::KLoads8) + (lane >> 3);   // V row r: one full row per 8 lanes
+      lds_dma16(vg + r * 128 + 16 * ((lane & 7) ^ ((r >> 2) & 7)), vsb + 1024 * (u - dl::KLoads8));
+    } else {
+      lds_dma16(lane < 32 ? skg + 4 * lane : svg + 4 * (lane - 32), sb);
+    }
+  }
+}
+
+// int8: V of one chunk arrives by direct loads in a 16 KB LDS staging area:
+// row r (128 B, eight 16-byte pieces) sits at offset 128 r, with piece c at
+// slot c ^ ((r >> 2) & 7). All threads then widen it to bf16 and store it
+// transposed (column d, key pair kp: one bf16x2 word), the layout the int8 P.V
+// reads. Lane = key pair and odd pairs read their second row first, so both
+// the 16-byte staging reads and the transposed 4-byte writes are free of bank
+// conflicts.
+__device__ __forceinline__ uint32_t vstage_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 2) & 7)); }
+
+template <int NT>
+__device__ __forceinline__ void widen_v8(const uint8_t *vs, uint32_t *vt32) {
+  constexpr int ITEMS = (128 / 2) * 8;                     // (key pair, 16-byte column)
+  for (int idx = threadIdx.x; idx < ITEMS; idx += NT) {
+    const int kp = idx & 63, dc = idx >> 6, odd = kp & 1;
+    const u32x4 ra = *(const u32x4 *)(vs + vstage_off(2 * kp + odd, dc));
+    const u32x4 rb = *(const u32x4 *)(vs + vstage_off(2 * kp + 1 - odd, dc));
+    u32x4 va, vb;                                          // rows 2kp and 2kp + 1
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      va[w] = odd ? rb[w] : ra[w];
+      vb[w] = odd ? ra[w] : rb[w];
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float lo = (float)(int8_t)((va[e >> 2] >> (8 * (e & 3))) & 0xffu);
+      const float hi = (float)(int8_t)((vb[e >> 2] >> (8 * (e & 3))) & 0xffu);
+      vt32[((dc * 16 + e) * kVStride >> 1) + kp] = pack_bf16x2(lo, hi);
     }
   }
 }
@@ -424,10 +269,12 @@ struct Ent {
 // continuous chunk stream across them, so the next unit's first chunk is
 // loaded while the current unit's last chunk is computed.  A workgroup stops
 // at the first unit index past the end; indices only grow, so none is lost.
-template <int NT>
+template <int NT, bool I8>
 __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, int nunits, unsigned int *ctr) {
-  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][dl::KBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][dl::VBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][I8 ? dl::KBuf8 : dl::KBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][I8 ? dl::VBuf8 : dl::VBuf];
+  __shared__ __attribute__((aligned(16))) float sbuf[2][I8 ? 2 * kChunkDl : 4];   // int8: sK, sV of the chunk
+  __shared__ __attribute__((aligned(1024))) uint8_t vstage[I8 ? kChunkDl * 128 : 16];   // int8: V rows in flight
   __shared__ int s_claim[2];
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -463,7 +310,22 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     const int j = sgpr(en.jv);
     if (j >= 0 && j < N) {
       const size_t row0 = (size_t)en.g * S + (size_t)j * B + en.kc * kChunkDl;
-      dl_issue(a.K + row0 * 256, a.V + row0 * 256, lds_addr(kbuf[b]), lds_addr(vbuf[b]), wave, NW);
+      if constexpr (!I8) {
+        dl_issue(a.K + row0 * 256, a.V + row0 * 256, lds_addr(kbuf[b]), lds_addr(vbuf[b]), wave, NW);
+      } else {
+        dl_issue8(a.K + row0 * 128, a.V + row0 * 128, a.sK + row0, a.sV + row0, lds_addr(kbuf[b]),
+                  lds_addr(vstage), lds_addr(sbuf[b]), wave, NW);
+      }
+    }
+  };
+  // int8: once every wave's loads of entry en have arrived (the caller waits and
+  // synchronises), its staged V is widened into buffer b; the barrier after it
+  // publishes buffer b and frees the staging area
+  auto put_v = [&](const Ent &en, int b) {
+    if constexpr (I8) {
+      const int j = sgpr(en.jv);
+      if (j >= 0 && j < N) widen_v8<NT>(vstage, (uint32_t *)vbuf[b]);
+      __syncthreads();
     }
   };
 
@@ -474,6 +336,11 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   int parity = 0;
   Ent e0 = fetch(cur, 0), e1 = fetch(cur, 1);
   issue(e0, 0);
+  if constexpr (I8) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    put_v(e0, 0);
+  }
 
   // per-lane operand offsets: K rows (lane % 32) at column half hf; V^T per 32-column tile
   const int kl = (lane & 31) * dl::KRow + 16 * hf;
@@ -497,7 +364,8 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     const int qtok = qtok0 + (lane & 31);
     const size_t tok = (size_t)(cur.g * a.G + (live ? hh : 0)) * S + qtok;
     u32x4 qf[8];
-    load_q<false>(a.Q, tok, qf);
+    load_q<I8>(a.Q, tok, qf);
+    const float qsc = I8 ? qscale * a.sQ[tok] : qscale;
     f32x16 o[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
@@ -522,27 +390,41 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
         uint32_t vp[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) vp[dt] = opaque(lds_addr(vbuf[buf]) + vl[dt]);
+        const float *sks = sbuf[buf], *svs = sbuf[buf] + kChunkDl;
 #pragma unroll 1
         for (int kt = 0; kt < kChunkDl / 32; ++kt) {
           const int kb = kt * 32;
-          f32x16 acc = {};
-#pragma unroll
-          for (int s = 0; s < 8; ++s)
-            acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s), qf[s], acc);
           float x[16];
+          if constexpr (!I8) {
+            f32x16 acc = {};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) x[r] = acc[r];
+            for (int s = 0; s < 8; ++s)
+              acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s), qf[s], acc);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) x[r] = acc[r];
+          } else {
+            // int32 tile (LDS rows permuted: accumulator r of this lane is key kb + swap23(acc_row(r))),
+            // times the key scales; the query scale enters with sigma below
+            raw_scores<true>(kbuf[buf], kb, qf, x);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 s4 = *(const f32x4 *)(sks + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) x[4 * q + e] *= s4[e];
+            }
+          }
           if (diag) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (key0 + kb + acc_row(r, lane) > qtok) x[r] = -INFINITY;
+              if (key0 + kb + (I8 ? swap23(acc_row(r, lane)) : acc_row(r, lane)) > qtok) x[r] = -INFINITY;
           }
           float mx = x[0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
           {
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qscale;
+            mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])));
+            mx = mx > -INFINITY ? mx * qsc : -INFINITY;
           }
           const bool grow = mx > m + kRescaleDl;
           if (__any(grow)) {
@@ -554,25 +436,53 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
           }
           u32x4 pf[2];
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(x[8 * s2 + 2 * w], qscale, -m)),
-                                              fast_exp2(fmaf(x[8 * s2 + 2 * w + 1], qscale, -m)));
-              pf[s2][w] = pw;
-              l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
-                                                  __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
-            }
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
+          if constexpr (!I8) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
-              o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(x[8 * s2 + 2 * w], qsc, -m)),
+                                                fast_exp2(fmaf(x[8 * s2 + 2 * w + 1], qsc, -m)));
+                pf[s2][w] = pw;
+                l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
+                                                    __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
+              }
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2)
+                o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
+          } else {
+            // weights (summed into l) times the value scales, then P.V against the widened V^T
+            float pv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              pv[r] = fast_exp2(fmaf(x[r], qsc, -m));
+              l += pv[r];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 s4 = *(const f32x4 *)(svs + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
+#pragma unroll
+              for (int e = 0; e < 4; ++e) pv[4 * q + e] *= s4[e];
+            }
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+              pf[s2] = u32x4{pack_bf16x2(pv[8 * s2 + 0], pv[8 * s2 + 1]), pack_bf16x2(pv[8 * s2 + 2], pv[8 * s2 + 3]),
+                             pack_bf16x2(pv[8 * s2 + 4], pv[8 * s2 + 5]), pack_bf16x2(pv[8 * s2 + 6], pv[8 * s2 + 7])};
+            const uint16_t *vt = (const uint16_t *)vbuf[buf];
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+              const uint16_t *vrow = vt + (dt * 32 + (lane & 31)) * kVStride + kb + 8 * hf;
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma_bf16(*(const u32x4 *)(vrow + 16 * s2), pf[s2], o[dt]);
+            }
+          }
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
+      put_v(e1, buf ^ 1);                          // int8: the next chunk's V, widened and transposed
       e0 = e1;
       e1 = e2;
     }
@@ -635,38 +545,27 @@ __global__ void __launch_bounds__(2 * B) k_probe_qk_i8(const uint8_t *Q, const u
   }
 }
 
-template <int NT, bool I8>
-hipError_t run_attn(const Plan &p, const AttnArgs &a, hipStream_t st) {
-  hipLaunchKernelGGL((k_attn_jobs<NT, I8>), dim3(p.Hkv * p.N * a.parts), dim3(NT), 0, st, a);
-  return hipGetLastError();
-}
 
-template <int NT>
+template <int NT, bool I8>
 hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
   const int nunits = p.Hkv * p.N * a.parts;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT>, NT, 0) != hipSuccess) per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT, I8>, NT, 0) != hipSuccess) per_cu = 0;
   const int cus = cu_count();
   const int grid = std::max(1, std::min(nunits, std::max(1, per_cu) * std::max(1, cus)));
   hipLaunchKernelGGL(k_attn_prep, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
                      nunits, a.parts, p.B / kChunkDl, utab, ctr);
-  hipLaunchKernelGGL((k_attn_dl<NT>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits, ctr);
+  hipLaunchKernelGGL((k_attn_dl<NT, I8>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits, ctr);
   return hipGetLastError();
 }
 
 template <bool I8>
 hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
   const int need = 64 * p.G * a.qpw;                 // G * qpw <= 16 (G * b <= 2048)
-  if (!I8) {
-    if (need <= 256) return run_attn_dl<256>(p, a, ctr, utab, st);
-    if (need <= 512) return run_attn_dl<512>(p, a, ctr, utab, st);
-    if (need <= 768) return run_attn_dl<768>(p, a, ctr, utab, st);
-    return run_attn_dl<1024>(p, a, ctr, utab, st);
-  }
-  if (need <= 256) return run_attn<256, I8>(p, a, st);
-  if (need <= 512) return run_attn<512, I8>(p, a, st);
-  if (need <= 768) return run_attn<768, I8>(p, a, st);
-  return run_attn<1024, I8>(p, a, st);
+  if (need <= 256) return run_attn_dl<256, I8>(p, a, ctr, utab, st);
+  if (need <= 512) return run_attn_dl<512, I8>(p, a, ctr, utab, st);
+  if (need <= 768) return run_attn_dl<768, I8>(p, a, ctr, utab, st);
+  return run_attn_dl<1024, I8>(p, a, ctr, utab, st);
 }
 
 }  // namespace
