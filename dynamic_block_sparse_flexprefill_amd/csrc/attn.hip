@@ -15,15 +15,19 @@
 //
 // Kernel layout.  The explainer's section 2.2 notes that grouped-query heads
 // re-fetch the same K/V blocks; section 3.2 schedules sparse attention from a
-// compact job list.  Here one workgroup runs one job (KV group g, query block
-// i) -- the union of the G heads' key blocks -- or a share of its query tiles:
-// each key block is staged in LDS once (128 keys at a time) and used by every
-// head of the group whose mask bit is set.  One wave owns one (head, 32-query
-// tile).  The next 128-key chunk is loaded into registers while the current
-// one is computed from the other of two LDS buffers.  Scores are computed transposed, S^T = K Q^T, on the
-// 32x32x16 matrix cores so that every lane owns one query row; its softmax
-// weights are then already the operand of O^T += V^T P^T (V is transposed
-// while staged).  Jobs run longest first (job_order).
+// compact job list.  A job is (KV group g, query block i) with the union of
+// the G heads' key blocks; a work unit is a job or a share of its query
+// tiles.  The kernel is persistent: one workgroup per CU takes units in job
+// order (longest first), the first ones statically and the rest from an
+// atomic counter.  Each key block is staged in LDS once, 128 keys at a time,
+// and used by every head of the group whose mask bit is set; one wave owns
+// one (head, 32-query tile).  One stream of chunks runs across units: while
+// chunk c is computed from one LDS buffer, chunk c + 1 is copied into the
+// other by direct global-to-LDS loads.  Scores are computed transposed,
+// S^T = K Q^T, on the 32x32x16 matrix cores so that every lane owns one query
+// row; its softmax weights are then already the operand of O^T += V^T P^T,
+// whose V^T operand comes from LDS transpose reads of the key-major V rows
+// (int8: V is widened to bf16 and stored transposed after its chunk arrives).
 #include <algorithm>
 
 #include "fp_common.hpp"
@@ -42,18 +46,14 @@ struct AttnArgs {
   float c2;
 };
 
-constexpr int kChunk = 128;                  // keys staged per step
-constexpr int kVStride = kChunk + 8;         // bf16 elements per transposed V row (272 B)
-constexpr float kRescale = 8.0f;             // lazy-rescale headroom (log2 units)
-// Headroom of the bf16 kernel: weights stay below 2^24 before a rescale, so
-// O^T (at most 2^24 times the key count times max |V|) stays far inside fp32.
+constexpr int kChunkDl = 128;                // keys per staged chunk
+constexpr int kVStride = kChunkDl + 8;       // bf16 elements per transposed int8-path V row (272 B)
+// Lazy-rescale headroom: weights stay below 2^24 before a rescale, so O^T (at
+// most 2^24 times the key count times max |V|) stays far inside fp32.
 constexpr float kRescaleDl = 24.0f;
 
 template <bool I8> struct KL {
-  static constexpr int RB = I8 ? 128 : 256;            // global bytes per key row
-  static constexpr int Stride = I8 ? 144 : 272;        // LDS bytes per key row (padded)
-  static constexpr int KPieces = kChunk * RB / 16;     // 16-byte pieces of a K chunk
-  static constexpr int VItems = (kChunk / 2) * (RB / 16);  // (key pair, 16-byte column)
+  static constexpr int Stride = I8 ? 144 : 272;        // LDS bytes per staged key row (padded)
 };
 
 // K rows are staged in a permuted order: LDS row rho holds key swap23(rho)
@@ -114,8 +114,6 @@ __device__ __forceinline__ void raw_scores(const uint8_t *ks, int key0, const u3
 //    i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12.  Lane 4e + q of a block
 //    addresses key row e, columns 4q .. 4q + 3 of its 16-column slice, so the
 //    block receives 16 columns x 4 consecutive keys, transposed.
-// keys per staged chunk of the bf16 kernel
-constexpr int kChunkDl = 128;
 
 namespace dl {
 constexpr int KSlots = 17;                          // 16 B slots per staged K row
