@@ -278,15 +278,25 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_group(const int32_t *jwor
   for (int k = tid; k < N; k += kSortThreads) sorted[(size_t)g * N + k] = keys[k];
 }
 
+// With LDS, every workgroup first copies all Hkv * N sorted keys into LDS (at most
+// kRankLdsKeys) and searches there.
+constexpr int kRankLdsKeys = 8192;
+template <bool LDS>
 __global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, int32_t *order) {
+  extern __shared__ unsigned long long skeys[];
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (LDS) {
+    for (int t = threadIdx.x; t < Hkv * N; t += blockDim.x) skeys[t] = sorted[t];
+    __syncthreads();
+  }
   if (e >= Hkv * N) return;
+  const unsigned long long *src = LDS ? skeys : sorted;
   const int g = e / N, k = e % N;
-  const unsigned long long key = sorted[e];
+  const unsigned long long key = src[e];
   int rank = k;
   for (int o = 0; o < Hkv; ++o) {
     if (o == g) continue;
-    const unsigned long long *l = sorted + (size_t)o * N;   // descending
+    const unsigned long long *l = src + (size_t)o * N;      // descending
     int lo = 0, hi = N;                                      // count of entries > key
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -337,7 +347,16 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_sort_group, dim3(p.Hkv), dim3(kSortThreads), lds, st, w.jwork, p.N, w.jkeys);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(k_rank_jobs, dim3((jobs + 255) / 256), dim3(256), 0, st, w.jkeys, p.N, p.Hkv, io->job_order);
+  if (jobs <= kRankLdsKeys) {
+    const size_t lds = sizeof(unsigned long long) * jobs;
+    e = hipFuncSetAttribute((const void *)k_rank_jobs<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_rank_jobs<true>, dim3((jobs + 1023) / 1024), dim3(1024), lds, st, w.jkeys, p.N, p.Hkv,
+                       io->job_order);
+  } else {
+    hipLaunchKernelGGL(k_rank_jobs<false>, dim3((jobs + 255) / 256), dim3(256), 0, st, w.jkeys, p.N, p.Hkv,
+                       io->job_order);
+  }
   return hipGetLastError();
 }
 
