@@ -45,6 +45,7 @@ CONFIG_TEXT = {
     "3b-128k": "Llama-3.2-3B-shaped attention layer, S=131072, b=128, Hq=24, Hkv=8, d=128",
     "8b-64k": "Llama-3-8B-shaped attention layer, S=65536, b=256, Hq=32, Hkv=8, d=128, 3/4 heads vertical-slash",
     "w8a8-128k": "W8A8 Llama-3.2-3B-shaped attention layer, S=131072, b=128, Hq=24, Hkv=8, d=128",
+    "3b-128k-b64": "Llama-3.2-3B-shaped attention layer with 64-token blocks, S=131072, b=64, Hq=24, Hkv=8, d=128",
 }
 
 

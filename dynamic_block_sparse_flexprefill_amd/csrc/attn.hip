@@ -185,6 +185,43 @@ __device__ __forceinline__ void dl_issue8(const uint8_t *kg, const uint8_t *vg, 
   }
 }
 
+// Two-source forms for 64-key blocks: LDS rows 0..63 from the rows at ka/va (first block),
+// rows 64..127 from those at kb_/vb_ (second block); otherwise as dl_issue / dl_issue8.
+__device__ __forceinline__ void dl_issue2(const uint8_t *ka, const uint8_t *va, const uint8_t *kb_,
+                                          const uint8_t *vb_, uint32_t kb, uint32_t vb, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  for (int u = wave; u < dl::KLoads + dl::VLoads; u += nw) {
+    if (u < dl::KLoads) {
+      const int s = 64 * u + lane, row = s / dl::KSlots, c = min(s - row * dl::KSlots, 15);
+      lds_dma16((row < 64 ? ka + row * 256 : kb_ + (row - 64) * 256) + 16 * c, kb + 1024 * u);
+    } else {
+      const int v = u - dl::KLoads, row = 4 * v + (lane >> 4), c = (lane & 15) ^ (4 * (lane >> 4));
+      lds_dma16((row < 64 ? va + row * 256 : vb_ + (row - 64) * 256) + 16 * c, vb + 1024 * v);
+    }
+  }
+}
+__device__ __forceinline__ void dl_issue8_2(const uint8_t *ka, const uint8_t *va, const float *ska,
+                                            const float *sva, const uint8_t *kb_, const uint8_t *vb_,
+                                            const float *skb, const float *svb, uint32_t kb, uint32_t vsb,
+                                            uint32_t sb, int wave, int nw) {
+  const int lane = threadIdx.x & 63;
+  for (int u = wave; u < dl::KLoads8 + 17; u += nw) {
+    if (u < dl::KLoads8) {
+      // key swap23(rho) lies in the same 64-row half as row rho (the swap stays inside groups of 16)
+      const int s = 64 * u + lane, rho = s / dl::KSlots8, c = min(s - rho * dl::KSlots8, 7), key = swap23(rho);
+      lds_dma16((key < 64 ? ka + key * 128 : kb_ + (key - 64) * 128) + 16 * c, kb + 1024 * u);
+    } else if (u < dl::KLoads8 + 16) {
+      const int r = 8 * (u - dl::KLoads8) + (lane >> 3);
+      lds_dma16((r < 64 ? va + r * 128 : vb_ + (r - 64) * 128) + 16 * ((lane & 7) ^ ((r >> 2) & 7)),
+                vsb + 1024 * (u - dl::KLoads8));
+    } else {
+      // lanes 0..15 / 16..31: sK of the two blocks, 32..47 / 48..63: sV
+      const int q = lane >> 4, o = 4 * (lane & 15);
+      lds_dma16(q == 0 ? ska + o : q == 1 ? skb + o : q == 2 ? sva + o : svb + o, sb);
+    }
+  }
+}
+
 // int8: V of one chunk arrives by direct loads in a 16 KB LDS staging area:
 // row r (128 B, eight 16-byte pieces) sits at offset 128 r, with piece c at
 // slot c ^ ((r >> 2) & 7). All threads then widen it to bf16 and store it
@@ -250,16 +287,19 @@ __device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstla
 // tile share `part` of it, its first job-list entry p0, chunk count and the
 // chunk the rotated visiting order starts from.
 struct Unit {
-  int u, g, i, part, p0, total, rot;
+  int u, g, i, part, p0, n, total, rot;        // n: job-list entries, total: chunks
   bool empty;                                  // no job-list entry: one chunk that computes nothing
 };
 
 // Job-list entry of one chunk: key block jv and head mask maskv (as loaded,
-// made scalar where used), 128-key chunk kc of the block, KV group g.
+// made scalar where used), 128-key chunk kc of the block, KV group g.  With
+// 64-key blocks a chunk holds two consecutive entries, the second in jv2/maskv2.
 struct Ent {
   int jv;
   uint32_t maskv;
   int kc, g;
+  int jv2;                                     // 64-key blocks: the chunk's second entry (-1: none)
+  uint32_t maskv2;
 };
 
 // Persistent form: one workgroup per compute unit takes units in job order
@@ -267,7 +307,7 @@ struct Ent {
 // continuous chunk stream across them, so the next unit's first chunk is
 // loaded while the current unit's last chunk is computed.  A workgroup stops
 // at the first unit index past the end; indices only grow, so none is lost.
-template <int NT, bool I8>
+template <int NT, bool I8, bool PAIR>
 __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, int nunits, unsigned int *ctr) {
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][I8 ? dl::KBuf8 : dl::KBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][I8 ? dl::VBuf8 : dl::VBuf];
@@ -278,35 +318,55 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int NW = NT / 64;
   const int N = a.N, S = a.S, B = a.B;
-  const int nck = B / kChunkDl;
+  const int nck = B / kChunkDl;                 // 128-key chunks per block (0 with 64-key blocks)
   const int hh = wave / a.qpw;
   const bool live = hh < a.G;                    // else a spare wave: it only stages and waits
   const float qscale = a.c2;
 
   auto unit_from = [&](int u, const int4 &t) -> Unit {
-    Unit x{u, 0, 0, 0, 0, 0, 0, true};
+    Unit x{u, 0, 0, 0, 0, 0, 0, 0, true};
     if (u >= nunits) return x;
     const int job = sgpr(t.x);
     x.part = u % a.parts;
     x.g = job / N;
     x.i = job - x.g * N;
     x.p0 = sgpr(t.y);
-    x.total = sgpr(t.z);
+    x.n = sgpr(t.z);
+    x.total = PAIR ? (x.n + 1) >> 1 : x.n * nck;
     x.rot = sgpr(t.w);
     x.empty = x.total == 0;
     if (x.empty) x.total = 1;
     return x;
   };
   auto fetch = [&](const Unit &x, int c) -> Ent {
-    if (c >= x.total || x.empty) return Ent{-1, 0u, 0, 0};
+    if (c >= x.total || x.empty) return Ent{-1, 0u, 0, 0, -1, 0u};
     int cr = c + x.rot;
     cr = cr >= x.total ? cr - x.total : cr;
-    const int e = x.p0 + cr / nck;
-    return Ent{vload(a.job_blk + e), vload(a.job_mask + e), cr % nck, x.g};
+    if constexpr (PAIR) {
+      const int e = x.p0 + 2 * cr;
+      const bool two = 2 * cr + 1 < x.n;
+      return Ent{vload(a.job_blk + e), vload(a.job_mask + e), 0, x.g, two ? vload(a.job_blk + e + 1) : -1,
+                 two ? vload(a.job_mask + e + 1) : 0u};
+    } else {
+      const int e = x.p0 + cr / nck;
+      return Ent{vload(a.job_blk + e), vload(a.job_mask + e), cr % nck, x.g, -1, 0u};
+    }
   };
   auto issue = [&](const Ent &en, int b) {
     const int j = sgpr(en.jv);
-    if (j >= 0 && j < N) {
+    if (PAIR && j >= 0 && j < N) {
+      // second block: a missing or out-of-range one repeats the first (loaded, never run)
+      int j2 = sgpr(en.jv2);
+      j2 = j2 >= 0 && j2 < N ? j2 : j;
+      const size_t ra = (size_t)en.g * S + (size_t)j * B, rb = (size_t)en.g * S + (size_t)j2 * B;
+      if constexpr (!I8) {
+        dl_issue2(a.K + ra * 256, a.V + ra * 256, a.K + rb * 256, a.V + rb * 256, lds_addr(kbuf[b]),
+                  lds_addr(vbuf[b]), wave, NW);
+      } else {
+        dl_issue8_2(a.K + ra * 128, a.V + ra * 128, a.sK + ra, a.sV + ra, a.K + rb * 128, a.V + rb * 128,
+                    a.sK + rb, a.sV + rb, lds_addr(kbuf[b]), lds_addr(vstage), lds_addr(sbuf[b]), wave, NW);
+      }
+    } else if (!PAIR && j >= 0 && j < N) {
       const size_t row0 = (size_t)en.g * S + (size_t)j * B + en.kc * kChunkDl;
       if constexpr (!I8) {
         dl_issue(a.K + row0 * 256, a.V + row0 * 256, lds_addr(kbuf[b]), lds_addr(vbuf[b]), wave, NW);
@@ -330,7 +390,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   if ((int)blockIdx.x >= nunits) return;
   Unit cur = unit_from(blockIdx.x, vload(utab + blockIdx.x));
   int nxt_id = blockIdx.x + gridDim.x;                // claimed unit that follows cur
-  Unit nxt{nunits, 0, 0, 0, 0, 0, 0, true};
+  Unit nxt{nunits, 0, 0, 0, 0, 0, 0, 0, true};
   int parity = 0;
   Ent e0 = fetch(cur, 0), e1 = fetch(cur, 1);
   issue(e0, 0);
@@ -382,7 +442,16 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
       const int j0 = sgpr(e0.jv);
       const uint32_t mask0 = (uint32_t)sgpr((int)e0.maskv);
       const int key0 = j0 * B + e0.kc * kChunkDl;
-      if (live && j0 >= 0 && j0 < N && ((mask0 >> hh) & 1u) && key0 <= qtok0 + 31) {
+      // 64-key blocks: each half runs on its own (this wave's head in its mask, a key at or
+      // before the tile's last query); otherwise both halves follow the one entry
+      const int j2 = PAIR ? sgpr(e0.jv2) : -1;
+      const int key2 = j2 * B;
+      const bool ok0 = live && j0 >= 0 && j0 < N && ((mask0 >> hh) & 1u) && key0 <= qtok0 + 31;
+      const bool run_a = ok0 && (!PAIR || key0 <= qtok0 + 31);
+      const bool run_b = PAIR ? live && j0 >= 0 && j0 < N && j2 >= 0 && j2 < N &&
+                                    (((uint32_t)sgpr((int)e0.maskv2) >> hh) & 1u) && key2 <= qtok0 + 31
+                              : ok0;
+      if (run_a || run_b) {
         const bool diag = key0 + kChunkDl - 1 > qtok0;
         const uint32_t kp = opaque(lds_addr(kbuf[buf]) + kl);
         uint32_t vp[4];
@@ -391,7 +460,10 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
         const float *sks = sbuf[buf], *svs = sbuf[buf] + kChunkDl;
 #pragma unroll 1
         for (int kt = 0; kt < kChunkDl / 32; ++kt) {
-          const int kb = kt * 32;
+          const int kb = kt * 32;                  // LDS row of the tile
+          const int key_t = PAIR ? (kt < 2 ? key0 : key2) + 32 * (kt & 1) : key0 + kb;   // its first key
+          if (PAIR && (!(kt < 2 ? run_a : run_b) || key_t > qtok0 + 31)) continue;
+          const bool diag_t = PAIR ? key_t + 31 > qtok0 : diag;
           float x[16];
           if constexpr (!I8) {
             f32x16 acc = {};
@@ -411,10 +483,10 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
               for (int e = 0; e < 4; ++e) x[4 * q + e] *= s4[e];
             }
           }
-          if (diag) {
+          if (diag_t) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (key0 + kb + (I8 ? swap23(acc_row(r, lane)) : acc_row(r, lane)) > qtok) x[r] = -INFINITY;
+              if (key_t + (I8 ? swap23(acc_row(r, lane)) : acc_row(r, lane)) > qtok) x[r] = -INFINITY;
           }
           float mx = x[0];
 #pragma unroll
@@ -507,17 +579,18 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   }
 }
 
-// Unit table {job, first job-list entry, chunks, rotated start} and a zeroed claim counter.
+// Unit table {job, first job-list entry, entry count, rotated start chunk} and a zeroed claim counter.
 __global__ void k_attn_prep(const int32_t *job_order, const int32_t *job_ptr, int nunits, int parts,
                             int nck, int4 *utab, unsigned int *ctr) {
   const int u = blockIdx.x * blockDim.x + threadIdx.x;
   if (u == 0) ctr[0] = 0u;
   if (u >= nunits) return;
   const int job = job_order[u / parts];
-  const int p0 = job_ptr[job], total = (job_ptr[job + 1] - p0) * nck;
+  const int p0 = job_ptr[job], n = job_ptr[job + 1] - p0;
+  const int total = nck > 0 ? n * nck : (n + 1) >> 1;    // chunks (nck = 0: two 64-key blocks each)
   // chunks start at a per-job offset so that workgroups do not all fetch the same (sink) blocks at once
   const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
-  utab[u] = int4{job, p0, total, rot};
+  utab[u] = int4{job, p0, n, rot};
 }
 
 // out[c * B + r] = Q8[h, i*B + r] . K8[g, j*B + c] through the int8 tile code.
@@ -544,26 +617,27 @@ __global__ void __launch_bounds__(2 * B) k_probe_qk_i8(const uint8_t *Q, const u
 }
 
 
-template <int NT, bool I8>
+template <int NT, bool I8, bool PAIR>
 hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
   const int nunits = p.Hkv * p.N * a.parts;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT, I8>, NT, 0) != hipSuccess) per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT, I8, PAIR>, NT, 0) != hipSuccess)
+    per_cu = 0;
   const int cus = cu_count();
   const int grid = std::max(1, std::min(nunits, std::max(1, per_cu) * std::max(1, cus)));
   hipLaunchKernelGGL(k_attn_prep, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
                      nunits, a.parts, p.B / kChunkDl, utab, ctr);
-  hipLaunchKernelGGL((k_attn_dl<NT, I8>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits, ctr);
+  hipLaunchKernelGGL((k_attn_dl<NT, I8, PAIR>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits, ctr);
   return hipGetLastError();
 }
 
-template <bool I8>
+template <bool I8, bool PAIR>
 hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
-  const int need = 64 * p.G * a.qpw;                 // G * qpw <= 16 (G * b <= 2048)
-  if (need <= 256) return run_attn_dl<256, I8>(p, a, ctr, utab, st);
-  if (need <= 512) return run_attn_dl<512, I8>(p, a, ctr, utab, st);
-  if (need <= 768) return run_attn_dl<768, I8>(p, a, ctr, utab, st);
-  return run_attn_dl<1024, I8>(p, a, ctr, utab, st);
+  const int need = 64 * p.G * a.qpw;                 // G * qpw <= 16 (G <= 16, G * b <= 2048)
+  if (need <= 256) return run_attn_dl<256, I8, PAIR>(p, a, ctr, utab, st);
+  if (need <= 512) return run_attn_dl<512, I8, PAIR>(p, a, ctr, utab, st);
+  if (need <= 768) return run_attn_dl<768, I8, PAIR>(p, a, ctr, utab, st);
+  return run_attn_dl<1024, I8, PAIR>(p, a, ctr, utab, st);
 }
 
 }  // namespace
@@ -587,13 +661,18 @@ hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, c
     if (qtiles % d == 0 && p.G * d <= 12) qpw = d;
   a.qpw = qpw;
   a.parts = qtiles / qpw;
-  return i8 ? dispatch_attn<true>(p, a, ctr, utab, st) : dispatch_attn<false>(p, a, ctr, utab, st);
+  if (p.B == 64)   // two 64-key blocks per 128-key chunk
+    return i8 ? dispatch_attn<true, true>(p, a, ctr, utab, st) : dispatch_attn<false, true>(p, a, ctr, utab, st);
+  return i8 ? dispatch_attn<true, false>(p, a, ctr, utab, st) : dispatch_attn<false, false>(p, a, ctr, utab, st);
 }
 
 hipError_t launch_probe_qk_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
                               int j, int32_t *out, hipStream_t st) {
   const int g = h / p.G;
-  if (p.B == 128)
+  if (p.B == 64)
+    hipLaunchKernelGGL(k_probe_qk_i8<64>, dim3(1), dim3(128), 0, st, (const uint8_t *)Q8,
+                       (const uint8_t *)K8, p.S, h, g, i, j, out);
+  else if (p.B == 128)
     hipLaunchKernelGGL(k_probe_qk_i8<128>, dim3(1), dim3(256), 0, st, (const uint8_t *)Q8,
                        (const uint8_t *)K8, p.S, h, g, i, j, out);
   else

@@ -14,9 +14,9 @@ int make_plan(const fp_shape *s, Plan *p) {
   if (!s || !p) return FP_EINVAL;
   if (s->S <= 0 || s->b <= 0 || s->Hq <= 0 || s->Hkv <= 0 || s->d <= 0) return FP_EINVAL;
   if (s->S % s->b != 0 || s->Hq % s->Hkv != 0) return FP_EINVAL;
-  if (s->d != 128 || (s->b != 128 && s->b != 256)) return FP_EUNSUPPORTED;
+  if (s->d != 128 || (s->b != 64 && s->b != 128 && s->b != 256)) return FP_EUNSUPPORTED;
   const int N = s->S / s->b, G = s->Hq / s->Hkv;
-  if (N > 8192 || (int64_t)G * s->b > 2048) return FP_EUNSUPPORTED;
+  if (N > 8192 || (int64_t)G * s->b > 2048 || G > 16) return FP_EUNSUPPORTED;
   memset(p, 0, sizeof(*p));
   p->S = s->S; p->B = s->b; p->Hq = s->Hq; p->Hkv = s->Hkv; p->d = s->d;
   p->N = N; p->G = G;

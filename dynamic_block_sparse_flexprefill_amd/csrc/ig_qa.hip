@@ -229,7 +229,8 @@ hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, 
   pa.pattern = pattern;
   pa.qbar = w.qbar;
   hipError_t e;
-  if (p.B == 128) e = i8 ? run_pool<128, true>(p, pa, st) : run_pool<128, false>(p, pa, st);
+  if (p.B == 64) e = i8 ? run_pool<64, true>(p, pa, st) : run_pool<64, false>(p, pa, st);
+  else if (p.B == 128) e = i8 ? run_pool<128, true>(p, pa, st) : run_pool<128, false>(p, pa, st);
   else e = i8 ? run_pool<256, true>(p, pa, st) : run_pool<256, false>(p, pa, st);
   if (e != hipSuccess) return e;
 

@@ -519,6 +519,11 @@ hipError_t run(const Plan &p, const StatArgs &a, hipStream_t st) {
 template <bool I8>
 hipError_t dispatch(const Plan &p, const StatArgs &a, hipStream_t st) {
   const int tiles = p.G * p.B / 32;      // at most 64 (G*b <= 2048)
+  if (p.B == 64) {
+    if (tiles <= 16) return run<64, 1, I8>(p, a, st);
+    if (tiles <= 32) return run<64, 2, I8>(p, a, st);
+    return run<64, 4, I8>(p, a, st);
+  }
   if (p.B == 128) {
     if (tiles <= 16) return run<128, 1, I8>(p, a, st);
     if (tiles <= 32) return run<128, 2, I8>(p, a, st);
@@ -571,6 +576,14 @@ template <bool I8>
 hipError_t dispatch1(const Plan &p, const StatArgs &a, unsigned int *bar, int32_t *status,
                      hipStream_t st, bool *used) {
   const int tiles = p.G * p.B / 32;
+  if (p.B == 64) {
+    if (tiles <= 4) return run1<64, 256, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 8) return run1<64, 512, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 12) return run1<64, 768, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 16) return run1<64, 1024, 1, I8>(p, a, bar, status, st, used);
+    if (tiles <= 32) return run1<64, 1024, 2, I8>(p, a, bar, status, st, used);
+    return run1<64, 1024, 4, I8>(p, a, bar, status, st, used);
+  }
   if (p.B == 128) {
     if (tiles <= 4) return run1<128, 256, 1, I8>(p, a, bar, status, st, used);
     if (tiles <= 8) return run1<128, 512, 1, I8>(p, a, bar, status, st, used);

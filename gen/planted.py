@@ -80,6 +80,8 @@ CONFIGS: Dict[str, LayerConfig] = {
     "8b-64k": LayerConfig("8b-64k", S=65536, b=256, Hq=32, Hkv=8, gamma=0.95, vs_frac=0.75),
     # W8A8 variant of the 128K 3B layer
     "w8a8-128k": LayerConfig("w8a8-128k", S=131072, b=128, Hq=24, Hkv=8, int8=True),
+    # the 128K 3B layer with 64-token blocks (N = 2048)
+    "3b-128k-b64": LayerConfig("3b-128k-b64", S=131072, b=64, Hq=24, Hkv=8),
 }
 
 

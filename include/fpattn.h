@@ -46,9 +46,9 @@
  *    the device status word (fp_index_out.status) and stop writing past the
  *    capacity; read it after the stream synchronises.
  *  - Identical inputs give bit-identical outputs (no floating-point atomics).
- *  - Supported shapes: d = 128; b in {128, 256}; S a positive multiple of b
- *    with S / b <= 8192; Hq a multiple of Hkv; G * b <= 2048 where
- *    G = Hq / Hkv; gamma in (0, 1]; tau >= 0.
+ *  - Supported shapes: d = 128; b in {64, 128, 256}; S a positive multiple
+ *    of b with S / b <= 8192; Hq a multiple of Hkv; G <= 16 and G * b <= 2048
+ *    where G = Hq / Hkv; gamma in (0, 1]; tau >= 0.
  */
 #ifndef FPATTN_H
 #define FPATTN_H

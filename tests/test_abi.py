@@ -45,7 +45,9 @@ def test_version_and_strerror():
     (2048, 128, 5, 2, 128, fpa.FP_EINVAL),        # Hq % Hkv
     (0, 128, 4, 2, 128, fpa.FP_EINVAL),
     (2048, 128, 4, 2, 64, fpa.FP_EUNSUPPORTED),   # d
-    (2048, 64, 4, 2, 128, fpa.FP_EUNSUPPORTED),   # b
+    (2048, 32, 4, 2, 128, fpa.FP_EUNSUPPORTED),   # b
+    (2048, 64, 4, 2, 128, fpa.FP_OK),             # b = 64
+    (4096, 64, 32, 1, 128, fpa.FP_EUNSUPPORTED),  # G = 32: more heads per group than attention waves
     (128 * 8193, 128, 4, 2, 128, fpa.FP_EUNSUPPORTED),  # N > 8192
     (4096, 256, 16, 1, 128, fpa.FP_EUNSUPPORTED),  # G * b > 2048
     (4096, 128, 16, 1, 128, fpa.FP_OK),            # G * b = 2048

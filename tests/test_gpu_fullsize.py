@@ -76,7 +76,7 @@ def sampled_rows(c, rng, n=24):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["3b-32k", "3b-128k", "8b-64k", "w8a8-128k"])
+@pytest.mark.parametrize("name", ["3b-32k", "3b-128k", "8b-64k", "w8a8-128k", "3b-128k-b64"])
 def test_fullsize_parity(name):
     c = gen.CONFIGS[name]
     say(f"fullsize {name}: S={c.S} b={c.b} Hq={c.Hq} Hkv={c.Hkv} gamma={c.gamma}")

@@ -38,7 +38,7 @@ def cfg(name="tiny", **kw):
 
 
 # ------------------------------------------------------------------ int8 tile
-@pytest.mark.parametrize("b", [128, 256])
+@pytest.mark.parametrize("b", [64, 128, 256])
 def test_probe_qk_i8_exact(b):
     say(f"probe_qk_i8 b={b}")
     rng = np.random.default_rng(11)
@@ -93,6 +93,8 @@ ATTN_CASES = [
     ("tiny-G8", dict(S=1024, Hq=8, Hkv=1), 0.9),
     ("tiny-G5", dict(S=1024, Hq=10, Hkv=2), 0.9),        # 10 waves per job: two spare waves
     ("tiny-G7-b256", dict(S=2048, b=256, Hq=7, Hkv=1), 0.9),
+    ("tiny-b64", dict(S=1024, b=64, Hq=4, Hkv=2), 0.9),     # two 64-key blocks per staged chunk
+    ("tiny-b64-G3", dict(S=2048, b=64, Hq=6, Hkv=2), 0.9),
 ]
 
 
@@ -102,8 +104,10 @@ def test_attn_bf16_on_oracle_csr(name, kw, gamma):
     _attn_case(cfg(**kw), gamma)
 
 
-@pytest.mark.parametrize("name,kw,gamma", ATTN_CASES[:4] + ATTN_CASES[5:6] + ATTN_CASES[7:8],
-                         ids=[c[0] + f"-g{c[2]}" for c in ATTN_CASES[:4] + ATTN_CASES[5:6] + ATTN_CASES[7:8]])
+ATTN_I8_CASES = ATTN_CASES[:4] + ATTN_CASES[5:6] + ATTN_CASES[7:8] + ATTN_CASES[9:11]
+
+
+@pytest.mark.parametrize("name,kw,gamma", ATTN_I8_CASES, ids=[c[0] + f"-g{c[2]}" for c in ATTN_I8_CASES])
 def test_attn_i8_on_oracle_csr(name, kw, gamma):
     say(f"attn i8 {name} gamma={gamma}")
     _attn_case(cfg(**kw), gamma, i8=True)
@@ -145,6 +149,8 @@ INDEX_CASES = [
     ("tiny-G16", dict(S=1024, Hq=16, Hkv=1), 0.9),
     ("tiny-N70", dict(S=128 * 70, Hq=4, Hkv=2), 0.9),
     ("tiny-G5", dict(S=2048, Hq=10, Hkv=2), 0.9),
+    ("tiny-b64", dict(S=2048, b=64, Hq=4, Hkv=2), 0.9),
+    ("tiny-b64-G3", dict(S=4096, b=64, Hq=6, Hkv=2), 0.9),
 ]
 
 
@@ -180,8 +186,10 @@ def test_index_bf16(name, kw, gamma):
     _index_case(cfg(**kw), gamma)
 
 
-@pytest.mark.parametrize("name,kw,gamma", INDEX_CASES[:2] + INDEX_CASES[4:7],
-                         ids=[c[0] for c in INDEX_CASES[:2] + INDEX_CASES[4:7]])
+INDEX_I8_CASES = INDEX_CASES[:2] + INDEX_CASES[4:7] + INDEX_CASES[11:13]
+
+
+@pytest.mark.parametrize("name,kw,gamma", INDEX_I8_CASES, ids=[c[0] for c in INDEX_I8_CASES])
 def test_index_i8(name, kw, gamma):
     say(f"index i8 {name} gamma={gamma}")
     _index_case(cfg(**kw), gamma, i8=True)

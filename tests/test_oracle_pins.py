@@ -50,7 +50,8 @@ def test_page_facts():
     f = json.load(open(os.path.join(GOLD, "page_facts.json")))
     cfg = gen.CONFIGS["3b-128k"]
     assert cfg.tau == f["tau"]["value"]
-    assert all(c.b in f["block_sizes"]["value"] for c in gen.CONFIGS.values())
+    stated = set(f["block_sizes"]["value"]) | set(f["tuned_block_sizes"]["value"])
+    assert all(c.b in stated for c in gen.CONFIGS.values())
     assert (cfg.b, cfg.S) == (f["naive_intermediate_per_head"]["rows"], f["naive_intermediate_per_head"]["cols"])
     # one fp32 block score per key block of one head
     assert cfg.N * 4 == f["score_buffer_bytes_128k"]["approx"]
