@@ -418,7 +418,9 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
       claim = atomicAdd(ctr + z, 1u);
     }
     const int4 ntab = vload(utab + min(nxt_id, nunits - 1));   // (ignored past the end)
-    const int qtok0 = cur.i * B + (cur.part * a.qpw + wave % a.qpw) * 32;
+    // query tile of this wave, rotated by head: the waves sharing a SIMD (wave % 4) then hold
+    // different tiles, which evens out the per-SIMD work on diagonal blocks
+    const int qtok0 = cur.i * B + (cur.part * a.qpw + (wave + hh) % a.qpw) * 32;
     const int qtok = qtok0 + (lane & 31);
     const size_t tok = (size_t)(cur.g * a.G + (live ? hh : 0)) * S + qtok;
     u32x4 qf[8];
@@ -462,7 +464,8 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
         for (int kt = 0; kt < kChunkDl / 32; ++kt) {
           const int kb = kt * 32;                  // LDS row of the tile
           const int key_t = PAIR ? (kt < 2 ? key0 : key2) + 32 * (kt & 1) : key0 + kb;   // its first key
-          if (PAIR && (!(kt < 2 ? run_a : run_b) || key_t > qtok0 + 31)) continue;
+          // a tile whose keys all follow the wave's last query contributes nothing
+          if (PAIR ? !(kt < 2 ? run_a : run_b) || key_t > qtok0 + 31 : key_t > qtok0 + 31) continue;
           const bool diag_t = PAIR ? key_t + 31 > qtok0 : diag;
           float x[16];
           if constexpr (!I8) {
