@@ -219,6 +219,43 @@ def test_index_deterministic_and_end_to_end():
     assert mx <= MAXABS and rms <= RMS
 
 
+@pytest.mark.parametrize("i8", [False, True], ids=["bf16", "i8"])
+def test_attn_repeated_calls_share_one_workspace(i8):
+    """The persistent attention kernel keeps its unit table and claim counter in the workspace.
+    Calls that reuse one workspace, with a call of another shape (b = 64) in between, must give
+    bit-identical outputs, each equal to the oracle's within the attention tolerance."""
+    say(f"attn repeated calls on one workspace, {'i8' if i8 else 'bf16'}")
+    ca, cb = cfg(S=4096, Hq=6, Hkv=2), cfg(S=2048, b=64, Hq=6, Hkv=2)
+    sa, sb = fpa.shape_of(ca.S, ca.b, ca.Hq, ca.Hkv), fpa.shape_of(cb.S, cb.b, cb.Hq, cb.Hkv)
+    ws = fpa.Workspace(sa if fpa.workspace_bytes(sa) >= fpa.workspace_bytes(sb) else sb, "cuda")
+    La, Lb = gen.make(ca), gen.make(cb)
+
+    def run(c, L):
+        if i8:
+            t = P.layer_i8_on_device(L)
+            idx = fpa.index_i8(t["q8"], t["sq"], t["k8"], t["sk"], c.b, c.gamma, c.tau, ws=ws)
+            return fpa.attn_i8(t["q8"], t["sq"], t["k8"], t["sk"], t["v8"], t["sv"], idx, ws=ws), idx
+        Qd, Kd, Vd = P.layer_on_device(L)
+        idx = fpa.index(Qd, Kd, c.b, c.gamma, c.tau, ws=ws)
+        return fpa.attn(Qd, Kd, Vd, idx, ws=ws), idx
+
+    O1, idx = run(ca, La)
+    Ob, _ = run(cb, Lb)
+    O2, _ = run(ca, La)
+    O3, _ = run(ca, La)
+    torch.cuda.synchronize()
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(O1.view(torch.int16), O3.view(torch.int16))
+    rp, ci = P.gpu_rows(idx)
+    if i8:
+        d = La.int8()
+        Oref = oracle.attn.attn_i8(d["q8"], d["sq"], d["k8"], d["sk"], d["v8"], d["sv"], rp, ci, ca.b)
+    else:
+        Oref = oracle.attn.attn(La.f32("q"), La.f32("k"), La.f32("v"), rp, ci, ca.b)
+    mx, rms = P.attn_errors(O1, Oref)
+    assert mx <= MAXABS and rms <= RMS, (mx, rms)
+
+
 def test_capacity_overflow_sets_status():
     say("capacity overflow status")
     c = cfg()
