@@ -460,8 +460,78 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) vp[dt] = opaque(lds_addr(vbuf[buf]) + vl[dt]);
         const float *sks = sbuf[buf], *svs = sbuf[buf] + kChunkDl;
+        bool piped = false;
+        if constexpr (!I8 && !PAIR && NT <= 768) {
+          if (!diag) {
+            // Every key of the chunk precedes the wave's first query: no tile is masked or
+            // skipped, and the four tiles run software-pipelined with P.V one tile behind.
+            // The P.V products of tile kt - 1 are issued in the same basic block as the
+            // softmax of tile kt, so the matrix cores work while the wave computes
+            // exponentials.  The new reference maximum is chosen without a branch; only the
+            // (rare) rescale of O is one, placed after tile kt - 1 has been added.
+            piped = true;
+            auto qk = [&](int kb) {
+              f32x16 acc = {};
+#pragma unroll
+              for (int s = 0; s < 8; ++s)
+                acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s),
+                                qf[s], acc);
+              return acc;
+            };
+            // softmax weights of one tile (bf16 pairs) against the raised reference maximum
+            auto weights = [&](const f32x16 &sc, u32x4 pf[2], float &alpha) {
+              float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+              for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+              mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qsc;
+              const bool grow = mx > m + kRescaleDl;
+              const float mnew = grow ? mx : m;
+              alpha = fast_exp2(m - mnew);               // exactly 1 where the maximum stays
+              m = mnew;
+              l *= alpha;
+#pragma unroll
+              for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                  const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(sc[8 * s2 + 2 * w], qsc, -m)),
+                                                  fast_exp2(fmaf(sc[8 * s2 + 2 * w + 1], qsc, -m)));
+                  pf[s2][w] = pw;
+                  l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
+                                                      __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
+                }
+              return __any(grow);
+            };
+            auto pv = [&](int kb, const u32x4 pf[2]) {
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                  o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
+            };
+            u32x4 pp[2];
+            float alpha;
+            if (weights(qk(0), pp, alpha)) {
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+            }
+#pragma unroll
+            for (int kt = 1; kt < kChunkDl / 32; ++kt) {
+              const f32x16 sc = qk(32 * kt);
+              pv(32 * (kt - 1), pp);
+              u32x4 pn[2];
+              if (weights(sc, pn, alpha)) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+              }
+              pp[0] = pn[0];
+              pp[1] = pn[1];
+            }
+            pv(kChunkDl - 32, pp);
+          }
+        }
 #pragma unroll 1
-        for (int kt = 0; kt < kChunkDl / 32; ++kt) {
+        for (int kt = 0; kt < (piped ? 0 : kChunkDl / 32); ++kt) {
           const int kb = kt * 32;                  // LDS row of the tile
           const int key_t = PAIR ? (kt < 2 ? key0 : key2) + 32 * (kt & 1) : key0 + kb;   // its first key
           // a tile whose keys all follow the wave's last query contributes nothing

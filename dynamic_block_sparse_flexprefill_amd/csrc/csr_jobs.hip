@@ -74,7 +74,7 @@ __device__ __forceinline__ uint32_t row_word(const JobArgs &a, int h, int i, int
   return word & causal_mask_word(i, w);
 }
 
-constexpr int kMaxG = 16;
+constexpr int kMaxG = 16;                 // the job mask holds one bit per head of a group
 constexpr int kJobWaves = 4;
 
 // Inclusive prefix sum over the wave (32-bit): Hillis-Steele inside each
@@ -94,18 +94,19 @@ __device__ __forceinline__ int wave_scan_incl(int x) {
 
 // Pass 1 (WRITE = false): row counts (when ROWS) and union counts / work per job.
 // Pass 2 (WRITE = true): columns of the rows (when ROWS) and job entries.
-template <bool ROWS, bool WRITE>
+// GM >= G bounds the per-head arrays (registers) at compile time.
+template <int GM, bool ROWS, bool WRITE>
 __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
   const int lane = threadIdx.x & 63;
   const int job = blockIdx.x * kJobWaves + (threadIdx.x >> 6);
   if (job >= a.Hkv * a.N) return;
   const int g = job / a.N, i = job % a.N, G = a.G;
   const int nwi = (i >> 5) + 1;
-  int rbase[kMaxG];
+  int rbase[GM];
   int ucarry = 0, work = 0, ucount = 0;
-  int rcount[kMaxG];
+  int rcount[GM];
 #pragma unroll
-  for (int hh = 0; hh < kMaxG; ++hh) {
+  for (int hh = 0; hh < GM; ++hh) {
     rcount[hh] = 0;
     rbase[hh] = 0;
     if (WRITE && ROWS && hh < G) rbase[hh] = a.row_ptr[(g * G + hh) * a.N + i];
@@ -113,22 +114,22 @@ __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
   const int jb = WRITE ? a.job_ptr[job] : 0, je = WRITE ? a.job_ptr[job + 1] : 0;
   for (int w0 = 0; w0 < nwi; w0 += 64) {
     const int w = w0 + lane;
-    uint32_t wd[kMaxG];
+    uint32_t wd[GM];
     uint32_t U = 0u;
 #pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh) {
+    for (int hh = 0; hh < GM; ++hh) {
       wd[hh] = (hh < G && w < nwi) ? row_word(a, g * G + hh, i, w) : 0u;
       U |= wd[hh];
     }
     if (!WRITE) {
 #pragma unroll
-      for (int hh = 0; hh < kMaxG; ++hh)
+      for (int hh = 0; hh < GM; ++hh)
         if (hh < G) rcount[hh] += wave_sum_int(__popc(wd[hh]));
       ucount += wave_sum_int(__popc(U));
     } else {
       if (ROWS) {
 #pragma unroll
-        for (int hh = 0; hh < kMaxG; ++hh) {
+        for (int hh = 0; hh < GM; ++hh) {
           if (hh >= G) continue;
           const int r = (g * G + hh) * a.N + i;
           const int c = __popc(wd[hh]);
@@ -152,7 +153,7 @@ __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
         m &= m - 1u;
         uint32_t hm = 0u;
 #pragma unroll
-        for (int hh = 0; hh < kMaxG; ++hh) hm |= ((wd[hh] >> b) & 1u) << hh;
+        for (int hh = 0; hh < GM; ++hh) hm |= ((wd[hh] >> b) & 1u) << hh;
         a.job_blk[pos] = 32 * w + b;
         a.job_mask[pos] = hm;
         ++pos;
@@ -162,7 +163,7 @@ __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
   }
   if (!WRITE && lane == 0) {
 #pragma unroll
-    for (int hh = 0; hh < kMaxG; ++hh) {
+    for (int hh = 0; hh < GM; ++hh) {
       if (hh >= G) continue;
       work += rcount[hh];
       if (ROWS) a.row_ptr[(g * G + hh) * a.N + i + 1] = rcount[hh];
@@ -202,8 +203,7 @@ struct ScanJob {
 // clamped to cap (the overflow is reported through `bit`).  Tiles of
 // kScanThreads * 8 counts; a tile's total fits 32 bits (counts <= N <= 8192),
 // the running carry is 64-bit.
-__global__ void __launch_bounds__(kScanThreads) k_scan(ScanJob s0, ScanJob s1, int32_t *status) {
-  const ScanJob s = blockIdx.x == 0 ? s0 : s1;
+__device__ void scan_counts(const ScanJob &s, int32_t *status) {
   __shared__ int wtot[kScanThreads / 64];
   constexpr int E = 8;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -252,10 +252,9 @@ __device__ __forceinline__ unsigned long long job_key(const int32_t *jwork, int 
   return ((unsigned long long)(uint32_t)jwork[job] << 32) | (0xffffffffu - (uint32_t)job);
 }
 
-__global__ void __launch_bounds__(kSortThreads) k_sort_group(const int32_t *jwork, int N,
-                                                             unsigned long long *sorted) {
-  extern __shared__ unsigned long long keys[];
-  const int tid = threadIdx.x, g = blockIdx.x;
+__device__ void sort_group(const int32_t *jwork, int N, int g, unsigned long long *sorted,
+                           unsigned long long *keys) {
+  const int tid = threadIdx.x;
   int P = 1;
   while (P < N) P <<= 1;
   for (int k = tid; k < P; k += kSortThreads) keys[k] = k < N ? job_key(jwork, g * N + k) : 0ull;
@@ -276,6 +275,19 @@ __global__ void __launch_bounds__(kSortThreads) k_sort_group(const int32_t *jwor
     }
   }
   for (int k = tid; k < N; k += kSortThreads) sorted[(size_t)g * N + k] = keys[k];
+}
+
+// One launch for both steps that follow the count pass: workgroups 0 .. nscan-1
+// scan the job (and row) counts; the next Hkv workgroups, when `sorted` is
+// set, each sort one KV group's job keys (the sort needs only the job work).
+static_assert(kScanThreads == kSortThreads, "the scans and sorts share one launch");
+__global__ void __launch_bounds__(kScanThreads) k_scan_sort(ScanJob s0, ScanJob s1, int nscan, int32_t *status,
+                                                            const int32_t *jwork, int N,
+                                                            unsigned long long *sorted) {
+  extern __shared__ unsigned long long keys[];
+  const int blk = blockIdx.x;
+  if (blk < nscan) scan_counts(blk == 0 ? s0 : s1, status);
+  else sort_group(jwork, N, blk - nscan, sorted, keys);
 }
 
 // With LDS, every workgroup first copies all Hkv * N sorted keys into LDS (at most
@@ -314,6 +326,14 @@ __global__ void k_order_fallback(int N, int Hkv, int32_t *order) {
   order[k] = (k % Hkv) * N + (N - 1 - k / Hkv);
 }
 
+template <int GM, bool WRITE>
+hipError_t run_jobs(const Plan &p, const JobArgs &a, hipStream_t st, bool rows) {
+  const dim3 grid((p.Hkv * p.N + kJobWaves - 1) / kJobWaves), block(64 * kJobWaves);
+  if (rows) hipLaunchKernelGGL((k_jobs<GM, true, WRITE>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_jobs<GM, false, WRITE>), grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st, bool rows) {
   JobArgs a;
   a.N = p.N; a.G = p.G; a.Hkv = p.Hkv; a.nw32 = p.nw32;
@@ -324,29 +344,35 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   a.job_ptr = io->job_ptr; a.job_blk = io->job_blk; a.job_mask = io->job_mask;
   a.jwork = w.jwork;
   const int jobs = p.Hkv * p.N, rcount = p.Hq * p.N;
-  const dim3 grid((jobs + kJobWaves - 1) / kJobWaves), block(64 * kJobWaves);
   hipError_t e;
-  if (rows) hipLaunchKernelGGL((k_jobs<true, false>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_jobs<false, false>), grid, block, 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.G <= 1) e = run_jobs<1, false>(p, a, st, rows);
+  else if (p.G <= 2) e = run_jobs<2, false>(p, a, st, rows);
+  else if (p.G <= 4) e = run_jobs<4, false>(p, a, st, rows);
+  else if (p.G <= 8) e = run_jobs<8, false>(p, a, st, rows);
+  else e = run_jobs<kMaxG, false>(p, a, st, rows);
+  if (e != hipSuccess) return e;
   const ScanJob sj{io->job_ptr, jobs, io->job_cap, (uint32_t)FP_STATUS_JOB_OVERFLOW};
   const ScanJob sr{io->row_ptr, rcount, io->col_cap, (uint32_t)FP_STATUS_CSR_OVERFLOW};
-  hipLaunchKernelGGL(k_scan, dim3(rows ? 2 : 1), dim3(kScanThreads), 0, st, sj, sr, io->status);
+  const int nscan = rows ? 2 : 1;
+  const bool sort = p.N <= kSortMax;
+  int P = 1;
+  while (P < p.N) P <<= 1;
+  const size_t slds = sort ? sizeof(unsigned long long) * P : 0;
+  e = hipFuncSetAttribute((const void *)k_scan_sort, hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_scan_sort, dim3(nscan + (sort ? p.Hkv : 0)), dim3(kScanThreads), slds, st, sj, sr, nscan,
+                     io->status, w.jwork, p.N, w.jkeys);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (rows) hipLaunchKernelGGL((k_jobs<true, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_jobs<false, true>), grid, block, 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (p.N > kSortMax) {
+  if (p.G <= 1) e = run_jobs<1, true>(p, a, st, rows);
+  else if (p.G <= 2) e = run_jobs<2, true>(p, a, st, rows);
+  else if (p.G <= 4) e = run_jobs<4, true>(p, a, st, rows);
+  else if (p.G <= 8) e = run_jobs<8, true>(p, a, st, rows);
+  else e = run_jobs<kMaxG, true>(p, a, st, rows);
+  if (e != hipSuccess) return e;
+  if (!sort) {
     hipLaunchKernelGGL(k_order_fallback, dim3((jobs + 255) / 256), dim3(256), 0, st, p.N, p.Hkv, io->job_order);
     return hipGetLastError();
   }
-  int P = 1;
-  while (P < p.N) P <<= 1;
-  const size_t lds = sizeof(unsigned long long) * P;
-  e = hipFuncSetAttribute((const void *)k_sort_group, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_sort_group, dim3(p.Hkv), dim3(kSortThreads), lds, st, w.jwork, p.N, w.jkeys);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (jobs <= kRankLdsKeys) {
     const size_t lds = sizeof(unsigned long long) * jobs;
     e = hipFuncSetAttribute((const void *)k_rank_jobs<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

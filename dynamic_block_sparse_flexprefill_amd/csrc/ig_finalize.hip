@@ -32,7 +32,8 @@ struct FinArgs {
   uint32_t *sel;
 };
 
-constexpr int kFinThreads = 256;
+constexpr int kFinThreads = 1024;
+constexpr int kFinRowGroups = 32;     // row groups of the last-block query mean (LDS: [32][128] partials)
 
 template <bool I8>
 __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
@@ -42,23 +43,25 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
   float *vv = ev + N;               // [N] vertical mass
   float *sv = vv + N;               // [N] slash mass
   float *qb = sv + N;               // [128] mean query of the last block
-  float *qpart = qb + 128;          // [32][128] row-group partial sums
-  uint32_t *msk = (uint32_t *)(qpart + 32 * 128);   // [2][nw32]
-  __shared__ double redd[16];
-  __shared__ float redf[16];
+  float *qpart = qb + 128;          // [kFinRowGroups][128] row-group partial sums
+  uint32_t *msk = (uint32_t *)(qpart + kFinRowGroups * 128);   // [2][nw32]
+  __shared__ double redd[kFinThreads / 64];
+  __shared__ float redf[kFinThreads / 64];
   const int tid = threadIdx.x, h = blockIdx.x, g = h / a.G;
 
-  // Mean of the last query block: 16-byte loads, rows split over RG groups,
-  // group partials combined in order.
+  // Mean of the last query block: 16-byte loads, rows split over RG groups
+  // (the threads past RG * CPR only join the barriers), group partials
+  // combined in order.
   {
-    constexpr int RB = I8 ? 128 : 256, CPR = RB / 16, EPC = I8 ? 16 : 8, RG = kFinThreads / CPR;
+    constexpr int RB = I8 ? 128 : 256, CPR = RB / 16, EPC = I8 ? 16 : 8;
+    constexpr int RG = kFinThreads / CPR < kFinRowGroups ? kFinThreads / CPR : kFinRowGroups;
     const int ch = tid % CPR, rg = tid / CPR;
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
     const size_t tok0 = (size_t)h * S + (S - B);
 #pragma unroll 8
-    for (int r = rg; r < B; r += RG) {
+    for (int r = rg; r < B && rg < RG; r += RG) {
       const u32x4 v = *(const u32x4 *)(a.Q + (tok0 + r) * RB + ch * 16);
       if (!I8) {
 #pragma unroll
@@ -72,8 +75,10 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
         for (int e = 0; e < 16; ++e) acc[e] += sc * (float)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xffu);
       }
     }
+    if (rg < RG) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) qpart[rg * 128 + ch * EPC + e] = acc[e];
+      for (int e = 0; e < EPC; ++e) qpart[rg * 128 + ch * EPC + e] = acc[e];
+    }
     __syncthreads();
     if (tid < 128) {
       float sum = 0.0f;
@@ -158,7 +163,7 @@ hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float
   a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
   a.pattern = out->pattern; a.jsd = out->jsd; a.stats = out->stats;
   a.sel = w.sel;
-  const size_t lds = sizeof(float) * (3 * (size_t)p.N + 128 + 32 * 128) + sizeof(uint32_t) * 2 * p.nw32;
+  const size_t lds = sizeof(float) * (3 * (size_t)p.N + 128 + kFinRowGroups * 128) + sizeof(uint32_t) * 2 * p.nw32;
   const void *fn = i8 ? (const void *)k_ig_finalize<true> : (const void *)k_ig_finalize<false>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

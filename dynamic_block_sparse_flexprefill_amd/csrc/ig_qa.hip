@@ -10,13 +10,14 @@
 //   J(h, i) = Sel(softmax_{j<=i}(e), gamma) u {0, i}
 // with Sel the cumulative-mass selection (explainer section 3.1).
 //
-// k_pool_q streams the Q blocks of the heads the divergence test labelled
-// query-aware (and only those) and writes their means; it is bound by HBM: one
-// wave per query block, each load instruction covering consecutive rows (1 KiB
-// contiguous for bf16), partial column sums combined across lanes at the end.
-// k_qa_rows16 (k_qa_rows for N > 2048) scores consecutive query blocks of one
-// head against the pooled keys, and each wave then selects its rows and writes
-// them as bit sets (one bit per key block).
+// Only the Q blocks of the heads the divergence test labelled query-aware are
+// read.  k_qa_rows16 (N <= 2048) pools its own 16 query blocks -- one wave per
+// block, each load instruction covering consecutive rows (1 KiB contiguous for
+// bf16), partial column sums combined across lanes at the end -- so the HBM
+// read of Q overlaps the scoring and selection of other workgroups; it then
+// scores those blocks against the pooled keys, and each wave selects its rows
+// and writes them as bit sets (one bit per key block).  For N > 2048, k_pool_q
+// writes the means to the workspace first and k_qa_rows scores from there.
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 #include "fp_select.hpp"
@@ -34,24 +35,26 @@ struct PoolArgs {
   float *qbar;       // [Hq][N][128]
 };
 
-// One thread per (query block, 16-byte column): rows summed in order.
+// Column sums of one query block (B rows from token tok0) by one wave: lane
+// (rr, ch) adds rows rr, rr + RPL, ... of 16-byte column chunk ch in order, then
+// the RPL partial sums of each chunk are combined across lanes; afterwards lanes
+// with rr == 0 hold the block's sums of columns ch * EPC .. ch * EPC + EPC - 1.
+template <int B, bool I8> struct PoolGeo {
+  static constexpr int RB = I8 ? 128 : 256, CPR = RB / 16, EPC = I8 ? 16 : 8;
+  static constexpr int RPL = 64 / CPR;          // rows read together by one wave
+};
+
 template <int B, bool I8>
-__global__ void __launch_bounds__(kQaThreads) k_pool_q(PoolArgs a) {
-  const int h = blockIdx.y;
-  if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
-  constexpr int RB = I8 ? 128 : 256, CPR = RB / 16, EPC = I8 ? 16 : 8;
-  constexpr int RPL = 64 / CPR;                 // rows read together by one wave
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int blk = blockIdx.x * (kQaThreads / 64) + wave, ch = lane % CPR, rr = lane / CPR;
-  if (blk >= a.N) return;
-  const size_t tok0 = (size_t)h * a.S + (size_t)blk * B;
-  const uint8_t *p = a.Q + (tok0 + rr) * RB + ch * 16;
-  float acc[EPC];
+__device__ __forceinline__ void pool_block(const uint8_t *Q, const float *sQ, size_t tok0,
+                                           float acc[PoolGeo<B, I8>::EPC]) {
+  using PG = PoolGeo<B, I8>;
+  const int lane = threadIdx.x & 63, ch = lane % PG::CPR, rr = lane / PG::CPR;
+  const uint8_t *p = Q + (tok0 + rr) * PG::RB + ch * 16;
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+  for (int e = 0; e < PG::EPC; ++e) acc[e] = 0.0f;
 #pragma unroll 8
-  for (int r = 0; r < B; r += RPL) {
-    const u32x4 v = *(const u32x4 *)(p + (size_t)r * RB);
+  for (int r = 0; r < B; r += PG::RPL) {
+    const u32x4 v = *(const u32x4 *)(p + (size_t)r * PG::RB);
     if (!I8) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -59,15 +62,15 @@ __global__ void __launch_bounds__(kQaThreads) k_pool_q(PoolArgs a) {
         acc[2 * e + 1] += bf16hi(v[e]);
       }
     } else {
-      const float s = a.sQ[tok0 + r + rr];
+      const float s = sQ[tok0 + r + rr];
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[e] += s * (float)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xffu);
     }
   }
   // lanes ch, ch + CPR, ... hold partial sums of the same columns
 #pragma unroll
-  for (int e = 0; e < EPC; ++e) {
-    if (CPR == 16) {
+  for (int e = 0; e < PG::EPC; ++e) {
+    if (PG::CPR == 16) {
       acc[e] += bfly<4>(acc[e]);
       acc[e] += bfly<5>(acc[e]);
     } else {
@@ -76,16 +79,31 @@ __global__ void __launch_bounds__(kQaThreads) k_pool_q(PoolArgs a) {
       acc[e] += bfly<5>(acc[e]);
     }
   }
+}
+
+// One wave per query block; the means go to qbar (used when N > 2048).
+template <int B, bool I8>
+__global__ void __launch_bounds__(kQaThreads) k_pool_q(PoolArgs a) {
+  const int h = blockIdx.y;
+  if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
+  using PG = PoolGeo<B, I8>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int blk = blockIdx.x * (kQaThreads / 64) + wave, ch = lane % PG::CPR, rr = lane / PG::CPR;
+  if (blk >= a.N) return;
+  float acc[PG::EPC];
+  pool_block<B, I8>(a.Q, a.sQ, (size_t)h * a.S + (size_t)blk * B, acc);
   if (rr == 0) {
-    float4 *dst = (float4 *)(a.qbar + ((size_t)h * a.N + blk) * 128 + ch * EPC);
+    float4 *dst = (float4 *)(a.qbar + ((size_t)h * a.N + blk) * 128 + ch * PG::EPC);
 #pragma unroll
-    for (int e = 0; e < EPC / 4; ++e)
+    for (int e = 0; e < PG::EPC / 4; ++e)
       dst[e] = make_float4(acc[4 * e] / B, acc[4 * e + 1] / B, acc[4 * e + 2] / B, acc[4 * e + 3] / B);
   }
 }
 
 struct QaArgs {
-  int N, G, R, nw32;
+  const uint8_t *Q;  // query tokens (pooled in the 16-row kernel)
+  const float *sQ;
+  int S, N, G, R, nw32;
   float sigma, gamma;
   const uint8_t *pattern;
   const float *qbar, *kbar;
@@ -118,11 +136,13 @@ __device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev,
 }
 
 // Logits of 16 query-aware rows on the fp32 matrix cores (16x16x4): the
-// workgroup's pooled queries are the A operand (lane l: row l % 16, quarter
-// l / 16 of every 16-wide slice of d), each wave sweeps 16-column tiles of K-bar
-// as the B operand, 32 products per tile; rows then select as above.
+// workgroup first pools its 16 query blocks (two per wave, read straight from
+// Q) into LDS; those means are the A operand (lane l: row l % 16, quarter
+// l / 16 of every 16-wide slice of d), each wave sweeps 16-column tiles of
+// K-bar as the B operand, 32 products per tile; rows then select as above.
 // Used while 16 rows of logits fit in LDS (N <= 2048).
 constexpr int kQa16Threads = 512;
+template <int B, bool I8>
 __global__ void __launch_bounds__(kQa16Threads) k_qa_rows16(QaArgs a) {
   const int h = blockIdx.y;
   if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
@@ -132,11 +152,28 @@ __global__ void __launch_bounds__(kQa16Threads) k_qa_rows16(QaArgs a) {
   const int rows = min(16, N - i0);
   const int g = h / a.G;
   float *ev = smem;                                   // [16][N] logits / weights
-  uint32_t *words = (uint32_t *)(ev + (size_t)16 * N);  // [8 waves][nw32]
+  float *qs = ev + (size_t)16 * N;                    // [16][128] pooled queries
+  uint32_t *words = (uint32_t *)(qs + 16 * 128);      // [8 waves][nw32]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 4, rl = lane & 15;
 
+  {
+    using PG = PoolGeo<B, I8>;
+    const int ch = lane % PG::CPR, rr = lane / PG::CPR;
+    for (int r = wave; r < rows; r += kQa16Threads / 64) {
+      float acc[PG::EPC];
+      pool_block<B, I8>(a.Q, a.sQ, (size_t)h * a.S + (size_t)(i0 + r) * B, acc);
+      if (rr == 0) {
+        float4 *dst = (float4 *)(qs + r * 128 + ch * PG::EPC);
+#pragma unroll
+        for (int e = 0; e < PG::EPC / 4; ++e)
+          dst[e] = make_float4(acc[4 * e] / B, acc[4 * e + 1] / B, acc[4 * e + 2] / B, acc[4 * e + 3] / B);
+      }
+    }
+  }
+  __syncthreads();
+
   f32x4 qa[8];
-  const float *qrow = a.qbar + ((size_t)h * N + min(i0 + rl, N - 1)) * 128 + 4 * q;
+  const float *qrow = qs + min(rl, rows - 1) * 128 + 4 * q;
 #pragma unroll
   for (int t = 0; t < 8; ++t) qa[t] = *(const f32x4 *)(qrow + 16 * t);
   const int ntile = (i0 + rows - 1) / 16 + 1;         // column tiles covering j <= i0 + rows - 1
@@ -218,10 +255,36 @@ hipError_t run_pool(const Plan &p, const PoolArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int B, bool I8>
+hipError_t run_qa16(const Plan &p, const QaArgs &a, hipStream_t st) {
+  const size_t lds = sizeof(float) * ((size_t)16 * p.N + 16 * 128) + sizeof(uint32_t) * 8 * p.nw32;
+  const void *fn = (const void *)k_qa_rows16<B, I8>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_qa_rows16<B, I8>), dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
                         const uint8_t *pattern, const Work &w, hipStream_t st) {
+  QaArgs a;
+  a.Q = (const uint8_t *)Q;
+  a.sQ = sQ;
+  a.S = p.S; a.N = p.N; a.G = p.G; a.nw32 = p.nw32;
+  a.R = p.N >= 2048 ? (p.N >= 4096 ? 2 : 4) : 8;
+  a.sigma = 1.0f / sqrtf((float)p.d);
+  a.gamma = gamma;
+  a.pattern = pattern;
+  a.qbar = w.qbar;
+  a.kbar = w.kbar;
+  a.rowbits = w.rowbits;
+  if (p.N <= 2048) {   // pooling fused into the row kernel
+    if (p.B == 64) return i8 ? run_qa16<64, true>(p, a, st) : run_qa16<64, false>(p, a, st);
+    if (p.B == 128) return i8 ? run_qa16<128, true>(p, a, st) : run_qa16<128, false>(p, a, st);
+    return i8 ? run_qa16<256, true>(p, a, st) : run_qa16<256, false>(p, a, st);
+  }
   PoolArgs pa;
   pa.Q = (const uint8_t *)Q;
   pa.sQ = sQ;
@@ -233,23 +296,6 @@ hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, 
   else if (p.B == 128) e = i8 ? run_pool<128, true>(p, pa, st) : run_pool<128, false>(p, pa, st);
   else e = i8 ? run_pool<256, true>(p, pa, st) : run_pool<256, false>(p, pa, st);
   if (e != hipSuccess) return e;
-
-  QaArgs a;
-  a.N = p.N; a.G = p.G; a.nw32 = p.nw32;
-  a.R = p.N >= 2048 ? (p.N >= 4096 ? 2 : 4) : 8;
-  a.sigma = 1.0f / sqrtf((float)p.d);
-  a.gamma = gamma;
-  a.pattern = pattern;
-  a.qbar = w.qbar;
-  a.kbar = w.kbar;
-  a.rowbits = w.rowbits;
-  if (p.N <= 2048) {
-    const size_t lds = sizeof(float) * (size_t)16 * p.N + sizeof(uint32_t) * 8 * p.nw32;
-    e = hipFuncSetAttribute((const void *)k_qa_rows16, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_qa_rows16, dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
-    return hipGetLastError();
-  }
   const size_t lds = sizeof(float) * ((size_t)a.R * p.N + a.R * 128) + sizeof(uint32_t) * 4 * p.nw32;
   e = hipFuncSetAttribute((const void *)k_qa_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;

@@ -257,13 +257,15 @@ struct Stat1Args {
 
 // Every workgroup arrives, then waits until all have; the wait is bounded so
 // every wave exits even if the launch did not keep all workgroups resident.
+// The counter is polled with relaxed loads (each acquire load would also
+// invalidate the L2 of the polling workgroup's XCD); one fence follows the wait.
 __device__ void grid_barrier(unsigned int *bar, unsigned int nblocks, int32_t *status) {
   __syncthreads();
   if (threadIdx.x == 0) {
     __threadfence();
     atomicAdd(bar, 1u);
     unsigned int spins = 0;
-    while (__hip_atomic_load(bar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < nblocks) {
+    while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nblocks) {
       __builtin_amdgcn_s_sleep(4);
       if (++spins > (1u << 24)) {
         atomicOr((unsigned int *)status, (unsigned int)FP_STATUS_WAIT_TIMEOUT);
@@ -281,15 +283,34 @@ struct KStage {
   static constexpr int KP = (PIECES + NT - 1) / NT;
   u32x4 r[KP];
   float s;
+  // Every thread issues the same KP (+1) loads (indices past the block repeat its last
+  // piece and are never stored), so the number of loads in flight is the same on every
+  // path and the wait before a stage's store leaves the other stage's loads in flight.
   __device__ __forceinline__ void load(const StatArgs &a, int g, int j) {
     const size_t row0 = (size_t)g * a.S + (size_t)j * B;
     const uint8_t *src = a.K + row0 * RB;
 #pragma unroll
     for (int u = 0; u < KP; ++u) {
-      const int idx = threadIdx.x + u * NT;
-      if (idx < PIECES) r[u] = *(const u32x4 *)(src + (size_t)idx * 16);
+      const int idx = min((int)threadIdx.x + u * NT, PIECES - 1);
+      r[u] = *(const u32x4 *)(src + (size_t)idx * 16);
     }
-    if (I8 && threadIdx.x < B) s = a.sK[row0 + threadIdx.x];
+    if (I8) s = a.sK[row0 + min((int)threadIdx.x, B - 1)];
+  }
+  // bf16: column sums of this thread's pieces (all in 16-byte column chunk
+  // threadIdx.x % CPR, since NT is a multiple of CPR), rows in order.
+  __device__ __forceinline__ void colsum(float acc[8]) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int u = 0; u < KP; ++u) {
+      if ((int)threadIdx.x + u * NT < PIECES) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[2 * w] += bf16lo(r[u][w]);
+          acc[2 * w + 1] += bf16hi(r[u][w]);
+        }
+      }
+    }
   }
   __device__ __forceinline__ void store(uint8_t *ks, float *sk) const {
 #pragma unroll
@@ -301,7 +322,9 @@ struct KStage {
   }
 };
 
-template <int B, int NT, int TPW, bool I8>
+// KBS: the chunk's pooled key blocks are kept in LDS and written after the block loop
+// (no stores among the loads of the K stream); otherwise each block's is stored at once.
+template <int B, int NT, int TPW, bool I8, bool KBS>
 __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
   const StatArgs &a = args.s;
   constexpr int QT = B / 32, NWV = NT / 64, RG = NT / 64;
@@ -316,6 +339,7 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
   const int j0 = chunk * cpb, nb = min(N, j0 + cpb) - j0;
   constexpr int NTL = NWV * TPW;                                  // tile slots
   float *red = part + (size_t)NTL * cpb * 64;                     // [cpb][NTL][2]
+  float *kbs = red + (size_t)cpb * NTL * 2;                       // [cpb][128] pooled key blocks (KBS)
 
   u32x4 qf[TPW][Tile<I8>::KS];
   float qscale[TPW], mref[TPW], lsum[TPW];
@@ -335,21 +359,52 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     lsum[u] = 0.0f;
   }
 
+  // The Q fragments (and scales) are waited for here, before any K block is in flight:
+  // otherwise the compiler, unable to prove them loaded inside the block loop, waits for
+  // every outstanding load at their first use there, including the next blocks' prefetch.
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+
   // K blocks stream through registers two blocks ahead of their use (two stages, alternating)
   KStage<B, NT, I8> stg0, stg1;
-  if (nb > 0) stg0.load(a, g, j0);
-  if (nb > 1) stg1.load(a, g, j0 + 1);
+  stg0.load(a, g, j0);                      // nb >= 1 for every workgroup of the grid
+  stg1.load(a, g, j0 + min(1, nb - 1));
   auto block = [&](int jj, KStage<B, NT, I8> &stg) {
     const int j = j0 + jj;
     // (the previous block's closing barrier has already retired every read of ks, sk and kpart)
+    if constexpr (!I8) {
+      // bf16 mean-pooled key block from the staged registers: lanes l, l + 16, l + 32,
+      // l + 48 of a wave hold the same column chunk; each wave's sums go to kpart[wave]
+      static_assert(NT % KStage<B, NT, I8>::CPR == 0 && KStage<B, NT, I8>::CPR == 16, "column chunk per lane");
+      float cs[8];
+      stg.colsum(cs);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        cs[e] += bfly<4>(cs[e]);
+        cs[e] += bfly<5>(cs[e]);
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kpart[wave][8 * lane + e] = cs[e];
+      }
+    }
     stg.store(ks, sk);
     __syncthreads();
-    if (jj + 2 < nb) stg.load(a, g, j + 2);
+    // unconditional, so every path through the loop has the same loads in flight (past the
+    // chunk's end the stage re-reads its last block, still in L2, and is never stored)
+    stg.load(a, g, j0 + min(jj + 2, nb - 1));
     const bool diag = (j == N - 1);
+    if constexpr (!I8) {
+      if (threadIdx.x < 128) {
+        float sm = 0.0f;
+        for (int q = 0; q < RG; ++q) sm += kpart[q][threadIdx.x];
+        if constexpr (KBS) kbs[jj * 128 + threadIdx.x] = sm / (float)B;
+        else a.kbar[((size_t)g * N + j) * 128 + threadIdx.x] = sm / (float)B;
+      }
+    }
 
-    // mean-pooled key block: RG row groups of two columns per thread (one 2-column read
+    // int8: mean-pooled key block from LDS: RG row groups of two columns per thread (one 2-column read
     // per row, rows rg, rg + RG, ... in two interleaved partial sums), combined in order
-    {
+    if constexpr (I8) {
       const int dp = threadIdx.x & 63, rg = threadIdx.x >> 6;
       float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
 #pragma unroll 4
@@ -386,7 +441,96 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
       float lo_acc = 0.0f, hi_acc = 0.0f;
       float *prow = part + ((size_t)(wave * TPW + u) * cpb) * 64;   // [cpb][32][2] of this tile
       const int tq = t % QT;            // this wave's 32 query rows are tq*32 .. tq*32+31
-      for (int kt = 0; kt < QT; ++kt) {
+      bool piped = false;
+      if constexpr (TPW == 1 && NT <= 768 && B <= 128) {
+        if (!diag) {
+          // Software-pipelined form for every block but the last: the wave visits its key
+          // tiles in the order tq + 1, tq + 2, ... (mod QT), so the one tile whose keys fall on
+          // both sides of the query rows (kt == tq) comes last, at a fixed position; the
+          // products of the next tile are issued between the exponentials of the current
+          // one.  The tile loop has no branch: the new reference maximum is chosen by a
+          // select and the running sums are rescaled every tile (by exactly 1 where the
+          // maximum stays); the partials stored for earlier blocks are rescaled once, after
+          // the loop, by the product of the block's factors, 2^(m_start - m_end).
+          piped = true;
+          const float m_start = mref[u];
+          auto tile = [&](int kt) {
+            if constexpr (!I8) {
+              const uint8_t *arow = ks + (kt * 32 + (lane & 31)) * Tile<I8>::Stride + 16 * (lane >> 5);
+              f32x16 acc = {};
+#pragma unroll
+              for (int s = 0; s < 8; ++s) acc = mfma_bf16(*(const u32x4 *)(arow + 32 * s), qf[u][s], acc);
+              return acc;
+            } else {
+              float x[16];
+              tile_scores<I8>(ks, sk, qf[u], 1.0f, kt, 1.0f, x);
+              f32x16 r;
+#pragma unroll
+              for (int e = 0; e < 16; ++e) r[e] = x[e];
+              return r;
+            }
+          };
+          f32x16 nx = tile((tq + 1) % QT);
+#pragma unroll
+          for (int pos = 0; pos < QT; ++pos) {
+            const int kt = (tq + 1 + pos) % QT;
+            const f32x16 x = nx;
+            if (pos + 1 < QT) nx = tile((tq + 2 + pos) % QT);
+            float mx = fmaxf(x[0], x[1]);
+#pragma unroll
+            for (int r = 2; r < 16; ++r) mx = fmaxf(mx, x[r]);
+            mx = fmaxf(mx, xor32(mx)) * qscale[u];
+            const bool grow = mx > mref[u] + kHeadroom;
+            const float mnew = grow ? mx : mref[u];
+            const float alpha = fast_exp2(mref[u] - mnew);   // exactly 1 where the maximum stays
+            lo_acc *= alpha;
+            hi_acc *= alpha;
+            lsum[u] *= alpha;
+            mref[u] = mnew;
+            const float qs = qscale[u], mneg = -mnew;
+            if (pos + 1 < QT) {
+              // all keys of the tile lie on one side of the wave's query rows
+              float e = 0.0f;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) e += fast_exp2(fmaf(x[r], qs, mneg));
+              const bool below = kt < tq;
+              lo_acc += below ? e : 0.0f;
+              hi_acc += below ? 0.0f : e;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const float e = fast_exp2(fmaf(x[r], qs, mneg));
+                if (kt * 32 + acc_row(r, lane) <= qrow[u]) lo_acc += e;
+                else hi_acc += e;
+              }
+            }
+            // the tile's sums are needed here (an empty use), so they stay with the next
+            // tile's products instead of sinking below the branch after the loop
+            asm volatile("" ::"v"(lo_acc), "v"(hi_acc));
+            if (pos + 1 < QT && !I8) {
+              // interleave: the next tile's products, one operand read ahead, each followed by
+              // a share of this tile's vector work
+              __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+              for (int g8 = 0; g8 < 8; ++g8) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+              }
+            }
+          }
+          const bool moved = mref[u] != m_start;
+          if (__any(moved)) {
+            const float ab = fast_exp2(m_start - mref[u]);
+            if (moved && lane < 32)
+              for (int q = 0; q < jj; ++q) {
+                prow[q * 64 + 2 * lane] *= ab;
+                prow[q * 64 + 2 * lane + 1] *= ab;
+              }
+          }
+        }
+      }
+      for (int kt = 0; kt < (piped ? 0 : QT); ++kt) {
         if (diag && kt > tq) break;     // keys after every query row of the tile
         float x[16];
         tile_scores<I8>(ks, sk, qf[u], 1.0f, kt, 1.0f, x);
@@ -446,15 +590,26 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
       }
     }
     __syncthreads();
-    if (threadIdx.x < 128) {
-      float s = 0.0f;
-      for (int q = 0; q < RG; ++q) s += kpart[q][threadIdx.x];
-      a.kbar[((size_t)g * N + j) * 128 + threadIdx.x] = s / (float)B;
+    if constexpr (I8) {
+      if (threadIdx.x < 128) {
+        float sm = 0.0f;
+        for (int q = 0; q < RG; ++q) sm += kpart[q][threadIdx.x];
+        if constexpr (KBS) kbs[jj * 128 + threadIdx.x] = sm / (float)B;
+        else a.kbar[((size_t)g * N + j) * 128 + threadIdx.x] = sm / (float)B;
+      }
     }
   };
-  for (int jj = 0; jj < nb; jj += 2) {
+  // pairs of blocks, then an odd last block: no block of the loop body is conditional
+  int jj = 0;
+  for (; jj + 1 < nb; jj += 2) {
     block(jj, stg0);
-    if (jj + 1 < nb) block(jj + 1, stg1);
+    block(jj + 1, stg1);
+  }
+  if (jj < nb) block(jj, stg0);
+  if constexpr (KBS) {
+    // the chunk's pooled key blocks, written once the stream is done (no stores among its loads)
+    __syncthreads();
+    for (int k = threadIdx.x; k < nb * 128; k += NT) a.kbar[((size_t)g * N + j0) * 128 + k] = kbs[k];
   }
 
   // per-chunk (m_ref, sum) of every row, then the grid-wide merge
@@ -474,10 +629,23 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     if (t >= ntiles) continue;
     const int h = g * G + t / QT;
     const float2 *pp = a.part + ((size_t)h * B + qrow[u]) * a.nch;
-    float M = kNegBig;
-    for (int c = 0; c < a.nch; ++c) M = fmaxf(M, pp[c].x);
-    float L = 0.0f;
-    for (int c = 0; c < a.nch; ++c) L += pp[c].y * exp2f(pp[c].x - M);
+    // the row's per-chunk pairs, up to 32 loaded together (one memory round trip per batch);
+    // batches merge into the running (M, L), chunks in order
+    float M = kNegBig, L = 0.0f;
+    constexpr int CB = 32;
+    for (int c0 = 0; c0 < a.nch; c0 += CB) {
+      float2 v[CB];
+#pragma unroll
+      for (int k = 0; k < CB; ++k) v[k] = c0 + k < a.nch ? pp[c0 + k] : make_float2(kNegBig, 0.0f);
+      float Mb = M;
+#pragma unroll
+      for (int k = 0; k < CB; ++k) Mb = fmaxf(Mb, v[k].x);
+      float Lb = L * exp2f(M - Mb);
+#pragma unroll
+      for (int k = 0; k < CB; ++k) Lb += v[k].y * exp2f(v[k].x - Mb);
+      M = Mb;
+      L = Lb;
+    }
     const float wr = exp2f(mref[u] - M) / ((float)B * L);
     const float *prow = part + ((size_t)(wave * TPW + u) * cpb) * 64;
     for (int q = 0; q < nb; ++q) {
@@ -536,7 +704,31 @@ hipError_t dispatch(const Plan &p, const StatArgs &a, hipStream_t st) {
 
 
 // Single pass when every workgroup (one per CU) can hold its chunk's partials
-// in LDS and all are co-resident; *used tells the caller whether it ran.
+// in LDS and all are co-resident; *used tells the caller whether it ran.  The
+// pooled key blocks stay in LDS too when they fit (for 64-token blocks, whose
+// chunks are twice as long, they are otherwise stored block by block).
+template <int B, int NT, int TPW, bool I8, bool KBS>
+hipError_t launch1(const Plan &p, const StatArgs &a, size_t lds, unsigned int *bar, int32_t *status,
+                   hipStream_t st, bool *used) {
+  const int cus = cu_count();
+  const void *fn = (const void *)k_ig_stats1<B, NT, TPW, I8, KBS>;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, lds);
+  if (e != hipSuccess) return e;
+  if (per_cu < 1 || (long)a.nch * p.Hkv > (long)per_cu * cus) return hipSuccess;
+  // The grid (one workgroup per CU, at most per_cu per CU) fits the device at
+  // once, and the launch follows the previous kernel of the stream, so all
+  // workgroups are resident together; the barrier's wait is bounded anyway.
+  Stat1Args args{a, bar, status};
+  hipLaunchKernelGGL((k_ig_stats1<B, NT, TPW, I8, KBS>), dim3(a.nch, p.Hkv), dim3(NT), lds, st, args);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  *used = true;
+  return hipSuccess;
+}
+
 template <int B, int NT, int TPW, bool I8>
 hipError_t run1(const Plan &p, StatArgs a, unsigned int *bar, int32_t *status, hipStream_t st,
                 bool *used) {
@@ -549,26 +741,16 @@ hipError_t run1(const Plan &p, StatArgs a, unsigned int *bar, int32_t *status, h
   if (nch < 1 || nch > p.nch) return hipSuccess;
   const int cpb = (p.N + nch - 1) / nch;
   nch = (p.N + cpb - 1) / cpb;
-  const size_t lds = sizeof(float) * ((size_t)NTL * cpb * 64 + (size_t)cpb * NTL * 2);
-  const size_t static_lds = B * Tile<I8>::Stride + 4 * (NT / 64) * 128 + (I8 ? 4 * B : 4);
-  if (lds + static_lds > 160 * 1024) return hipSuccess;
-  const void *fn = (const void *)k_ig_stats1<B, NT, TPW, I8>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, NT, lds);
-  if (e != hipSuccess) return e;
-  if (per_cu < 1 || (long)nch * p.Hkv > (long)per_cu * cus) return hipSuccess;
   a.nch = nch;
   a.cpb = cpb;
-  // The grid (one workgroup per CU, at most per_cu per CU) fits the device at
-  // once, and the launch follows the previous kernel of the stream, so all
-  // workgroups are resident together; the barrier's wait is bounded anyway.
-  Stat1Args args{a, bar, status};
-  hipLaunchKernelGGL((k_ig_stats1<B, NT, TPW, I8>), dim3(nch, p.Hkv), dim3(NT), lds, st, args);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  *used = true;
+  const size_t lds = sizeof(float) * ((size_t)NTL * cpb * 64 + (size_t)cpb * NTL * 2);
+  const size_t lds_kbs = lds + sizeof(float) * (size_t)cpb * 128;
+  const size_t static_lds = B * Tile<I8>::Stride + 4 * (NT / 64) * 128 + (I8 ? 4 * B : 4);
+  if (lds_kbs + static_lds <= 160 * 1024)
+    return launch1<B, NT, TPW, I8, true>(p, a, lds_kbs, bar, status, st, used);
+  if constexpr (B == 64) {
+    if (lds + static_lds <= 160 * 1024) return launch1<B, NT, TPW, I8, false>(p, a, lds, bar, status, st, used);
+  }
   return hipSuccess;
 }
 
