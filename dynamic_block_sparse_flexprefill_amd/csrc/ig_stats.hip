@@ -606,11 +606,6 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     block(jj + 1, stg1);
   }
   if (jj < nb) block(jj, stg0);
-  if constexpr (KBS) {
-    // the chunk's pooled key blocks, written once the stream is done (no stores among its loads)
-    __syncthreads();
-    for (int k = threadIdx.x; k < nb * 128; k += NT) a.kbar[((size_t)g * N + j0) * 128 + k] = kbs[k];
-  }
 
   // per-chunk (m_ref, sum) of every row, then the grid-wide merge
 #pragma unroll
@@ -622,6 +617,11 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     }
   }
   grid_barrier(args.bar, gridDim.x * gridDim.y, args.status);
+  if constexpr (KBS) {
+    // the chunk's pooled key blocks (read only by later kernels): written after the K stream,
+    // so no stores sit among its loads, and after the barrier, so its fence has little to write back
+    for (int k = threadIdx.x; k < nb * 128; k += NT) a.kbar[((size_t)g * N + j0) * 128 + k] = kbs[k];
+  }
 
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
