@@ -557,9 +557,16 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             }
           }
           if (diag_t) {
+            // 4 * (lane / 32), the half-wave term of acc_row, computed here (one instruction the
+            // compiler cannot hoist): kept live across the loop it is spilled, and its reload
+            // waits for every load in flight, the next chunk's included
+            int hw4;
+            asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_and_b32 %0, 32, %0\n\tv_lshrrev_b32 %0, 3, %0" : "=v"(hw4));
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (key_t + (I8 ? swap23(acc_row(r, lane)) : acc_row(r, lane)) > qtok) x[r] = -INFINITY;
+            for (int r = 0; r < 16; ++r) {
+              const int row = 8 * (r >> 2) + hw4 + (r & 3);
+              if (key_t + (I8 ? swap23(row) : row) > qtok) x[r] = -INFINITY;
+            }
           }
           float mx = x[0];
 #pragma unroll
