@@ -88,17 +88,29 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
     __syncthreads();
   }
 
-  // Pooled logits against every mean-pooled key block.
-  for (int j = tid; j < N; j += kFinThreads) {
-    const float4 *kr = (const float4 *)(a.kbar + ((size_t)g * N + j) * 128);
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int c = 0; c < 32; ++c) {
-      const float4 k4 = kr[c];
-      acc += qb[4 * c] * k4.x + qb[4 * c + 1] * k4.y + qb[4 * c + 2] * k4.z + qb[4 * c + 3] * k4.w;
+  // Pooled logits against every mean-pooled key block: a wave takes 16 blocks at a time,
+  // four adjacent lanes per block, each lane a contiguous quarter (32 columns, 128 bytes);
+  // the four partial dots are combined across the lanes.
+  {
+    const int wv = tid >> 6, ln = tid & 63, rr = ln >> 2, qq = ln & 3;
+    const float *qp = qb + 32 * qq;
+    for (int j0 = wv * 16; j0 < N; j0 += (kFinThreads / 64) * 16) {
+      const int j = j0 + rr;
+      float acc = 0.0f;
+      if (j < N) {
+        const float4 *kr = (const float4 *)(a.kbar + ((size_t)g * N + j) * 128 + 32 * qq);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float4 k4 = kr[c];
+          acc += qp[4 * c] * k4.x + qp[4 * c + 1] * k4.y + qp[4 * c + 2] * k4.z + qp[4 * c + 3] * k4.w;
+        }
+      }
+      acc += bfly<0>(acc);
+      acc += bfly<1>(acc);
+      if (qq == 0 && j < N) ev[j] = a.sigma * acc;
     }
-    ev[j] = a.sigma * acc;
   }
+  __syncthreads();   // ev[j] is read below by thread j, not by the lane that wrote it
   float mx = kNegBig;
   for (int j = tid; j < N; j += kFinThreads) mx = fmaxf(mx, ev[j]);
   mx = block_max(mx, redf);
