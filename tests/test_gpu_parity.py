@@ -151,6 +151,9 @@ INDEX_CASES = [
     ("tiny-G5", dict(S=2048, Hq=10, Hkv=2), 0.9),
     ("tiny-b64", dict(S=2048, b=64, Hq=4, Hkv=2), 0.9),
     ("tiny-b64-G3", dict(S=4096, b=64, Hq=6, Hkv=2), 0.9),
+    # N = 2560 > 2048: query blocks pooled through the workspace (two launches), rows longer
+    # than 1024 blocks selected from LDS; one vertical-slash and one query-aware group
+    ("N2560-b64", dict(S=64 * 2560, b=64, Hq=2, Hkv=2), 0.9),
 ]
 
 
@@ -186,7 +189,7 @@ def test_index_bf16(name, kw, gamma):
     _index_case(cfg(**kw), gamma)
 
 
-INDEX_I8_CASES = INDEX_CASES[:2] + INDEX_CASES[4:7] + INDEX_CASES[11:13]
+INDEX_I8_CASES = INDEX_CASES[:2] + INDEX_CASES[4:7] + INDEX_CASES[11:14]
 
 
 @pytest.mark.parametrize("name,kw,gamma", INDEX_I8_CASES, ids=[c[0] for c in INDEX_I8_CASES])
