@@ -29,6 +29,8 @@
 // TPW tiles of 32 last-block query rows and keeps their Q fragments in
 // registers; scores are computed transposed (keys x queries) on the 32x32x16
 // bf16 (or 32x32x32 int8) matrix cores so that every lane holds one query row.
+#include <cstdlib>
+
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 
@@ -805,9 +807,14 @@ hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *s
   a.c2 = kLog2e / sqrtf((float)p.d);
   a.part = w.part; a.rowml = w.rowml; a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
   bool used = false;
-  hipError_t e = i8 ? dispatch1<true>(p, a, w.bar, status, st, &used)
-                    : dispatch1<false>(p, a, w.bar, status, st, &used);
-  if (e != hipSuccess || used) return e;
+  // FPATTN_STATS_TWO_PASS=1 (read on every call) selects the two-pass form for any shape, so
+  // that tests can check it at sizes whose single-pass partials would fit in LDS
+  const char *force = getenv("FPATTN_STATS_TWO_PASS");
+  if (!(force && force[0] == '1')) {
+    hipError_t e = i8 ? dispatch1<true>(p, a, w.bar, status, st, &used)
+                      : dispatch1<false>(p, a, w.bar, status, st, &used);
+    if (e != hipSuccess || used) return e;
+  }
   return i8 ? dispatch<true>(p, a, st) : dispatch<false>(p, a, st);
 }
 

@@ -158,6 +158,10 @@ int64_t fp_job_capacity(const fp_shape *shape);
  * K is read from HBM once, in increasing block order; nothing of size
  * Hq x S is written to memory.  Errors: FP_EINVAL, FP_EUNSUPPORTED,
  * FP_EWORKSPACE, FP_EHIP; capacity overflow through out->status.
+ * The environment variable FPATTN_STATS_TWO_PASS=1 (read on every call, for
+ * tests) makes the statistics stream K twice instead of holding per-row
+ * partials on chip -- the form otherwise used only when those do not fit;
+ * results agree to rounding.
  */
 int fp_index(const fp_shape *shape, const void *Q, const void *K,
              float gamma, float tau, fp_index_out *out,

@@ -198,6 +198,19 @@ def test_index_i8(name, kw, gamma):
     _index_case(cfg(**kw), gamma, i8=True)
 
 
+TWO_PASS_CASES = [c for c in INDEX_CASES if c[0] in ("tiny", "tiny-G16", "tiny-N70", "tiny-b256-G4", "tiny-b64-G3")]
+
+
+@pytest.mark.parametrize("name,kw,gamma", TWO_PASS_CASES, ids=[c[0] for c in TWO_PASS_CASES])
+@pytest.mark.parametrize("i8", [False, True], ids=["bf16", "i8"])
+def test_index_two_pass_statistics(name, kw, gamma, i8, monkeypatch):
+    """The two-pass statistics form (used when the single pass's partials do not fit in LDS)
+    forced at small sizes."""
+    say(f"index {'i8' if i8 else 'bf16'} two-pass statistics {name} gamma={gamma}")
+    monkeypatch.setenv("FPATTN_STATS_TWO_PASS", "1")
+    _index_case(cfg(**kw), gamma, i8=i8)
+
+
 def test_index_deterministic_and_end_to_end():
     say("index + attn determinism, tiny")
     c = cfg()
