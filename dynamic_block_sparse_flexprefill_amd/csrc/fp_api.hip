@@ -37,6 +37,7 @@ int make_plan(const fp_shape *s, Plan *p) {
   p->off_sel = o;    o = align_up(o + sizeof(uint32_t) * Hq * 2 * p->nw32);
   p->off_rowbits = o; o = align_up(o + sizeof(uint32_t) * Hq * (size_t)N * p->nw32);
   p->off_qbar = o;   o = align_up(o + sizeof(float) * Hq * (size_t)N * 128);
+  p->off_pe = o;     o = align_up(o + sizeof(float) * Hq * (size_t)N);
   p->off_jwork = o;  o = align_up(o + sizeof(int32_t) * Hkv * N);
   p->off_bar = o;    o = align_up(o + 256);
   p->off_jkeys = o;  o = align_up(o + sizeof(unsigned long long) * Hkv * N);
@@ -56,6 +57,7 @@ Work carve(const Plan &p, void *ws) {
   w.sel = (uint32_t *)(b + p.off_sel);
   w.rowbits = (uint32_t *)(b + p.off_rowbits);
   w.qbar = (float *)(b + p.off_qbar);
+  w.pe = (float *)(b + p.off_pe);
   w.jwork = (int32_t *)(b + p.off_jwork);
   w.bar = (unsigned int *)(b + p.off_bar);
   w.jkeys = (unsigned long long *)(b + p.off_jkeys);
@@ -142,8 +144,9 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   hipStream_t st = (hipStream_t)stream;
   Work w = carve(p, ws);
   FP_LAUNCH(launch_status_init(out->status, w.bar, st));
-  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st));
-  FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st));
+  bool have_pe = false;
+  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st, &have_pe));
+  FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, have_pe));
   FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st));
   FP_LAUNCH(launch_rows_and_jobs(p, out, w, st));
   return FP_OK;

@@ -25,6 +25,7 @@ struct Plan {
   size_t off_sel;    // u32    [Hq*2*nw32] vertical / slash selections (bit sets)
   size_t off_rowbits; // u32   [Hq*N*nw32] row bit sets (query-aware rows; every row in fp_build_jobs)
   size_t off_qbar;   // float  [Hq*N*d]    mean-pooled query blocks (query-aware heads)
+  size_t off_pe;     // float  [Hq*N]      pooled-estimate logits sigma * qbar_last . kbar_j
   size_t off_jwork;  // int32  [Hkv*N]     work per grouped job
   size_t off_bar;    // u32    [64]        [0]: grid-barrier counter of the single-pass statistics;
                      //                     [32]: unit counter of the persistent attention kernel
@@ -42,6 +43,7 @@ struct Work {
   float *lo, *hi, *kbar;
   uint32_t *sel, *rowbits;
   float *qbar;
+  float *pe;
   int32_t *jwork;
   unsigned int *bar;
   unsigned long long *jkeys;
@@ -52,13 +54,15 @@ Work carve(const Plan &p, void *ws);
 // ---- launchers: each returns hipSuccess or the launch error.
 // Statistics of the last query block against every key block
 // (two passes over K: row max / sum, then block mass).
+// *have_pe: whether the statistics also wrote the pooled-estimate logits (w.pe).
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ,
                            const void *K, const float *sK, const Work &w, int32_t *status,
-                           hipStream_t st);
+                           hipStream_t st, bool *have_pe);
 // Per head: pooled estimate, divergence, pattern, vertical / slash selection.
+// have_pe: the pooled-estimate logits are in w.pe (else they are computed here).
 hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,
                               float gamma, float tau, const fp_index_out *out,
-                              const Work &w, hipStream_t st);
+                              const Work &w, hipStream_t st, bool have_pe);
 // Query-aware rows: pooled queries of every block against pooled keys.
 hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
                         const uint8_t *pattern, const Work &w, hipStream_t st);

@@ -27,6 +27,7 @@ struct FinArgs {
   int S, N, B, G, nw32;
   float sigma, gamma, tau;
   const float *lo, *hi, *kbar;
+  const float *pe;          // pooled-estimate logits [Hq][N] from the statistics, or NULL
   uint8_t *pattern;
   float *jsd, *stats;
   uint32_t *sel;
@@ -49,6 +50,10 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
   __shared__ float redf[kFinThreads / 64];
   const int tid = threadIdx.x, h = blockIdx.x, g = h / a.G;
 
+  if (a.pe) {
+    // the statistics pass already formed sigma * mean(Q_last) . mean(K_j)
+    for (int j = tid; j < N; j += kFinThreads) ev[j] = a.pe[(size_t)h * N + j];
+  } else {
   // Mean of the last query block: 16-byte loads, rows split over RG groups
   // (the threads past RG * CPR only join the barriers), group partials
   // combined in order.
@@ -111,6 +116,7 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
     }
   }
   __syncthreads();   // ev[j] is read below by thread j, not by the lane that wrote it
+  }
   float mx = kNegBig;
   for (int j = tid; j < N; j += kFinThreads) mx = fmaxf(mx, ev[j]);
   mx = block_max(mx, redf);
@@ -165,7 +171,7 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
 
 hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,
                               float gamma, float tau, const fp_index_out *out, const Work &w,
-                              hipStream_t st) {
+                              hipStream_t st, bool have_pe) {
   FinArgs a;
   a.Q = (const uint8_t *)Q;
   a.sQ = sQ;
@@ -173,6 +179,7 @@ hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float
   a.sigma = 1.0f / sqrtf((float)p.d);
   a.gamma = gamma; a.tau = tau;
   a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
+  a.pe = have_pe ? w.pe : nullptr;
   a.pattern = out->pattern; a.jsd = out->jsd; a.stats = out->stats;
   a.sel = w.sel;
   const size_t lds = sizeof(float) * (3 * (size_t)p.N + 128 + kFinRowGroups * 128) + sizeof(uint32_t) * 2 * p.nw32;

@@ -48,6 +48,8 @@ struct StatArgs {
   float2 *rowml;      // [Hq*B] merged (max, sum)
   float *lo, *hi;     // [Hq*N]
   float *kbar;        // [Hkv*N*128]
+  float *pe;          // [Hq*N] pooled-estimate logits (single pass only)
+  float sigma;        // 1/sqrt(d)
 };
 
 template <bool I8> struct Tile;
@@ -341,7 +343,8 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
   const int j0 = chunk * cpb, nb = min(N, j0 + cpb) - j0;
   constexpr int NTL = NWV * TPW;                                  // tile slots
   float *red = part + (size_t)NTL * cpb * 64;                     // [cpb][NTL][2]
-  float *kbs = red + (size_t)cpb * NTL * 2;                       // [cpb][128] pooled key blocks (KBS)
+  float *qsm = red + (size_t)cpb * NTL * 2;                       // [G][128] mean of each last query block
+  float *kbs = qsm + (size_t)G * 128;                             // [cpb][128] pooled key blocks (KBS)
 
   u32x4 qf[TPW][Tile<I8>::KS];
   float qscale[TPW], mref[TPW], lsum[TPW];
@@ -359,6 +362,47 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     qscale[u] = (I8 ? a.sQ[tok] : 1.0f) * a.c2;
     mref[u] = -1e30f;
     lsum[u] = 0.0f;
+  }
+
+  // Mean of each of the group's last query blocks, for the pooled estimate, summed through
+  // the staging buffer ks before the K stream starts: thread (16-byte column chunk, head,
+  // row group) adds its rows in order, then the row groups are combined in order.
+  {
+    constexpr int CPR = Tile<I8>::RowBytes / 16, EPC = I8 ? 16 : 8, KSB = B * Tile<I8>::Stride;
+    const int R = max(1, min(NT / (CPR * G), KSB / (G * 512)));
+    float *qpart = (float *)ks;                                   // [G][R][128]
+    const int tid = threadIdx.x;
+    if (tid < CPR * G * R) {
+      const int ch = tid % CPR, hh = (tid / CPR) % G, rg = tid / (CPR * G);
+      const size_t tok0 = (size_t)(g * G + hh) * S + (S - B);
+      float acc[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] = 0.0f;
+      for (int r = rg; r < B; r += R) {
+        const u32x4 v = *(const u32x4 *)(a.Q + (tok0 + r) * Tile<I8>::RowBytes + ch * 16);
+        if (!I8) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc[2 * e] += bf16lo(v[e]);
+            acc[2 * e + 1] += bf16hi(v[e]);
+          }
+        } else {
+          const float sc = a.sQ[tok0 + r];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] += sc * (float)(int8_t)((v[e >> 2] >> (8 * (e & 3))) & 0xffu);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) qpart[(hh * R + rg) * 128 + ch * EPC + e] = acc[e];
+    }
+    __syncthreads();
+    for (int k = tid; k < G * 128; k += NT) {
+      const int hh = k / 128, dd = k % 128;
+      float sm = 0.0f;
+      for (int q = 0; q < R; ++q) sm += qpart[(hh * R + q) * 128 + dd];
+      qsm[k] = sm / (float)B;
+    }
+    __syncthreads();                                              // ks is about to stage K
   }
 
   // The Q fragments (and scales) are waited for here, before any K block is in flight:
@@ -624,6 +668,20 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     // so no stores sit among its loads, and after the barrier, so its fence has little to write back
     for (int k = threadIdx.x; k < nb * 128; k += NT) a.kbar[((size_t)g * N + j0) * 128 + k] = kbs[k];
   }
+  // pooled-estimate logits of the chunk's blocks, sigma * mean(Q_last) . mean(K_j) (K-bar from
+  // LDS, or as this workgroup stored it before the barrier)
+  for (int k = threadIdx.x; k < G * nb; k += NT) {
+    const int hh = k % G, q = k / G;
+    const float4 *kr = (const float4 *)(KBS ? kbs + (size_t)q * 128 : a.kbar + ((size_t)g * N + j0 + q) * 128);
+    const float4 *qr = (const float4 *)(qsm + hh * 128);
+    float sm = 0.0f;
+#pragma unroll 8
+    for (int c = 0; c < 32; ++c) {
+      const float4 kv = kr[c], qv = qr[c];
+      sm += qv.x * kv.x + qv.y * kv.y + qv.z * kv.z + qv.w * kv.w;
+    }
+    a.pe[(size_t)(g * G + hh) * N + j0 + q] = a.sigma * sm;
+  }
 
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
@@ -745,7 +803,7 @@ hipError_t run1(const Plan &p, StatArgs a, unsigned int *bar, int32_t *status, h
   nch = (p.N + cpb - 1) / cpb;
   a.nch = nch;
   a.cpb = cpb;
-  const size_t lds = sizeof(float) * ((size_t)NTL * cpb * 64 + (size_t)cpb * NTL * 2);
+  const size_t lds = sizeof(float) * ((size_t)NTL * cpb * 64 + (size_t)cpb * NTL * 2 + (size_t)p.G * 128);
   const size_t lds_kbs = lds + sizeof(float) * (size_t)cpb * 128;
   const size_t static_lds = B * Tile<I8>::Stride + 4 * (NT / 64) * 128 + (I8 ? 4 * B : 4);
   if (lds_kbs + static_lds <= 160 * 1024)
@@ -797,7 +855,8 @@ int cu_count() {
 }
 
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
-                           const float *sK, const Work &w, int32_t *status, hipStream_t st) {
+                           const float *sK, const Work &w, int32_t *status, hipStream_t st,
+                           bool *have_pe) {
   StatArgs a;
   a.Q = (const uint8_t *)Q;
   a.sQ = sQ;
@@ -806,6 +865,9 @@ hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *s
   a.S = p.S; a.N = p.N; a.G = p.G; a.nch = p.nch; a.cpb = p.cpb;
   a.c2 = kLog2e / sqrtf((float)p.d);
   a.part = w.part; a.rowml = w.rowml; a.lo = w.lo; a.hi = w.hi; a.kbar = w.kbar;
+  a.pe = w.pe;
+  a.sigma = 1.0f / sqrtf((float)p.d);
+  *have_pe = false;
   bool used = false;
   // FPATTN_STATS_TWO_PASS=1 (read on every call) selects the two-pass form for any shape, so
   // that tests can check it at sizes whose single-pass partials would fit in LDS
@@ -813,6 +875,7 @@ hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *s
   if (!(force && force[0] == '1')) {
     hipError_t e = i8 ? dispatch1<true>(p, a, w.bar, status, st, &used)
                       : dispatch1<false>(p, a, w.bar, status, st, &used);
+    *have_pe = used;
     if (e != hipSuccess || used) return e;
   }
   return i8 ? dispatch<true>(p, a, st) : dispatch<false>(p, a, st);
