@@ -155,6 +155,12 @@ INDEX_CASES = [
     # than 1024 blocks selected from LDS; one vertical-slash and one query-aware group
     ("N2560-b64", dict(S=64 * 2560, b=64, Hq=2, Hkv=2), 0.9),
 ]
+# the largest block counts: N = 4608 (> 4096: two query-aware rows per workgroup) and the
+# supported maximum N = 8192 (one vertical-slash head)
+LARGE_N_CASES = [
+    ("N4608-b64", dict(S=64 * 4608, b=64, Hq=2, Hkv=2), 0.9),
+    ("N8192-b64-vs", dict(S=64 * 8192, b=64, Hq=1, Hkv=1, vs_frac=1.0), 0.9),
+]
 
 
 def _index_case(c, gamma, i8=False):
@@ -196,6 +202,33 @@ INDEX_I8_CASES = INDEX_CASES[:2] + INDEX_CASES[4:7] + INDEX_CASES[11:14]
 def test_index_i8(name, kw, gamma):
     say(f"index i8 {name} gamma={gamma}")
     _index_case(cfg(**kw), gamma, i8=True)
+
+
+@pytest.mark.parametrize("name,kw,gamma", LARGE_N_CASES, ids=[c[0] for c in LARGE_N_CASES])
+def test_index_and_attn_large_n(name, kw, gamma):
+    """Index parity at the largest block counts, then attention on sampled query blocks
+    (the first, the last and six others) against the oracle on the device's CSR."""
+    say(f"index + attn bf16 {name} gamma={gamma}")
+    c = cfg(**kw)
+    idx, _ = _index_case(c, gamma)
+    L = gen.make(c)
+    Qd, Kd, Vd = P.layer_on_device(L)
+    O = fpa.attn(Qd, Kd, Vd, idx)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = [(h, i) for h in range(c.Hq) for i in sorted({0, c.N - 1, *rng.integers(1, c.N - 1, 6).tolist()})]
+    rp, ci = P.gpu_rows(idx)
+    ref = oracle.attn.attn(L.f32("q"), L.f32("k"), L.f32("v"), rp, ci, c.b, rows=rows)
+    Oh = O.float().cpu().numpy()
+    worst, sq, cnt = 0.0, 0.0, 0
+    for (h, i), ref_o in ref.items():
+        dlt = Oh[h, i * c.b:(i + 1) * c.b].astype(np.float64) - ref_o
+        worst = max(worst, float(np.abs(dlt).max()))
+        sq += float((dlt * dlt).sum())
+        cnt += dlt.size
+    rms = (sq / cnt) ** 0.5
+    say(f"  attention on {len(rows)} sampled query blocks: maxabs {worst:.3e} rms {rms:.3e}")
+    assert worst <= MAXABS and rms <= RMS
 
 
 TWO_PASS_CASES = [c for c in INDEX_CASES if c[0] in ("tiny", "tiny-G16", "tiny-N70", "tiny-b256-G4", "tiny-b64-G3")]
