@@ -8,7 +8,8 @@ include/fpattn.h:
                                           key blocks, grouped-query job list)
   attn(Q, K, V, index)         -> O      (block-sparse causal attention, bf16)
 
-plus their W8A8 forms index_i8 / attn_i8.  This package only marshals
+plus their W8A8 forms index_i8 / attn_i8, and index_batch / attn_batch for
+ragged batches of sequences packed one after another.  This package only marshals
 arguments; there is no CPU path.
 """
 from .binding import (  # noqa: F401
@@ -17,4 +18,5 @@ from .binding import (  # noqa: F401
     VERTICAL_SLASH, QUERY_AWARE, FpError, FpShape, FpIndexOut, Index, Workspace,
     lib, strerror, shape_of, workspace_bytes, csr_capacity, job_capacity,
     index, index_i8, build_jobs, attn, attn_i8, probe_qk_i8, LIB_PATH,
+    index_batch, attn_batch, unpack,
 )

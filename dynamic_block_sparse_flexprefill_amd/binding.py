@@ -78,8 +78,11 @@ def lib() -> ctypes.CDLL:
         L.fp_attn.argtypes = [sp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
         L.fp_attn_i8.argtypes = [sp, _P, _P, _P, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
         L.fp_probe_qk_i8.argtypes = [sp, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]
+        lp = ctypes.POINTER(ctypes.c_int32)
+        L.fp_index_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
+        L.fp_attn_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8"):
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -284,6 +287,60 @@ def attn_i8(Q8, sQ, K8, sK, V8, sV, idx: Index, *, out: Optional[torch.Tensor] =
                           ctypes.byref(o), _ptr(O), _ptr(ws.buf), ws.nbytes, _stream(stream))
     if rc:
         raise FpError(rc, "fp_attn_i8")
+    return O
+
+
+def unpack(t: torch.Tensor, seqlens, H: int, d: int = 128) -> list:
+    """Views [H, S_s, d] of the sequences packed one after another in t (no copy)."""
+    views, off = [], 0
+    for S in seqlens:
+        n = H * int(S) * d
+        views.append(t[off:off + n].view(H, int(S), d))
+        off += n
+    return views
+
+
+def index_batch(Q: torch.Tensor, K: torch.Tensor, seqlens, b: int, Hq: int, Hkv: int, gamma: float,
+                tau: float, *, d: int = 128, stats: bool = False, ws: Optional[Workspace] = None,
+                stream=None) -> list:
+    """fp_index_batch: one Index per sequence of a ragged batch; Q (K) holds the sequences'
+    [Hq, S_s, d] ([Hkv, S_s, d]) bf16 blocks one after another, as 1-D tensors."""
+    lens = [int(S) for S in seqlens]
+    tot = sum(lens)
+    _check(Q, "Q", torch.bfloat16, (Hq * tot * d,))
+    _check(K, "K", torch.bfloat16, (Hkv * tot * d,))
+    outs = [Index.empty(shape_of(S, b, Hq, Hkv, d), Q.device, stats=stats) for S in lens]
+    shape = shape_of(max(lens), b, Hq, Hkv, d)     # S is ignored; the longest sizes the workspace
+    ws = _ws(shape, ws, Q.device)
+    arr = (FpIndexOut * len(lens))(*[o.c_struct() for o in outs])
+    rc = lib().fp_index_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens), _ptr(Q),
+                              _ptr(K), gamma, tau, arr, _ptr(ws.buf), ws.nbytes, _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_index_batch")
+    return outs
+
+
+def attn_batch(Q, K, V, seqlens, idxs: list, *, out: Optional[torch.Tensor] = None,
+               ws: Optional[Workspace] = None, stream=None) -> torch.Tensor:
+    """fp_attn_batch: block-sparse attention of a ragged batch packed as for index_batch;
+    returns O packed like Q."""
+    lens = [int(S) for S in seqlens]
+    if len(idxs) != len(lens):
+        raise TypeError("one Index per sequence is needed")
+    sh = idxs[0].shape
+    Hq, Hkv, d, b, tot = sh.Hq, sh.Hkv, sh.d, sh.b, sum(lens)
+    _check(Q, "Q", torch.bfloat16, (Hq * tot * d,))
+    _check(K, "K", torch.bfloat16, (Hkv * tot * d,))
+    _check(V, "V", torch.bfloat16, (Hkv * tot * d,))
+    O = torch.empty_like(Q) if out is None else out
+    _check(O, "O", torch.bfloat16, (Hq * tot * d,))
+    shape = shape_of(max(lens), b, Hq, Hkv, d)
+    ws = _ws(shape, ws, Q.device)
+    arr = (FpIndexOut * len(lens))(*[ix.c_struct() for ix in idxs])
+    rc = lib().fp_attn_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens), _ptr(Q),
+                             _ptr(K), _ptr(V), arr, _ptr(O), _ptr(ws.buf), ws.nbytes, _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_attn_batch")
     return O
 
 

@@ -98,7 +98,7 @@ const char *fp_strerror(int code) {
   switch (code) {
     case FP_OK: return "ok";
     case FP_EINVAL: return "invalid argument (null pointer, S % b != 0, Hq % Hkv != 0, gamma not in (0,1], tau < 0 or NaN, or a capacity below one entry per row)";
-    case FP_EUNSUPPORTED: return "unsupported shape (needs d = 128, b in {128, 256}, S/b <= 8192, (Hq/Hkv)*b <= 2048)";
+    case FP_EUNSUPPORTED: return "unsupported shape (needs d = 128, b in {64, 128, 256}, S/b <= 8192, Hq/Hkv <= 16, (Hq/Hkv)*b <= 2048)";
     case FP_EWORKSPACE: return "workspace smaller than fp_workspace_bytes()";
     case FP_ECAPACITY: return "CSR capacity exceeded (device status)";
     case FP_EHIP: return "HIP launch or query failed";
@@ -205,6 +205,67 @@ int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ, const i
                const float *sK, const int8_t *V8, const float *sV, const fp_index_out *csr,
                void *O, void *ws, size_t ws_bytes, void *stream) {
   return attn_common(shape, true, Q8, sQ, K8, sK, V8, sV, csr, O, ws, ws_bytes, stream);
+}
+
+// Ragged batches: every sequence is checked before anything is enqueued; the
+// workspace must cover the longest sequence's plan and is reused in order.
+static int batch_check(const fp_shape *shape, int nseq, const int32_t *seqlens, size_t ws_bytes,
+                       const fp_index_out *outs, bool need_pattern) {
+  if (!shape || nseq < 1 || !seqlens || !outs) return FP_EINVAL;
+  size_t need = 0;
+  for (int s = 0; s < nseq; ++s) {
+    fp_shape one = *shape;
+    one.S = seqlens[s];
+    Plan p;
+    int rc = make_plan(&one, &p);
+    if (rc) return rc;
+    const fp_index_out *o = outs + s;
+    if (need_pattern) {
+      if ((rc = check_out(p, o, true))) return rc;
+    } else if (!o->row_ptr || !o->col_idx || !o->job_ptr || !o->job_blk || !o->job_mask || !o->job_order) {
+      return FP_EINVAL;
+    }
+    need = p.total > need ? p.total : need;
+  }
+  return ws_bytes < need ? FP_EWORKSPACE : FP_OK;
+}
+
+int fp_index_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const void *Q, const void *K,
+                   float gamma, float tau, fp_index_out *outs, void *ws, size_t ws_bytes, void *stream) {
+  if (!Q || !K || !ws) return FP_EINVAL;
+  int rc = check_params(gamma, tau);
+  if (rc || (rc = batch_check(shape, nseq, seqlens, ws_bytes, outs, true))) return rc;
+  const uint8_t *q = (const uint8_t *)Q, *k = (const uint8_t *)K;
+  for (int s = 0; s < nseq; ++s) {
+    fp_shape one = *shape;
+    one.S = seqlens[s];
+    if ((rc = index_common(&one, false, q, nullptr, k, nullptr, gamma, tau, outs + s, ws, ws_bytes, stream)))
+      return rc;
+    q += (size_t)one.Hq * one.S * one.d * 2;      // bf16
+    k += (size_t)one.Hkv * one.S * one.d * 2;
+  }
+  return FP_OK;
+}
+
+int fp_attn_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const void *Q, const void *K,
+                  const void *V, const fp_index_out *csrs, void *O, void *ws, size_t ws_bytes, void *stream) {
+  if (!Q || !K || !V || !O || !ws) return FP_EINVAL;
+  int rc = batch_check(shape, nseq, seqlens, ws_bytes, csrs, false);
+  if (rc) return rc;
+  const uint8_t *q = (const uint8_t *)Q, *k = (const uint8_t *)K, *v = (const uint8_t *)V;
+  uint8_t *o = (uint8_t *)O;
+  for (int s = 0; s < nseq; ++s) {
+    fp_shape one = *shape;
+    one.S = seqlens[s];
+    if ((rc = attn_common(&one, false, q, nullptr, k, nullptr, v, nullptr, csrs + s, o, ws, ws_bytes, stream)))
+      return rc;
+    const size_t qb = (size_t)one.Hq * one.S * one.d * 2, kb = (size_t)one.Hkv * one.S * one.d * 2;
+    q += qb;
+    o += qb;
+    k += kb;
+    v += kb;
+  }
+  return FP_OK;
 }
 
 int fp_probe_qk_i8(const fp_shape *shape, const int8_t *Q8, const int8_t *K8, int h, int i,

@@ -216,6 +216,31 @@ int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
                void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Ragged batches of independent sequences (bf16), e.g. several prompts of
+ * different lengths in one call.  Sequence s has S_s = seqlens[s] tokens (host
+ * array, each a multiple of shape->b; shape->S is ignored) and is packed after
+ * sequence s - 1 in its own head-major layout: Q holds [Hq, S_s, d] blocks one
+ * after another, K (and V, O) [Hkv, S_s, d] (O like Q).  (A batch of equal
+ * lengths is also one call of fp_index / fp_attn with B*Hq and B*Hkv heads,
+ * since every quantity is per head or per KV group.)
+ *   outs / csrs: host array of nseq index outputs, one per sequence, each
+ *                sized for its own S_s as in fp_index.
+ *   ws: one workspace of at least fp_workspace_bytes of the longest sequence;
+ *       the sequences run in order on the stream and reuse it.
+ * Every sequence is checked before anything is enqueued (FP_EINVAL,
+ * FP_EUNSUPPORTED, FP_EWORKSPACE as for one sequence); FP_EHIP if a launch
+ * fails, after the earlier sequences have been enqueued.  Each sequence's
+ * capacity overflow is reported through its own status word.
+ */
+int fp_index_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
+                   const void *Q, const void *K, float gamma, float tau,
+                   fp_index_out *outs, void *ws, size_t ws_bytes, void *stream);
+int fp_attn_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
+                  const void *Q, const void *K, const void *V,
+                  const fp_index_out *csrs, void *O,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Test hook for the W8A8 score product: out[c][r] = Q8[h, i*b + r] .
  * K8[h / G, j*b + c] (exact int32) for r, c in [0, b), computed with the same
  * int8 matrix-core tile code that fp_index_i8 and fp_attn_i8 use.

@@ -22,7 +22,7 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fp_index", "fp_index_i8", "fp_attn", "fp_attn_i8", "fp_build_jobs",
               "fp_workspace_bytes", "fp_csr_capacity", "fp_job_capacity", "fp_strerror",
-              "fp_version", "fp_probe_qk_i8"):
+              "fp_version", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch"):
         assert n in names
 
 
@@ -125,3 +125,28 @@ def test_workspace_grows_with_shape():
     assert b > a > 0
     # nothing of size Hq x S x b: the 128K workspace stays far below the b x S score matrix of one head
     assert b < 128 * 131072 * 4
+
+
+def test_batch_rejects_bad_arguments():
+    """Ragged batches: every sequence is checked before anything is enqueued."""
+    L = fpa.lib()
+    P = ctypes.c_void_p(0x1000)
+    sh = fpa.shape_of(2048, 128, 4, 2)
+    lens = [1024, 384, 2048]
+    outs = (fpa.FpIndexOut * 3)(*[_dummy_out(fpa.shape_of(S, 128, 4, 2)) for S in lens])
+    arr = (ctypes.c_int32 * 3)(*lens)
+    big = 1 << 30
+    assert L.fp_index_batch(ctypes.byref(sh), 0, arr, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
+    assert L.fp_index_batch(ctypes.byref(sh), 3, None, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
+    assert L.fp_index_batch(ctypes.byref(sh), 3, arr, P, P, 1.5, 0.1, outs, P, big, None) == fpa.FP_EINVAL
+    assert L.fp_index_batch(ctypes.byref(sh), 3, arr, P, P, 0.9, 0.1, outs, P, 64, None) == fpa.FP_EWORKSPACE
+    ragged = (ctypes.c_int32 * 3)(1024, 300, 2048)       # 300 is not a multiple of b
+    assert L.fp_index_batch(ctypes.byref(sh), 3, ragged, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
+    small = (fpa.FpIndexOut * 3)(outs[0], _dummy_out(fpa.shape_of(384, 128, 4, 2), col_cap=4), outs[2])
+    assert L.fp_index_batch(ctypes.byref(sh), 3, arr, P, P, 0.9, 0.1, small, P, big, None) == fpa.FP_EINVAL
+    # the workspace must cover the longest sequence
+    need = fpa.workspace_bytes(fpa.shape_of(2048, 128, 4, 2))
+    assert L.fp_attn_batch(ctypes.byref(sh), 3, arr, P, P, P, outs, P, P, need - 1, None) == fpa.FP_EWORKSPACE
+    assert L.fp_attn_batch(ctypes.byref(sh), 3, arr, P, P, None, outs, P, P, big, None) == fpa.FP_EINVAL
+    bad = fpa.shape_of(2048, 128, 4, 2, 64)
+    assert L.fp_attn_batch(ctypes.byref(bad), 3, arr, P, P, P, outs, P, P, big, None) == fpa.FP_EUNSUPPORTED

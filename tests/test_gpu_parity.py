@@ -231,6 +231,32 @@ def test_index_and_attn_large_n(name, kw, gamma):
     assert worst <= MAXABS and rms <= RMS
 
 
+def test_ragged_batch():
+    """fp_index_batch / fp_attn_batch on three sequences of different lengths packed one
+    after another: every sequence's index and attention against the oracle."""
+    say("ragged batch: S = 1024, 384, 2048 (b = 128, Hq = 4, Hkv = 2)")
+    lens = [1024, 384, 2048]
+    cs = [cfg(S=S) for S in lens]
+    Ls = [gen.make(c) for c in cs]
+    dev = "cuda"
+    pack = lambda name: torch.cat([P.dev_bf16(getattr(L, name), dev).reshape(-1) for L in Ls])
+    Q, K, V = pack("q"), pack("k"), pack("v")
+    c0 = cs[0]
+    idxs = fpa.index_batch(Q, K, lens, c0.b, c0.Hq, c0.Hkv, c0.gamma, c0.tau)
+    O = fpa.attn_batch(Q, K, V, lens, idxs)
+    torch.cuda.synchronize()
+    Os = fpa.unpack(O, lens, c0.Hq)
+    for c, L, idx, Oc in zip(cs, Ls, idxs, Os):
+        assert int(idx.status.item()) == 0
+        ref = oi.index(L.f32("q"), L.f32("k"), c.b, c.gamma, c.tau)
+        P.compare_index(idx, ref, c.gamma, c.tau)
+        P.check_jobs(idx, c.G)
+        rp, ci = P.gpu_rows(idx)
+        mx, rms = P.attn_errors(Oc, oracle.attn.attn(L.f32("q"), L.f32("k"), L.f32("v"), rp, ci, c.b))
+        say(f"  S={c.S}: density {idx.density():.3f}, attention maxabs {mx:.2e} rms {rms:.2e}")
+        assert mx <= MAXABS and rms <= RMS
+
+
 TWO_PASS_CASES = [c for c in INDEX_CASES if c[0] in ("tiny", "tiny-G16", "tiny-N70", "tiny-b256-G4", "tiny-b64-G3")]
 
 
