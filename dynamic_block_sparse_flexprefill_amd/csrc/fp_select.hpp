@@ -21,7 +21,7 @@ namespace fp {
 
 // x[0..n) in LDS (values >= 0; elements visited as j = lane + 64 k).  Selected
 // bits are OR-ed into words[0 .. ceil(n/32)) (LDS, cleared by the caller).
-__device__ void wave_select_lds(const float *x, int n, float gamma, uint32_t *words) {
+__device__ __forceinline__ void wave_select_lds(const float *x, int n, float gamma, uint32_t *words) {
   const int lane = threadIdx.x & 63;
   float part = 0.0f, mxl = 0.0f;
   for (int j = lane; j < n; j += 64) {
@@ -42,6 +42,7 @@ __device__ void wave_select_lds(const float *x, int n, float gamma, uint32_t *wo
     const uint32_t mid = lo + ((hi - lo) >> 1);
     const float th = __uint_as_float(mid);
     float s = 0.0f;
+#pragma unroll 8
     for (int j = lane; j < n; j += 64) s += (x[j] >= th) ? x[j] : 0.0f;
     s = wave_sum(s);
     if (s >= target) lo = mid; else hi = mid;
@@ -72,9 +73,13 @@ __device__ void wave_select_lds(const float *x, int n, float gamma, uint32_t *wo
 
 constexpr int kGreedySteps = 24;
 
-// n <= 1024: the values live in registers (16 per lane).
-__device__ void wave_select_reg(const float *x, int n, float gamma, uint32_t *words) {
-  constexpr int VPL = 16;
+// n <= 64 * VPL: the values live in registers (VPL per lane, element lane + 64 k
+// in slot k), so every pass of the search is unrolled register work.  Per-lane
+// sums visit the elements in the same order for any VPL (absent slots add 0),
+// so the selection does not depend on which VPL serves a row.
+template <int VPL>
+__device__ __forceinline__ void wave_select_reg(const float *x, int n, float gamma, uint32_t *words) {
+  static_assert(VPL >= 1 && VPL <= 32, "one bit of `taken` per slot");
   const int lane = threadIdx.x & 63;
   float v[VPL];
   float part = 0.0f, mxl = 0.0f;
@@ -161,8 +166,17 @@ __device__ void wave_select_reg(const float *x, int n, float gamma, uint32_t *wo
   }
 }
 
+// The register form sized to the row (the cost of a search pass grows with VPL),
+// up to MAXV values per lane; longer rows search in LDS.  MAXV = 32 costs about
+// 36 more registers than 16, so kernels whose occupancy matters take 32 only
+// when their rows can exceed 1024 elements.
+template <int MAXV = 16>
 __device__ __forceinline__ void wave_select(const float *x, int n, float gamma, uint32_t *words) {
-  if (n <= 1024) wave_select_reg(x, n, gamma, words);
+  static_assert(MAXV == 16 || MAXV == 32, "register forms for up to 1024 or 2048 elements");
+  if (n <= 256) wave_select_reg<4>(x, n, gamma, words);
+  else if (n <= 512) wave_select_reg<8>(x, n, gamma, words);
+  else if (n <= 1024) wave_select_reg<16>(x, n, gamma, words);
+  else if (MAXV == 32 && n <= 2048) wave_select_reg<MAXV>(x, n, gamma, words);
   else wave_select_lds(x, n, gamma, words);
 }
 

@@ -162,7 +162,7 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
   if (wave < 2) {
     uint32_t *m = msk + wave * a.nw32;
     for (int w = tid & 63; w < a.nw32; w += 64) m[w] = 0u;
-    if (!qa) wave_select(wave == 0 ? vv : sv, N, a.gamma, m);
+    if (!qa) wave_select<32>(wave == 0 ? vv : sv, N, a.gamma, m);
     for (int w = tid & 63; w < a.nw32; w += 64) out[wave * a.nw32 + w] = m[w];
   }
 }

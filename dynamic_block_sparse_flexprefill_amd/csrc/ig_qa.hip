@@ -113,6 +113,7 @@ struct QaArgs {
 // One wave per row of logits ev[r][0..i0+r]: softmax weights, selection
 // ([E] 3.1 cumulative-gamma rule), block 0 and the diagonal forced in, and the
 // row's bit set written to rowbits.  words: LDS, (blockDim / 64) * nw32 words.
+template <int MAXV>
 __device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev, uint32_t *words) {
   const int N = a.N, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwv = blockDim.x >> 6;
   uint32_t *wd = words + wave * a.nw32;
@@ -120,12 +121,14 @@ __device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev,
     const int i = i0 + r, n = i + 1;
     float *x = ev + (size_t)r * N;
     float mx = kNegBig;
+#pragma unroll 8
     for (int j = lane; j < n; j += 64) mx = fmaxf(mx, x[j]);
     mx = wave_max(mx);
+#pragma unroll 8
     for (int j = lane; j < n; j += 64) x[j] = expf(x[j] - mx);
     const int nwr = (i >> 5) + 1;
     for (int w = lane; w < nwr; w += 64) wd[w] = 0u;
-    wave_select(x, n, a.gamma, wd);
+    wave_select<MAXV>(x, n, a.gamma, wd);
     if (lane == 0) {
       atomicOr(&wd[0], 1u);
       atomicOr(&wd[i >> 5], 1u << (i & 31));
@@ -140,9 +143,10 @@ __device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev,
 // Q) into LDS; those means are the A operand (lane l: row l % 16, quarter
 // l / 16 of every 16-wide slice of d), each wave sweeps 16-column tiles of
 // K-bar as the B operand, 32 products per tile; rows then select as above.
-// Used while 16 rows of logits fit in LDS (N <= 2048).
+// Used while 16 rows of logits fit in LDS (N <= 2048); WIDE (N > 1024) selects rows
+// of up to 2048 blocks in registers.
 constexpr int kQa16Threads = 512;
-template <int B, bool I8>
+template <int B, bool I8, bool WIDE>
 __global__ void __launch_bounds__(kQa16Threads) k_qa_rows16(QaArgs a) {
   const int h = blockIdx.y;
   if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
@@ -202,7 +206,7 @@ __global__ void __launch_bounds__(kQa16Threads) k_qa_rows16(QaArgs a) {
     }
   }
   __syncthreads();
-  select_rows(a, h, i0, rows, ev, words);
+  select_rows<WIDE ? 32 : 16>(a, h, i0, rows, ev, words);
 }
 
 __global__ void __launch_bounds__(kQaThreads) k_qa_rows(QaArgs a) {
@@ -245,7 +249,7 @@ __global__ void __launch_bounds__(kQaThreads) k_qa_rows(QaArgs a) {
   }
   __syncthreads();
 
-  select_rows(a, h, i0, rows, ev, words);
+  select_rows<16>(a, h, i0, rows, ev, words);
 }
 
 template <int B, bool I8>
@@ -255,14 +259,19 @@ hipError_t run_pool(const Plan &p, const PoolArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int B, bool I8>
-hipError_t run_qa16(const Plan &p, const QaArgs &a, hipStream_t st) {
+template <int B, bool I8, bool WIDE>
+hipError_t launch_qa16(const Plan &p, const QaArgs &a, hipStream_t st) {
   const size_t lds = sizeof(float) * ((size_t)16 * p.N + 16 * 128) + sizeof(uint32_t) * 8 * p.nw32;
-  const void *fn = (const void *)k_qa_rows16<B, I8>;
+  const void *fn = (const void *)k_qa_rows16<B, I8, WIDE>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_qa_rows16<B, I8>), dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
+  hipLaunchKernelGGL((k_qa_rows16<B, I8, WIDE>), dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int B, bool I8>
+hipError_t run_qa16(const Plan &p, const QaArgs &a, hipStream_t st) {
+  return p.N > 1024 ? launch_qa16<B, I8, true>(p, a, st) : launch_qa16<B, I8, false>(p, a, st);
 }
 
 }  // namespace
