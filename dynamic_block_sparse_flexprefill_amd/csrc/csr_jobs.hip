@@ -202,38 +202,54 @@ struct ScanJob {
 // In-place exclusive scan of counts x[1..n] into offsets x[0..n] (x[0] = 0),
 // clamped to cap (the overflow is reported through `bit`).  Tiles of
 // kScanThreads * 8 counts; a tile's total fits 32 bits (counts <= N <= 8192),
-// the running carry is 64-bit.
+// the running carry is 64-bit.  One workgroup does a whole array, so its global
+// accesses are kept coalesced: a tile is loaded lane-consecutively into LDS,
+// each thread scans 8 consecutive counts from there, and the offsets go back
+// through LDS the same way (one pad word per 32 keeps both LDS patterns free of
+// bank conflicts).
 __device__ void scan_counts(const ScanJob &s, int32_t *status) {
-  __shared__ int wtot[kScanThreads / 64];
-  constexpr int E = 8;
+  constexpr int E = 8, T = kScanThreads;
+  __shared__ int wtot[T / 64];
+  __shared__ int stage[T * E + T * E / 32];
+  auto at = [](int i) { return i + (i >> 5); };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   long long carry = 0;
-  for (int base = 0; base < s.n; base += kScanThreads * E) {
+  for (int base = 0; base < s.n; base += T * E) {
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int k = base + u * T + tid;
+      stage[at(u * T + tid)] = k < s.n ? s.x[1 + k] : 0;
+    }
+    __syncthreads();
     int v[E];
     int loc = 0;
 #pragma unroll
     for (int u = 0; u < E; ++u) {
-      const int k = base + tid * E + u;
-      v[u] = k < s.n ? s.x[1 + k] : 0;
+      v[u] = stage[at(tid * E + u)];
       loc += v[u];
     }
     const int incl = wave_scan_incl(loc);
     if (lane == 63) wtot[wave] = incl;
     __syncthreads();
-    int t = lane < kScanThreads / 64 ? wtot[lane] : 0;
+    int t = lane < T / 64 ? wtot[lane] : 0;
     t = wave_scan_incl(t);
     const int wpre = wave > 0 ? __builtin_amdgcn_readlane(t, wave - 1) : 0;
-    const int tile = __builtin_amdgcn_readlane(t, kScanThreads / 64 - 1);
-    __syncthreads();                               // wtot is rewritten by the next tile
+    const int tile = __builtin_amdgcn_readlane(t, T / 64 - 1);
     long long run = carry + wpre + (incl - loc);
 #pragma unroll
     for (int u = 0; u < E; ++u) {
-      const int k = base + tid * E + u;
       run += v[u];
-      if (k < s.n) s.x[1 + k] = (int32_t)(run < s.cap ? run : s.cap);
+      stage[at(tid * E + u)] = (int32_t)(run < s.cap ? run : s.cap);
+    }
+    __syncthreads();                               // (wtot is rewritten only after the next one)
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const int k = base + u * T + tid;
+      if (k < s.n) s.x[1 + k] = stage[at(u * T + tid)];
     }
     carry += tile;
+    __syncthreads();                               // stage is refilled by the next tile
   }
   if (tid == 0) {
     s.x[0] = 0;
