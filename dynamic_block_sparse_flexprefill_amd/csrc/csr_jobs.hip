@@ -308,7 +308,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_sort(ScanJob s0, ScanJob 
 
 // With LDS, every workgroup first copies all Hkv * N sorted keys into LDS (at most
 // kRankLdsKeys) and searches there.
-constexpr int kRankLdsKeys = 8192;
+constexpr int kRankLdsKeys = 16384;       // 128 KiB of keys
 template <bool LDS>
 __global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, int32_t *order) {
   extern __shared__ unsigned long long skeys[];
