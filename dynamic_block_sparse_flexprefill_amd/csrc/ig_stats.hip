@@ -653,13 +653,17 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
   }
   if (jj < nb) block(jj, stg0);
 
-  // per-chunk (m_ref, sum) of every row, then the grid-wide merge
+  // per-chunk (m_ref, sum) of every row, then the grid-wide merge.  Stored chunk-major,
+  // [head][chunk][row], so that a wave's 32 rows are one contiguous 256-byte store here
+  // and one contiguous load per chunk in the merge (row-major, each lane's pairs would
+  // sit in a different cache line: 32 lines per instruction, and as many dirty lines
+  // for the barrier's release to write back)
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int t = wave * TPW + u;
     if (t < ntiles && lane < 32) {
       const int h = g * G + t / QT;
-      a.part[((size_t)h * B + qrow[u]) * a.nch + chunk] = make_float2(mref[u], lsum[u]);
+      a.part[((size_t)h * a.nch + chunk) * B + qrow[u]] = make_float2(mref[u], lsum[u]);
     }
   }
   grid_barrier(args.bar, gridDim.x * gridDim.y, args.status);
@@ -688,7 +692,7 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     const int t = wave * TPW + u;
     if (t >= ntiles) continue;
     const int h = g * G + t / QT;
-    const float2 *pp = a.part + ((size_t)h * B + qrow[u]) * a.nch;
+    const float2 *pp = a.part + (size_t)h * a.nch * B + qrow[u];   // chunk c at pp[c * B]
     // the row's per-chunk pairs, up to 32 loaded together (one memory round trip per batch);
     // batches merge into the running (M, L), chunks in order
     float M = kNegBig, L = 0.0f;
@@ -696,7 +700,7 @@ __global__ void __launch_bounds__(NT) k_ig_stats1(Stat1Args args) {
     for (int c0 = 0; c0 < a.nch; c0 += CB) {
       float2 v[CB];
 #pragma unroll
-      for (int k = 0; k < CB; ++k) v[k] = c0 + k < a.nch ? pp[c0 + k] : make_float2(kNegBig, 0.0f);
+      for (int k = 0; k < CB; ++k) v[k] = c0 + k < a.nch ? pp[(size_t)(c0 + k) * B] : make_float2(kNegBig, 0.0f);
       float Mb = M;
 #pragma unroll
       for (int k = 0; k < CB; ++k) Mb = fmaxf(Mb, v[k].x);
