@@ -641,15 +641,24 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     uint16_t *orow = a.O + tok * 128;
     if (live) {
+      // Lane (row, hf) holds columns 32 dt + 8 j + 4 hf + (0..3), j = 0..3, of its query row.
+      // One swap with the other half-wave per 32-bit word (groups j = 0, 1 offered by the upper
+      // half, j = 2, 3 by the lower) leaves each lane columns 32 dt + 16 hf + (0..15), stored as
+      // two 16-byte pieces: half as many store instructions, each still covering 32 rows.
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) {
+        uint32_t lo[4], hi[4];
 #pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          const int d0 = dt * 32 + 8 * rq + 4 * hf;
-          const u32x2 w = u32x2{pack_bf16x2(o[dt][4 * rq] * inv, o[dt][4 * rq + 1] * inv),
-                                pack_bf16x2(o[dt][4 * rq + 2] * inv, o[dt][4 * rq + 3] * inv)};
-          *(u32x2 *)(orow + d0) = w;
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t pa = pack_bf16x2(o[dt][2 * k] * inv, o[dt][2 * k + 1] * inv);        // j = 0, 1
+          const uint32_t pb = pack_bf16x2(o[dt][8 + 2 * k] * inv, o[dt][8 + 2 * k + 1] * inv);  // j = 2, 3
+          const auto sw = __builtin_amdgcn_permlane32_swap(pa, pb, false, false);
+          lo[k] = sw[0];
+          hi[k] = sw[1];
         }
+        *(u32x4 *)(orow + dt * 32 + 16 * hf) = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        *(u32x4 *)(orow + dt * 32 + 16 * hf + 8) = u32x4{lo[2], lo[3], hi[2], hi[3]};
+      }
     }
 
     cur = nxt;                                     // (every unit has a chunk barrier, which published the claim)
