@@ -8,8 +8,9 @@ include/fpattn.h:
                                           key blocks, grouped-query job list)
   attn(Q, K, V, index)         -> O      (block-sparse causal attention, bf16)
 
-plus their W8A8 forms index_i8 / attn_i8, and index_batch / attn_batch for
-ragged batches of sequences packed one after another.  This package only marshals
+plus their W8A8 forms index_i8 / attn_i8, and index_batch / attn_batch (and
+index_i8_batch / attn_i8_batch) for ragged batches of sequences packed one
+after another.  This package only marshals
 arguments; there is no CPU path.
 """
 from .binding import (  # noqa: F401
@@ -18,5 +19,5 @@ from .binding import (  # noqa: F401
     VERTICAL_SLASH, QUERY_AWARE, FpError, FpShape, FpIndexOut, Index, Workspace,
     lib, strerror, shape_of, workspace_bytes, csr_capacity, job_capacity,
     index, index_i8, build_jobs, attn, attn_i8, probe_qk_i8, LIB_PATH,
-    index_batch, attn_batch, unpack,
+    index_batch, attn_batch, index_i8_batch, attn_i8_batch, unpack,
 )

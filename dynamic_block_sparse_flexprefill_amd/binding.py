@@ -81,8 +81,12 @@ def lib() -> ctypes.CDLL:
         lp = ctypes.POINTER(ctypes.c_int32)
         L.fp_index_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_attn_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
+        L.fp_index_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
+        L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
+                                       ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch"):
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch",
+                     "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -341,6 +345,56 @@ def attn_batch(Q, K, V, seqlens, idxs: list, *, out: Optional[torch.Tensor] = No
                              _ptr(K), _ptr(V), arr, _ptr(O), _ptr(ws.buf), ws.nbytes, _stream(stream))
     if rc:
         raise FpError(rc, "fp_attn_batch")
+    return O
+
+
+def index_i8_batch(Q8, sQ, K8, sK, seqlens, b: int, Hq: int, Hkv: int, gamma: float, tau: float, *,
+                   d: int = 128, stats: bool = False, ws: Optional[Workspace] = None, stream=None) -> list:
+    """fp_index_i8_batch: index_batch for W8A8 inputs; Q8 / K8 int8 and their per-token scales
+    sQ / sK fp32, each packed sequence after sequence as 1-D tensors."""
+    lens = [int(S) for S in seqlens]
+    tot = sum(lens)
+    _check(Q8, "Q8", torch.int8, (Hq * tot * d,))
+    _check(K8, "K8", torch.int8, (Hkv * tot * d,))
+    _check(sQ, "sQ", torch.float32, (Hq * tot,))
+    _check(sK, "sK", torch.float32, (Hkv * tot,))
+    outs = [Index.empty(shape_of(S, b, Hq, Hkv, d), Q8.device, stats=stats) for S in lens]
+    shape = shape_of(max(lens), b, Hq, Hkv, d)
+    ws = _ws(shape, ws, Q8.device)
+    arr = (FpIndexOut * len(lens))(*[o.c_struct() for o in outs])
+    rc = lib().fp_index_i8_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens),
+                                 _ptr(Q8), _ptr(sQ), _ptr(K8), _ptr(sK), gamma, tau, arr, _ptr(ws.buf),
+                                 ws.nbytes, _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_index_i8_batch")
+    return outs
+
+
+def attn_i8_batch(Q8, sQ, K8, sK, V8, sV, seqlens, idxs: list, *, out: Optional[torch.Tensor] = None,
+                  ws: Optional[Workspace] = None, stream=None) -> torch.Tensor:
+    """fp_attn_i8_batch: W8A8 attention of a ragged batch packed as for index_i8_batch;
+    returns bf16 O packed like Q8."""
+    lens = [int(S) for S in seqlens]
+    if len(idxs) != len(lens):
+        raise TypeError("one Index per sequence is needed")
+    sh = idxs[0].shape
+    Hq, Hkv, d, b, tot = sh.Hq, sh.Hkv, sh.d, sh.b, sum(lens)
+    _check(Q8, "Q8", torch.int8, (Hq * tot * d,))
+    _check(K8, "K8", torch.int8, (Hkv * tot * d,))
+    _check(V8, "V8", torch.int8, (Hkv * tot * d,))
+    _check(sQ, "sQ", torch.float32, (Hq * tot,))
+    _check(sK, "sK", torch.float32, (Hkv * tot,))
+    _check(sV, "sV", torch.float32, (Hkv * tot,))
+    O = torch.empty(Hq * tot * d, dtype=torch.bfloat16, device=Q8.device) if out is None else out
+    _check(O, "O", torch.bfloat16, (Hq * tot * d,))
+    shape = shape_of(max(lens), b, Hq, Hkv, d)
+    ws = _ws(shape, ws, Q8.device)
+    arr = (FpIndexOut * len(lens))(*[ix.c_struct() for ix in idxs])
+    rc = lib().fp_attn_i8_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens),
+                                _ptr(Q8), _ptr(sQ), _ptr(K8), _ptr(sK), _ptr(V8), _ptr(sV), arr, _ptr(O),
+                                _ptr(ws.buf), ws.nbytes, _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_attn_i8_batch")
     return O
 
 

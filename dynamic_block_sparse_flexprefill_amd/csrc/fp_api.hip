@@ -230,42 +230,81 @@ static int batch_check(const fp_shape *shape, int nseq, const int32_t *seqlens, 
   return ws_bytes < need ? FP_EWORKSPACE : FP_OK;
 }
 
-int fp_index_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const void *Q, const void *K,
-                   float gamma, float tau, fp_index_out *outs, void *ws, size_t ws_bytes, void *stream) {
-  if (!Q || !K || !ws) return FP_EINVAL;
+// Sequence s's tensors follow sequence s - 1's: element bytes 2 (bf16) or 1 (int8), and the
+// int8 forms' per-token scales likewise, one fp32 per head and token.
+static int index_batch_common(const fp_shape *shape, bool i8, int nseq, const int32_t *seqlens,
+                              const void *Q, const float *sQ, const void *K, const float *sK, float gamma,
+                              float tau, fp_index_out *outs, void *ws, size_t ws_bytes, void *stream) {
+  if (!Q || !K || !ws || (i8 && (!sQ || !sK))) return FP_EINVAL;
   int rc = check_params(gamma, tau);
   if (rc || (rc = batch_check(shape, nseq, seqlens, ws_bytes, outs, true))) return rc;
+  const size_t eb = i8 ? 1 : 2;
   const uint8_t *q = (const uint8_t *)Q, *k = (const uint8_t *)K;
   for (int s = 0; s < nseq; ++s) {
     fp_shape one = *shape;
     one.S = seqlens[s];
-    if ((rc = index_common(&one, false, q, nullptr, k, nullptr, gamma, tau, outs + s, ws, ws_bytes, stream)))
-      return rc;
-    q += (size_t)one.Hq * one.S * one.d * 2;      // bf16
-    k += (size_t)one.Hkv * one.S * one.d * 2;
+    if ((rc = index_common(&one, i8, q, sQ, k, sK, gamma, tau, outs + s, ws, ws_bytes, stream))) return rc;
+    q += (size_t)one.Hq * one.S * one.d * eb;
+    k += (size_t)one.Hkv * one.S * one.d * eb;
+    if (i8) {
+      sQ += (size_t)one.Hq * one.S;
+      sK += (size_t)one.Hkv * one.S;
+    }
   }
   return FP_OK;
 }
 
-int fp_attn_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const void *Q, const void *K,
-                  const void *V, const fp_index_out *csrs, void *O, void *ws, size_t ws_bytes, void *stream) {
-  if (!Q || !K || !V || !O || !ws) return FP_EINVAL;
+static int attn_batch_common(const fp_shape *shape, bool i8, int nseq, const int32_t *seqlens, const void *Q,
+                             const float *sQ, const void *K, const float *sK, const void *V, const float *sV,
+                             const fp_index_out *csrs, void *O, void *ws, size_t ws_bytes, void *stream) {
+  if (!Q || !K || !V || !O || !ws || (i8 && (!sQ || !sK || !sV))) return FP_EINVAL;
   int rc = batch_check(shape, nseq, seqlens, ws_bytes, csrs, false);
   if (rc) return rc;
+  const size_t eb = i8 ? 1 : 2;
   const uint8_t *q = (const uint8_t *)Q, *k = (const uint8_t *)K, *v = (const uint8_t *)V;
   uint8_t *o = (uint8_t *)O;
   for (int s = 0; s < nseq; ++s) {
     fp_shape one = *shape;
     one.S = seqlens[s];
-    if ((rc = attn_common(&one, false, q, nullptr, k, nullptr, v, nullptr, csrs + s, o, ws, ws_bytes, stream)))
-      return rc;
-    const size_t qb = (size_t)one.Hq * one.S * one.d * 2, kb = (size_t)one.Hkv * one.S * one.d * 2;
-    q += qb;
-    o += qb;
-    k += kb;
-    v += kb;
+    if ((rc = attn_common(&one, i8, q, sQ, k, sK, v, sV, csrs + s, o, ws, ws_bytes, stream))) return rc;
+    const size_t qn = (size_t)one.Hq * one.S, kn = (size_t)one.Hkv * one.S;
+    q += qn * one.d * eb;
+    o += qn * one.d * 2;                          // bf16 output
+    k += kn * one.d * eb;
+    v += kn * one.d * eb;
+    if (i8) {
+      sQ += qn;
+      sK += kn;
+      sV += kn;
+    }
   }
   return FP_OK;
+}
+
+int fp_index_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const void *Q, const void *K,
+                   float gamma, float tau, fp_index_out *outs, void *ws, size_t ws_bytes, void *stream) {
+  return index_batch_common(shape, false, nseq, seqlens, Q, nullptr, K, nullptr, gamma, tau, outs, ws,
+                            ws_bytes, stream);
+}
+
+int fp_attn_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const void *Q, const void *K,
+                  const void *V, const fp_index_out *csrs, void *O, void *ws, size_t ws_bytes, void *stream) {
+  return attn_batch_common(shape, false, nseq, seqlens, Q, nullptr, K, nullptr, V, nullptr, csrs, O, ws,
+                           ws_bytes, stream);
+}
+
+int fp_index_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const int8_t *Q8,
+                      const float *sQ, const int8_t *K8, const float *sK, float gamma, float tau,
+                      fp_index_out *outs, void *ws, size_t ws_bytes, void *stream) {
+  return index_batch_common(shape, true, nseq, seqlens, Q8, sQ, K8, sK, gamma, tau, outs, ws, ws_bytes,
+                            stream);
+}
+
+int fp_attn_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, const int8_t *Q8,
+                     const float *sQ, const int8_t *K8, const float *sK, const int8_t *V8, const float *sV,
+                     const fp_index_out *csrs, void *O, void *ws, size_t ws_bytes, void *stream) {
+  return attn_batch_common(shape, true, nseq, seqlens, Q8, sQ, K8, sK, V8, sV, csrs, O, ws, ws_bytes,
+                           stream);
 }
 
 int fp_probe_qk_i8(const fp_shape *shape, const int8_t *Q8, const int8_t *K8, int h, int i,

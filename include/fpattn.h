@@ -241,6 +241,22 @@ int fp_attn_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
                   void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The same for W8A8 inputs (as fp_index_i8 / fp_attn_i8): Q8, K8, V8 packed
+ * like Q, K, V above (one byte per element), and the per-token scales packed
+ * the same way, sQ as [Hq, S_s] blocks and sK, sV as [Hkv, S_s] blocks one
+ * after another.  O is bf16, packed like Q.  Null scales give FP_EINVAL.
+ */
+int fp_index_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
+                      const int8_t *Q8, const float *sQ, const int8_t *K8,
+                      const float *sK, float gamma, float tau,
+                      fp_index_out *outs, void *ws, size_t ws_bytes, void *stream);
+int fp_attn_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
+                     const int8_t *Q8, const float *sQ, const int8_t *K8,
+                     const float *sK, const int8_t *V8, const float *sV,
+                     const fp_index_out *csrs, void *O,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Test hook for the W8A8 score product: out[c][r] = Q8[h, i*b + r] .
  * K8[h / G, j*b + c] (exact int32) for r, c in [0, b), computed with the same
  * int8 matrix-core tile code that fp_index_i8 and fp_attn_i8 use.

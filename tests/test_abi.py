@@ -22,7 +22,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ("fp_index", "fp_index_i8", "fp_attn", "fp_attn_i8", "fp_build_jobs",
               "fp_workspace_bytes", "fp_csr_capacity", "fp_job_capacity", "fp_strerror",
-              "fp_version", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch"):
+              "fp_version", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch",
+              "fp_index_i8_batch", "fp_attn_i8_batch"):
         assert n in names
 
 
@@ -150,3 +151,9 @@ def test_batch_rejects_bad_arguments():
     assert L.fp_attn_batch(ctypes.byref(sh), 3, arr, P, P, None, outs, P, P, big, None) == fpa.FP_EINVAL
     bad = fpa.shape_of(2048, 128, 4, 2, 64)
     assert L.fp_attn_batch(ctypes.byref(bad), 3, arr, P, P, P, outs, P, P, big, None) == fpa.FP_EUNSUPPORTED
+    # W8A8 forms: the same checks, and the per-token scales are required
+    assert L.fp_index_i8_batch(ctypes.byref(sh), 3, arr, P, None, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
+    assert L.fp_index_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, 0.9, 0.1, outs, P, 64, None) == fpa.FP_EWORKSPACE
+    assert L.fp_index_i8_batch(ctypes.byref(sh), 3, ragged, P, P, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
+    assert L.fp_attn_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, P, None, outs, P, P, big, None) == fpa.FP_EINVAL
+    assert L.fp_attn_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, P, P, outs, P, P, need - 1, None) == fpa.FP_EWORKSPACE

@@ -257,6 +257,35 @@ def test_ragged_batch():
         assert mx <= MAXABS and rms <= RMS
 
 
+def test_ragged_batch_i8():
+    """fp_index_i8_batch / fp_attn_i8_batch on three W8A8 sequences of different lengths packed
+    one after another (int8 tensors and fp32 scales alike): index and attention per sequence
+    against the oracle."""
+    say("ragged batch i8: S = 768, 2048, 256 (b = 128, Hq = 6, Hkv = 2)")
+    lens = [768, 2048, 256]
+    cs = [cfg(S=S, Hq=6, Hkv=2) for S in lens]
+    Ls = [gen.make(c) for c in cs]
+    ts = [P.layer_i8_on_device(L) for L in Ls]
+    pack = lambda name: torch.cat([t[name].reshape(-1) for t in ts])
+    Q8, sQ, K8, sK, V8, sV = (pack(n) for n in ("q8", "sq", "k8", "sk", "v8", "sv"))
+    c0 = cs[0]
+    idxs = fpa.index_i8_batch(Q8, sQ, K8, sK, lens, c0.b, c0.Hq, c0.Hkv, c0.gamma, c0.tau)
+    O = fpa.attn_i8_batch(Q8, sQ, K8, sK, V8, sV, lens, idxs)
+    torch.cuda.synchronize()
+    Os = fpa.unpack(O, lens, c0.Hq)
+    for c, L, idx, Oc in zip(cs, Ls, idxs, Os):
+        assert int(idx.status.item()) == 0
+        d = L.int8()
+        ref = oi.index_i8(d["q8"], d["sq"], d["k8"], d["sk"], c.b, c.gamma, c.tau)
+        P.compare_index(idx, ref, c.gamma, c.tau)
+        P.check_jobs(idx, c.G)
+        rp, ci = P.gpu_rows(idx)
+        Oref = oracle.attn.attn_i8(d["q8"], d["sq"], d["k8"], d["sk"], d["v8"], d["sv"], rp, ci, c.b)
+        mx, rms = P.attn_errors(Oc, Oref)
+        say(f"  S={c.S}: density {idx.density():.3f}, attention maxabs {mx:.2e} rms {rms:.2e}")
+        assert mx <= MAXABS and rms <= RMS
+
+
 TWO_PASS_CASES = [c for c in INDEX_CASES if c[0] in ("tiny", "tiny-G16", "tiny-N70", "tiny-b256-G4", "tiny-b64-G3")]
 
 
