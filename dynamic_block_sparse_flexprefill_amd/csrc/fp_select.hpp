@@ -168,7 +168,7 @@ __device__ __forceinline__ void wave_select_reg(const float *x, int n, float gam
 
 // The register form sized to the row (the cost of a search pass grows with VPL),
 // up to MAXV values per lane; longer rows search in LDS.  MAXV = 32 costs about
-// 36 more registers than 16, so kernels whose occupancy matters take 32 only
+// 20 more registers than 16, so kernels whose occupancy matters take 32 only
 // when their rows can exceed 1024 elements.
 template <int MAXV = 16>
 __device__ __forceinline__ void wave_select(const float *x, int n, float gamma, uint32_t *words) {
