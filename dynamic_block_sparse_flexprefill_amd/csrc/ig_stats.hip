@@ -266,7 +266,9 @@ struct Stat1Args {
 __device__ void grid_barrier(unsigned int *bar, unsigned int nblocks, int32_t *status) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
+    // release before the (relaxed) arrival, acquire after the (relaxed) wait: the two
+    // fences pair up, so neither needs the other half of a full fence
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     atomicAdd(bar, 1u);
     unsigned int spins = 0;
     while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nblocks) {
@@ -276,7 +278,7 @@ __device__ void grid_barrier(unsigned int *bar, unsigned int nblocks, int32_t *s
         break;
       }
     }
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
 }
