@@ -12,13 +12,18 @@ either one shows up as a disagreement in the tests:
   (the stream-and-accumulate form of the explainer's section 3.1), instead of
   materialising the b x S matrix;
 * exhaustive_select: the fewest-items-reaching-a-mass optimum by enumerating
-  every subset (tiny n only).
+  every subset (tiny n only);
+* qa_rows_dense: query-aware rows from the whole N x N matrix of pooled
+  logits (pooling as a matrix product, causal block mask, row softmax through
+  scipy's log-sum-exp, exhaustive subset search per row), instead of one row
+  at a time with greedy selection.
 """
 from __future__ import annotations
 
 import itertools
 
 import numpy as np
+import scipy.special
 
 
 def as64(x) -> np.ndarray:
@@ -109,3 +114,36 @@ def exhaustive_select(x, gamma: float):
             opt = [c for c, ms in masses.items() if ms == best]
             return kk, best, opt
     return n, T, [tuple(range(n))]
+
+
+def pooling_matrix(S: int, b: int) -> np.ndarray:
+    """[N, S] matrix whose row i averages tokens i*b .. i*b + b - 1."""
+    return np.kron(np.eye(S // b), np.full((1, b), 1.0 / b))
+
+
+def qa_rows_dense(q, k, b: int, gamma: float):
+    """Query-aware rows of one head by brute force.
+
+    q: [S, d] queries of the head, k: [S, d] keys of its KV head.  The pooled
+    logits of every (query block i, key block j) pair form one N x N matrix
+    scaled by 1/sqrt(d); key blocks after the query block are masked out,
+    each row is normalised with log-sum-exp, and each row's selection is the
+    exhaustive optimum (fewest blocks reaching gamma of the row's mass, most
+    mass among those).  Returns one (p_i, optimal sets, k_min) per row, where
+    every optimal set already contains block 0 and the diagonal block i.
+    """
+    q, k = as64(q), as64(k)
+    S, d = q.shape
+    P = pooling_matrix(S, b)
+    logits = (P @ q) @ (P @ k).T / np.sqrt(d)
+    N = logits.shape[0]
+    causal = np.tril(np.ones((N, N), dtype=bool))
+    masked = np.where(causal, logits, -np.inf)
+    logp = masked - scipy.special.logsumexp(masked, axis=1, keepdims=True)
+    out = []
+    for i in range(N):
+        p_i = np.exp(logp[i, : i + 1])
+        kmin, _, opt = exhaustive_select(p_i, gamma)
+        sets = sorted({tuple(sorted(set(o) | {0, i})) for o in opt})
+        out.append((p_i, sets, kmin))
+    return out

@@ -218,6 +218,60 @@ def test_rows_structure_and_planted_labels():
     assert rp[0] == 0 and rp[-1] == ci.size and np.all(np.diff(rp) >= 1)
 
 
+def _qa_hand_layer():
+    ex = json.load(open(os.path.join(GOLD, "qa_rows_hand.json")))
+    S, b, d = ex["S"], ex["b"], ex["d"]
+    N = S // b
+    a, c = np.array(ex["a"], float), np.array(ex["c"], float)
+    kbar = np.zeros((N, d))
+    kbar[:, 0], kbar[:, 1] = 2 * np.log(a), 2 * np.log(c)
+    dk, dq = np.array(ex["k_delta"]), np.array(ex["q_eps"])
+    qbar = np.array(ex["qbar"], float)
+    K = np.zeros((1, S, d))
+    Q = np.zeros((1, S, d))
+    for j in range(N):
+        K[0, 2 * j], K[0, 2 * j + 1] = kbar[j] + dk, kbar[j] - dk
+        Q[0, 2 * j], Q[0, 2 * j + 1] = qbar[j] + dq, qbar[j] - dq
+    return ex, Q, K
+
+
+def test_qa_rows_hand_example():
+    """Query-aware rows and the pooled estimate against exact fractions (d = 4, so sigma = 1/2)."""
+    ex, Q, K = _qa_hand_layer()
+    res = oi.index(Q, K, ex["b"], ex["gamma"], 0.1, force_pattern={0: oi.QA})
+    hd = res.heads[0]
+    for want, row, p in zip(ex["rows"], hd.rows, hd.qa_p):
+        w = np.array(want["weights"], float)
+        np.testing.assert_allclose(p, w / want["den"], rtol=1e-13, atol=0)
+        assert list(row) == want["row"], want["i"]
+    pe = np.array(ex["p_est"]["weights"], float) / ex["p_est"]["den"]
+    np.testing.assert_allclose(hd.p, pe, rtol=1e-13, atol=0)
+    # the vertical mass through index() uses the same sigma as the independent streamed form
+    v2, sl2, _, _ = brute.streamed_stats(Q[0, -ex["b"]:], K[0], ex["b"])
+    np.testing.assert_allclose(hd.v, v2, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(hd.sl, sl2, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("gamma", [0.5, 0.8, 0.9, 0.97])
+def test_qa_rows_match_brute_force(seed, gamma):
+    """qa_row (greedy, one row at a time) against the dense pooled-logit matrix with exhaustive selection."""
+    rng = np.random.default_rng(100 + seed)
+    b, d = (2, 4, 8)[seed % 3], (4, 8, 16)[seed % 3]
+    N = 3 + seed % 8
+    S = N * b
+    scale = 1.0 + seed % 4
+    Q = rng.standard_normal((1, S, d)) * scale
+    K = rng.standard_normal((1, S, d)) * scale
+    res = oi.index(Q, K, b, gamma, 0.1, force_pattern={0: oi.QA})
+    ref = brute.qa_rows_dense(Q[0], K[0], b, gamma)
+    for i, (row, p, sel) in enumerate(zip(res.heads[0].rows, res.heads[0].qa_p, res.heads[0].qa_sel)):
+        p_ref, sets, kmin = ref[i]
+        np.testing.assert_allclose(p, p_ref, rtol=1e-11, atol=1e-15)
+        assert sel.k == kmin, (i, sel.k, kmin)
+        assert tuple(row) in sets, (i, list(row), sets)
+
+
 def test_single_block_sequence():
     rng = np.random.default_rng(2)
     Q, K, V = rand_layer(rng, 128, 128, 2, 1, 16)
