@@ -30,6 +30,8 @@ FP_STATUS_JOB_OVERFLOW = 2
 FP_STATUS_WAIT_TIMEOUT = 4
 VERTICAL_SLASH = 0
 QUERY_AWARE = 1
+PROBE_ATTN = 0
+PROBE_STATS = 1
 
 
 class FpShape(ctypes.Structure):
@@ -77,7 +79,8 @@ def lib() -> ctypes.CDLL:
         L.fp_build_jobs.argtypes = [sp, op, _P, ctypes.c_size_t, _P]
         L.fp_attn.argtypes = [sp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
         L.fp_attn_i8.argtypes = [sp, _P, _P, _P, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
-        L.fp_probe_qk_i8.argtypes = [sp, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]
+        L.fp_probe_qk_i8.argtypes = [sp, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]
+        L.fp_index_two_pass.argtypes = [sp, ctypes.c_int, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         lp = ctypes.POINTER(ctypes.c_int32)
         L.fp_index_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_attn_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
@@ -85,7 +88,7 @@ def lib() -> ctypes.CDLL:
         L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
                                        ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch",
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_batch", "fp_attn_batch",
                      "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -230,6 +233,31 @@ def index_i8(Q8, sQ, K8, sK, b: int, gamma: float, tau: float, *, stats: bool = 
                            ctypes.byref(o), _ptr(ws.buf), ws.nbytes, _stream(stream))
     if rc:
         raise FpError(rc, "fp_index_i8")
+    return out
+
+
+def index_two_pass(Q, K, b: int, gamma: float, tau: float, *, sQ=None, sK=None, stats: bool = False,
+                   out: Optional[Index] = None, ws: Optional[Workspace] = None, stream=None) -> Index:
+    """fp_index_two_pass: fp_index (bf16 Q, K) or fp_index_i8 (int8 Q, K with scales sQ, sK) with the
+    last-block statistics forced onto their two-pass form (a test entry point)."""
+    Hq, S, d = Q.shape
+    Hkv = K.shape[0]
+    shape = shape_of(S, b, Hq, Hkv, d)
+    i8 = Q.dtype == torch.int8
+    dt = torch.int8 if i8 else torch.bfloat16
+    _check(Q, "Q", dt, (Hq, S, d))
+    _check(K, "K", dt, (Hkv, S, d))
+    if i8:
+        _check(sQ, "sQ", torch.float32, (Hq, S))
+        _check(sK, "sK", torch.float32, (Hkv, S))
+    out = Index.empty(shape, Q.device, stats=stats) if out is None else out
+    ws = _ws(shape, ws, Q.device)
+    o = out.c_struct()
+    rc = lib().fp_index_two_pass(ctypes.byref(shape), 1 if i8 else 0, _ptr(Q), _ptr(sQ) if i8 else None, _ptr(K),
+                                 _ptr(sK) if i8 else None, gamma, tau, ctypes.byref(o), _ptr(ws.buf), ws.nbytes,
+                                 _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_index_two_pass")
     return out
 
 
@@ -398,14 +426,15 @@ def attn_i8_batch(Q8, sQ, K8, sK, V8, sV, seqlens, idxs: list, *, out: Optional[
     return O
 
 
-def probe_qk_i8(Q8, K8, b: int, h: int, i: int, j: int, stream=None) -> torch.Tensor:
-    """fp_probe_qk_i8: exact int32 tile out[c, r] = Q8[h, i*b+r] . K8[h/G, j*b+c]."""
+def probe_qk_i8(Q8, K8, b: int, h: int, i: int, j: int, path: int = PROBE_ATTN, stream=None) -> torch.Tensor:
+    """fp_probe_qk_i8: exact int32 tile out[c, r] = Q8[h, i*b+r] . K8[h/G, j*b+c] through the staging
+    and tile code of the attention kernel (PROBE_ATTN) or the statistics kernel (PROBE_STATS)."""
     Hq, S, d = Q8.shape
     shape = shape_of(S, b, Hq, K8.shape[0], d)
     _check(Q8, "Q8", torch.int8, (Hq, S, d))
     _check(K8, "K8", torch.int8, (K8.shape[0], S, d))
     out = torch.empty(b, b, dtype=torch.int32, device=Q8.device)
-    rc = lib().fp_probe_qk_i8(ctypes.byref(shape), _ptr(Q8), _ptr(K8), h, i, j, _ptr(out), _stream(stream))
+    rc = lib().fp_probe_qk_i8(ctypes.byref(shape), _ptr(Q8), _ptr(K8), h, i, j, path, _ptr(out), _stream(stream))
     if rc:
         raise FpError(rc, "fp_probe_qk_i8")
     return out

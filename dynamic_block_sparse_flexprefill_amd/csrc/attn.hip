@@ -682,29 +682,58 @@ __global__ void k_attn_prep(const int32_t *job_order, const int32_t *job_ptr, in
   utab[u] = int4{job, p0, n, rot};
 }
 
-// out[c * B + r] = Q8[h, i*B + r] . K8[g, j*B + c] through the int8 tile code.
-template <int B>
-__global__ void __launch_bounds__(2 * B) k_probe_qk_i8(const uint8_t *Q, const uint8_t *K, int S,
-                                                       int h, int g, int i, int j, int32_t *out) {
-  __shared__ __attribute__((aligned(16))) uint8_t ks[B * KL<true>::Stride];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint8_t *kb = K + ((size_t)g * S + (size_t)j * B) * 128;
-  for (int c = threadIdx.x; c < B * 8; c += blockDim.x) {
-    const int r = c / 8, col = c % 8;
-    *(u32x4 *)(ks + r * KL<true>::Stride + col * 16) = *(const u32x4 *)(kb + (size_t)r * 128 + col * 16);
-  }
-  __syncthreads();
-  const int qr = wave * 32 + (lane & 31);
-  u32x4 qf[8];
-  load_q<true>(Q, (size_t)h * S + (size_t)i * B + qr, qf);
-  for (int kt = 0; kt < B / 32; ++kt) {
-    float x[16];
-    raw_scores<true>(ks, kt * 32, qf, x);
+// Test hook: out[c * B + r] = Q8[h, i*B + r] . K8[g, j*B + c] through the W8A8 attention kernel's
+// own staging (direct-to-LDS loads of dl_issue8, or dl_issue8_2 for 64-key blocks, with K rows in
+// the swap23 order) and its int8 tile code, at the workgroup size the kernel runs with for this
+// shape; the accumulator rows are mapped back to keys as the kernel's masking does.  The V and
+// scale slots of the loads read bytes of the same key block (in bounds, never used).
+template <int NT>
+__global__ void __launch_bounds__(NT) k_probe_attn_i8(const uint8_t *Q, const uint8_t *K, int S, int B, int h,
+                                                      int g, int i, int j, int32_t *out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kbuf[dl::KBuf8];
+  __shared__ __attribute__((aligned(1024))) uint8_t vstage[kChunkDl * 128];
+  __shared__ __attribute__((aligned(16))) float sbuf[2 * kChunkDl];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  constexpr int NW = NT / 64;
+  const int nchunk = B >= kChunkDl ? B / kChunkDl : 1;
+  for (int kc = 0; kc < nchunk; ++kc) {
+    __syncthreads();                                          // the previous chunk's reads are done
+    const uint8_t *kg = K + ((size_t)g * S + (size_t)j * B + kc * kChunkDl) * 128;
+    const float *junk = (const float *)kg;
+    if (B >= kChunkDl)
+      dl_issue8(kg, kg, junk, junk, lds_addr(kbuf), lds_addr(vstage), lds_addr(sbuf), wave, NW);
+    else   // 64-key blocks: both halves of the chunk carry block j
+      dl_issue8_2(kg, kg, junk, junk, kg, kg, junk, junk, lds_addr(kbuf), lds_addr(vstage), lds_addr(sbuf),
+                  wave, NW);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __syncthreads();
+    const int keys = B >= kChunkDl ? kChunkDl : B;            // keys of block j in this chunk
+    for (int qt = wave; qt < B / 32; qt += NW) {
+      const int qr = qt * 32 + (lane & 31);
+      u32x4 qf[8];
+      load_q<true>(Q, (size_t)h * S + (size_t)i * B + qr, qf);
+      for (int kb = 0; kb < keys; kb += 32) {
+        float x[16];
+        raw_scores<true>(kbuf, kb, qf, x);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) out[(size_t)(kt * 32 + acc_row(r, lane)) * B + qr] = (int32_t)x[r];
+        for (int r = 0; r < 16; ++r) {
+          const int key = kc * kChunkDl + kb + swap23(acc_row(r, lane));
+          out[(size_t)key * B + qr] = (int32_t)x[r];
+        }
+      }
+    }
   }
 }
 
+// Query tiles per attention workgroup: the largest divisor of b/32 keeping G * qpw <= 12 waves.
+static int attn_qpw(const Plan &p) {
+  const int qtiles = p.B / 32;
+  int qpw = 1;
+  for (int d = 1; d <= qtiles; d <<= 1)
+    if (qtiles % d == 0 && p.G * d <= 12) qpw = d;
+  return qpw;
+}
 
 template <int NT, bool I8, bool PAIR>
 hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
@@ -744,29 +773,24 @@ hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, c
   a.c2 = kLog2e / sqrtf((float)p.d);
   // query tiles per workgroup: the largest divisor of b/32 keeping G * qpw <= 12 waves; the
   // workgroup size is the next supported one (256, 512, 768 or 1024 threads), spare waves idle
-  const int qtiles = p.B / 32;
-  int qpw = 1;
-  for (int d = 1; d <= qtiles; d <<= 1)
-    if (qtiles % d == 0 && p.G * d <= 12) qpw = d;
+  const int qpw = attn_qpw(p);
   a.qpw = qpw;
-  a.parts = qtiles / qpw;
+  a.parts = p.B / 32 / qpw;
   if (p.B == 64)   // two 64-key blocks per 128-key chunk
     return i8 ? dispatch_attn<true, true>(p, a, ctr, utab, st) : dispatch_attn<false, true>(p, a, ctr, utab, st);
   return i8 ? dispatch_attn<true, false>(p, a, ctr, utab, st) : dispatch_attn<false, false>(p, a, ctr, utab, st);
 }
 
-hipError_t launch_probe_qk_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
-                              int j, int32_t *out, hipStream_t st) {
+hipError_t launch_probe_attn_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i, int j,
+                                int32_t *out, hipStream_t st) {
+  // the workgroup size dispatch_attn picks for this shape
+  const int need = 64 * p.G * attn_qpw(p);
+  const uint8_t *q = (const uint8_t *)Q8, *k = (const uint8_t *)K8;
   const int g = h / p.G;
-  if (p.B == 64)
-    hipLaunchKernelGGL(k_probe_qk_i8<64>, dim3(1), dim3(128), 0, st, (const uint8_t *)Q8,
-                       (const uint8_t *)K8, p.S, h, g, i, j, out);
-  else if (p.B == 128)
-    hipLaunchKernelGGL(k_probe_qk_i8<128>, dim3(1), dim3(256), 0, st, (const uint8_t *)Q8,
-                       (const uint8_t *)K8, p.S, h, g, i, j, out);
-  else
-    hipLaunchKernelGGL(k_probe_qk_i8<256>, dim3(1), dim3(512), 0, st, (const uint8_t *)Q8,
-                       (const uint8_t *)K8, p.S, h, g, i, j, out);
+  if (need <= 256) hipLaunchKernelGGL(k_probe_attn_i8<256>, dim3(1), dim3(256), 0, st, q, k, p.S, p.B, h, g, i, j, out);
+  else if (need <= 512) hipLaunchKernelGGL(k_probe_attn_i8<512>, dim3(1), dim3(512), 0, st, q, k, p.S, p.B, h, g, i, j, out);
+  else if (need <= 768) hipLaunchKernelGGL(k_probe_attn_i8<768>, dim3(1), dim3(768), 0, st, q, k, p.S, p.B, h, g, i, j, out);
+  else hipLaunchKernelGGL(k_probe_attn_i8<1024>, dim3(1), dim3(1024), 0, st, q, k, p.S, p.B, h, g, i, j, out);
   return hipGetLastError();
 }
 

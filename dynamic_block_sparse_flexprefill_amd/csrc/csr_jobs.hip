@@ -294,8 +294,8 @@ __device__ void sort_group(const int32_t *jwork, int N, int g, unsigned long lon
 }
 
 // One launch for both steps that follow the count pass: workgroups 0 .. nscan-1
-// scan the job (and row) counts; the next Hkv workgroups, when `sorted` is
-// set, each sort one KV group's job keys (the sort needs only the job work).
+// scan the job (and row) counts; the next Hkv workgroups each sort one KV
+// group's job keys (the sort needs only the job work).
 static_assert(kScanThreads == kSortThreads, "the scans and sorts share one launch");
 __global__ void __launch_bounds__(kScanThreads) k_scan_sort(ScanJob s0, ScanJob s1, int nscan, int32_t *status,
                                                             const int32_t *jwork, int N,
@@ -335,13 +335,6 @@ __global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, in
   order[rank] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
 }
 
-// Fallback for N too large to sort a group in LDS: latest query blocks first.
-__global__ void k_order_fallback(int N, int Hkv, int32_t *order) {
-  const int k = blockIdx.x * blockDim.x + threadIdx.x;
-  if (k >= Hkv * N) return;
-  order[k] = (k % Hkv) * N + (N - 1 - k / Hkv);
-}
-
 template <int GM, bool WRITE>
 hipError_t run_jobs(const Plan &p, const JobArgs &a, hipStream_t st, bool rows) {
   const dim3 grid((p.Hkv * p.N + kJobWaves - 1) / kJobWaves), block(64 * kJobWaves);
@@ -370,13 +363,14 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   const ScanJob sj{io->job_ptr, jobs, io->job_cap, (uint32_t)FP_STATUS_JOB_OVERFLOW};
   const ScanJob sr{io->row_ptr, rcount, io->col_cap, (uint32_t)FP_STATUS_CSR_OVERFLOW};
   const int nscan = rows ? 2 : 1;
-  const bool sort = p.N <= kSortMax;
+  // every supported N (at most 8192, checked by make_plan) sorts a group in LDS
+  static_assert(kSortMax >= 8192, "a KV group's job keys fit in LDS for every supported N");
   int P = 1;
   while (P < p.N) P <<= 1;
-  const size_t slds = sort ? sizeof(unsigned long long) * P : 0;
+  const size_t slds = sizeof(unsigned long long) * P;
   e = hipFuncSetAttribute((const void *)k_scan_sort, hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_scan_sort, dim3(nscan + (sort ? p.Hkv : 0)), dim3(kScanThreads), slds, st, sj, sr, nscan,
+  hipLaunchKernelGGL(k_scan_sort, dim3(nscan + p.Hkv), dim3(kScanThreads), slds, st, sj, sr, nscan,
                      io->status, w.jwork, p.N, w.jkeys);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.G <= 1) e = run_jobs<1, true>(p, a, st, rows);
@@ -385,10 +379,6 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   else if (p.G <= 8) e = run_jobs<8, true>(p, a, st, rows);
   else e = run_jobs<kMaxG, true>(p, a, st, rows);
   if (e != hipSuccess) return e;
-  if (!sort) {
-    hipLaunchKernelGGL(k_order_fallback, dim3((jobs + 255) / 256), dim3(256), 0, st, p.N, p.Hkv, io->job_order);
-    return hipGetLastError();
-  }
   if (jobs <= kRankLdsKeys) {
     const size_t lds = sizeof(unsigned long long) * jobs;
     e = hipFuncSetAttribute((const void *)k_rank_jobs<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -133,7 +133,8 @@ int64_t fp_job_capacity(const fp_shape *shape) {
 
 static int index_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
                         const void *K, const float *sK, float gamma, float tau,
-                        fp_index_out *out, void *ws, size_t ws_bytes, void *stream) {
+                        fp_index_out *out, void *ws, size_t ws_bytes, void *stream,
+                        bool two_pass = false) {
   Plan p;
   int rc = make_plan(shape, &p);
   if (rc) return rc;
@@ -145,7 +146,7 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   Work w = carve(p, ws);
   FP_LAUNCH(launch_status_init(out->status, w.bar, st));
   bool have_pe = false;
-  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st, &have_pe));
+  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st, two_pass, &have_pe));
   FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, have_pe));
   FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st));
   FP_LAUNCH(launch_rows_and_jobs(p, out, w, st));
@@ -162,6 +163,13 @@ int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ, const 
                 const float *sK, float gamma, float tau, fp_index_out *out, void *ws,
                 size_t ws_bytes, void *stream) {
   return index_common(shape, true, Q8, sQ, K8, sK, gamma, tau, out, ws, ws_bytes, stream);
+}
+
+int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const float *sQ,
+                      const void *K, const float *sK, float gamma, float tau, fp_index_out *out,
+                      void *ws, size_t ws_bytes, void *stream) {
+  if (variant != 0 && variant != 1) return FP_EINVAL;
+  return index_common(shape, variant == 1, Q, sQ, K, sK, gamma, tau, out, ws, ws_bytes, stream, true);
 }
 
 int fp_build_jobs(const fp_shape *shape, fp_index_out *io, void *ws, size_t ws_bytes,
@@ -308,13 +316,15 @@ int fp_attn_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens, co
 }
 
 int fp_probe_qk_i8(const fp_shape *shape, const int8_t *Q8, const int8_t *K8, int h, int i,
-                   int j, int32_t *out, void *stream) {
+                   int j, int path, int32_t *out, void *stream) {
   Plan p;
   int rc = make_plan(shape, &p);
   if (rc) return rc;
   if (!Q8 || !K8 || !out) return FP_EINVAL;
   if (h < 0 || h >= p.Hq || i < 0 || i >= p.N || j < 0 || j >= p.N) return FP_EINVAL;
-  FP_LAUNCH(launch_probe_qk_i8(p, Q8, K8, h, i, j, out, (hipStream_t)stream));
+  if (path != FP_PROBE_ATTN && path != FP_PROBE_STATS) return FP_EINVAL;
+  if (path == FP_PROBE_ATTN) FP_LAUNCH(launch_probe_attn_i8(p, Q8, K8, h, i, j, out, (hipStream_t)stream));
+  else FP_LAUNCH(launch_probe_stats_i8(p, Q8, K8, h, i, j, out, (hipStream_t)stream));
   return FP_OK;
 }
 

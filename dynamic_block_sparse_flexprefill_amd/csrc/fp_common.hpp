@@ -61,7 +61,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
-// 2^x on the transcendental unit (no denormal fix-up; inputs here are <= 8).
+// 2^x on the transcendental unit, without a denormal fix-up (results below 2^-126 flush
+// to zero).  Inputs here are at most the rescale headroom: 16 in the statistics, 24 in
+// the attention.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---------------------------------------------------------------- reductions

@@ -54,10 +54,11 @@ Work carve(const Plan &p, void *ws);
 // ---- launchers: each returns hipSuccess or the launch error.
 // Statistics of the last query block against every key block
 // (two passes over K: row max / sum, then block mass).
+// two_pass: use the two-pass form even where the single pass fits (test entry point).
 // *have_pe: whether the statistics also wrote the pooled-estimate logits (w.pe).
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ,
                            const void *K, const float *sK, const Work &w, int32_t *status,
-                           hipStream_t st, bool *have_pe);
+                           hipStream_t st, bool two_pass, bool *have_pe);
 // Per head: pooled estimate, divergence, pattern, vertical / slash selection.
 // have_pe: the pooled-estimate logits are in w.pe (else they are computed here).
 hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,
@@ -79,8 +80,11 @@ int cu_count();
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,
                        void *O, unsigned int *ctr, int4 *utab, hipStream_t st);
-// One int8 score tile through the attention / statistics tile code.
-hipError_t launch_probe_qk_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
-                              int j, int32_t *out, hipStream_t st);
+// One exact int8 score tile through the W8A8 attention kernel's staging and tile code.
+hipError_t launch_probe_attn_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
+                                int j, int32_t *out, hipStream_t st);
+// The same through the single-pass statistics kernel's staging and tile code.
+hipError_t launch_probe_stats_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
+                                 int j, int32_t *out, hipStream_t st);
 
 }  // namespace fp

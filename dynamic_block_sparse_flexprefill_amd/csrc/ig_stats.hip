@@ -29,8 +29,6 @@
 // TPW tiles of 32 last-block query rows and keeps their Q fragments in
 // registers; scores are computed transposed (keys x queries) on the 32x32x16
 // bf16 (or 32x32x32 int8) matrix cores so that every lane holds one query row.
-#include <cstdlib>
-
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 
@@ -75,22 +73,31 @@ __device__ __forceinline__ void stage_k(const StatArgs &a, int g, int j, uint8_t
   }
 }
 
+// Exact int32 scores of one 32-key tile (kt) of the staged int8 block against one 32-query
+// tile: acc[r] <-> key kt*32 + acc_row(r, lane), query lane % 32.
+__device__ __forceinline__ i32x16 tile_raw_i8(const uint8_t *ks, const u32x4 *qf, int kt) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t *arow = ks + (kt * 32 + (lane & 31)) * Tile<true>::Stride + 16 * (lane >> 5);
+  i32x16 acc = {};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma_i8(*(const u32x4 *)(arow + 32 * s), qf[s], acc);
+  return acc;
+}
+
 // Scores of one 32-key tile (kt) against one 32-query tile: x[r] in log2 units.
 template <bool I8>
 __device__ __forceinline__ void tile_scores(const uint8_t *ks, const float *sk, const u32x4 *qf,
                                             float qscale, int kt, float c2, float x[16]) {
   const int lane = threadIdx.x & 63;
-  const uint8_t *arow = ks + (kt * 32 + (lane & 31)) * Tile<I8>::Stride + 16 * (lane >> 5);
   if (!I8) {
+    const uint8_t *arow = ks + (kt * 32 + (lane & 31)) * Tile<I8>::Stride + 16 * (lane >> 5);
     f32x16 acc = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc = mfma_bf16(*(const u32x4 *)(arow + 32 * s), qf[s], acc);
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = acc[r] * c2;
   } else {
-    i32x16 acc = {};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma_i8(*(const u32x4 *)(arow + 32 * s), qf[s], acc);
+    const i32x16 acc = tile_raw_i8(ks, qf, kt);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       x[r] = (float)acc[r] * (c2 * qscale) * sk[kt * 32 + acc_row(r, lane)];
@@ -846,7 +853,67 @@ hipError_t dispatch1(const Plan &p, const StatArgs &a, unsigned int *bar, int32_
   return run1<256, 1024, 4, I8>(p, a, bar, status, st, used);
 }
 
+// Test hook: the int32 tile Q8[h, i*B + r] . K8[g, j*B + c] through the single-pass kernel's own
+// staging (KStage register stage, padded LDS rows) and int8 tile code, at the workgroup size the
+// kernel runs with for this shape; out[c * B + r].  The scale slot of the stage reads bytes of K
+// (in bounds, unused).
+template <int B, int NT>
+__global__ void __launch_bounds__(NT) k_probe_stats_i8(const uint8_t *Q, const uint8_t *K, int S, int h, int g,
+                                                       int i, int j, int32_t *out) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks[B * Tile<true>::Stride];
+  __shared__ float sk[B];
+  StatArgs a{};
+  a.Q = Q;
+  a.K = K;
+  a.sK = (const float *)K;
+  a.S = S;
+  KStage<B, NT, true> stg;
+  stg.load(a, g, j);
+  stg.store(ks, sk);
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave >= B / 32) return;
+  const int qr = wave * 32 + (lane & 31);
+  const uint8_t *qp = Q + ((size_t)h * S + (size_t)i * B + qr) * Tile<true>::RowBytes + 16 * (lane >> 5);
+  u32x4 qf[Tile<true>::KS];
+#pragma unroll
+  for (int s = 0; s < Tile<true>::KS; ++s) qf[s] = *(const u32x4 *)(qp + 32 * s);
+  for (int kt = 0; kt < B / 32; ++kt) {
+    const i32x16 acc = tile_raw_i8(ks, qf, kt);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[(size_t)(kt * 32 + acc_row(r, lane)) * B + qr] = acc[r];
+  }
+}
+
+template <int B, int NT>
+hipError_t probe1(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i, int j, int32_t *out,
+                  hipStream_t st) {
+  hipLaunchKernelGGL((k_probe_stats_i8<B, NT>), dim3(1), dim3(NT), 0, st, (const uint8_t *)Q8,
+                     (const uint8_t *)K8, p.S, h, h / p.G, i, j, out);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// The workgroup size follows dispatch1 (tiles = G * b / 32).
+hipError_t launch_probe_stats_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i, int j,
+                                 int32_t *out, hipStream_t st) {
+  const int tiles = p.G * p.B / 32;
+  if (p.B == 64) {
+    if (tiles <= 4) return probe1<64, 256>(p, Q8, K8, h, i, j, out, st);
+    if (tiles <= 8) return probe1<64, 512>(p, Q8, K8, h, i, j, out, st);
+    if (tiles <= 12) return probe1<64, 768>(p, Q8, K8, h, i, j, out, st);
+    return probe1<64, 1024>(p, Q8, K8, h, i, j, out, st);
+  }
+  if (p.B == 128) {
+    if (tiles <= 4) return probe1<128, 256>(p, Q8, K8, h, i, j, out, st);
+    if (tiles <= 8) return probe1<128, 512>(p, Q8, K8, h, i, j, out, st);
+    if (tiles <= 12) return probe1<128, 768>(p, Q8, K8, h, i, j, out, st);
+    return probe1<128, 1024>(p, Q8, K8, h, i, j, out, st);
+  }
+  if (tiles <= 8) return probe1<256, 512>(p, Q8, K8, h, i, j, out, st);
+  return probe1<256, 1024>(p, Q8, K8, h, i, j, out, st);
+}
 
 int cu_count() {
   static int cache[64] = {0};
@@ -862,7 +929,7 @@ int cu_count() {
 
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                            const float *sK, const Work &w, int32_t *status, hipStream_t st,
-                           bool *have_pe) {
+                           bool two_pass, bool *have_pe) {
   StatArgs a;
   a.Q = (const uint8_t *)Q;
   a.sQ = sQ;
@@ -875,10 +942,9 @@ hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *s
   a.sigma = 1.0f / sqrtf((float)p.d);
   *have_pe = false;
   bool used = false;
-  // FPATTN_STATS_TWO_PASS=1 (read on every call) selects the two-pass form for any shape, so
-  // that tests can check it at sizes whose single-pass partials would fit in LDS
-  const char *force = getenv("FPATTN_STATS_TWO_PASS");
-  if (!(force && force[0] == '1')) {
+  // two_pass (the test entry point fp_index_two_pass) selects the two-pass form for any shape, so
+  // that it can be checked at sizes whose single-pass partials would fit in LDS
+  if (!two_pass) {
     hipError_t e = i8 ? dispatch1<true>(p, a, w.bar, status, st, &used)
                       : dispatch1<false>(p, a, w.bar, status, st, &used);
     *have_pe = used;

@@ -45,7 +45,13 @@
  *    capacity exceeded) cannot be known on the host: the kernels set bits in
  *    the device status word (fp_index_out.status) and stop writing past the
  *    capacity; read it after the stream synchronises.
- *  - Identical inputs give bit-identical outputs (no floating-point atomics).
+ *  - Identical inputs on the same device configuration give bit-identical
+ *    outputs (no floating-point atomics).  The statistics of fp_index split
+ *    the key blocks into one chunk per compute unit and KV group, and use the
+ *    single-pass form only where its partials fit in LDS at one workgroup per
+ *    compute unit; both follow the device's CU count, so results from devices
+ *    with different CU counts can differ in the last bits of v, sl and p (and,
+ *    where that moves a selection boundary, in the index sets).
  *  - Supported shapes: d = 128; b in {64, 128, 256}; S a positive multiple
  *    of b with S / b <= 8192; Hq a multiple of Hkv; G <= 16 and G * b <= 2048
  *    where G = Hq / Hkv; gamma in (0, 1]; tau >= 0.
@@ -62,7 +68,7 @@ extern "C" {
 
 #define FP_OK            0
 #define FP_EINVAL       (-1) /* null pointer, S % b != 0, Hq % Hkv != 0, gamma not in (0,1], tau < 0 or NaN */
-#define FP_EUNSUPPORTED (-2) /* d != 128, b not in {128,256}, N > 8192, G*b > 2048 */
+#define FP_EUNSUPPORTED (-2) /* d != 128, b not in {64,128,256}, N > 8192, G > 16, G*b > 2048 */
 #define FP_EWORKSPACE   (-3) /* workspace smaller than fp_workspace_bytes() */
 #define FP_ECAPACITY    (-4) /* (device status bit 1) CSR capacity exceeded */
 #define FP_EHIP         (-5) /* a HIP launch or query failed */
@@ -158,10 +164,6 @@ int64_t fp_job_capacity(const fp_shape *shape);
  * K is read from HBM once, in increasing block order; nothing of size
  * Hq x S is written to memory.  Errors: FP_EINVAL, FP_EUNSUPPORTED,
  * FP_EWORKSPACE, FP_EHIP; capacity overflow through out->status.
- * The environment variable FPATTN_STATS_TWO_PASS=1 (read on every call, for
- * tests) makes the statistics stream K twice instead of holding per-row
- * partials on chip -- the form otherwise used only when those do not fit;
- * results agree to rounding.
  */
 int fp_index(const fp_shape *shape, const void *Q, const void *K,
              float gamma, float tau, fp_index_out *out,
@@ -178,6 +180,20 @@ int fp_index(const fp_shape *shape, const void *Q, const void *K,
 int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
                 const int8_t *K8, const float *sK, float gamma, float tau,
                 fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Test entry point: fp_index (variant 0; sQ, sK ignored) or fp_index_i8
+ * (variant 1) with the last-block statistics forced onto their two-pass form,
+ * which streams K twice (row maxima and sums first, block mass second)
+ * instead of keeping per-row partials on chip until a grid-wide barrier.
+ * fp_index uses that form by itself only where the partials do not fit in
+ * LDS; this call lets tests check it at any size.  The results equal
+ * fp_index's up to floating-point rounding order.  Arguments, errors and
+ * outputs as fp_index / fp_index_i8; FP_EINVAL for another variant.
+ */
+int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const float *sQ,
+                      const void *K, const float *sK, float gamma, float tau,
+                      fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * Rebuild the grouped-query job list (job_ptr, job_blk, job_mask, job_order)
@@ -257,13 +273,23 @@ int fp_attn_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
                      void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Test hook for the W8A8 score product: out[c][r] = Q8[h, i*b + r] .
- * K8[h / G, j*b + c] (exact int32) for r, c in [0, b), computed with the same
- * int8 matrix-core tile code that fp_index_i8 and fp_attn_i8 use.
+ * Test hook for the W8A8 score product ([E] 3.3: INT8 x INT8 with INT32
+ * accumulation): out[c][r] = Q8[h, i*b + r] . K8[h / G, j*b + c] (exact
+ * int32) for r, c in [0, b), computed through the staging and int8
+ * matrix-core tile code of one of the two kernels that use it, at the
+ * workgroup size that kernel runs with for this shape:
+ *   path FP_PROBE_ATTN:  fp_attn_i8's kernel (direct-to-LDS loads, key rows
+ *                        in its permuted LDS order, mapped back to keys);
+ *   path FP_PROBE_STATS: fp_index_i8's single-pass statistics kernel
+ *                        (register-staged block, padded LDS rows).
  *   out: device int32 [b, b] (key-major: out[c * b + r]).
+ * Errors: FP_EINVAL (null pointer, h, i or j out of range, unknown path),
+ * FP_EUNSUPPORTED, FP_EHIP.
  */
+#define FP_PROBE_ATTN  0
+#define FP_PROBE_STATS 1
 int fp_probe_qk_i8(const fp_shape *shape, const int8_t *Q8, const int8_t *K8,
-                   int h, int i, int j, int32_t *out, void *stream);
+                   int h, int i, int j, int path, int32_t *out, void *stream);
 
 #ifdef __cplusplus
 }

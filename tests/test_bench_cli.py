@@ -71,3 +71,63 @@ def test_index_bytes_small_layer():
     # int8: one byte per element plus the fp32 row scales
     got8 = bench.index_bytes(c, pattern, nnz=3, njob=2, i8=True)
     assert got8 == (k // 2 + 256 * 4) + (qlast // 2 + 2 * 128 * 4) + (qa // 2 + 256 * 4) + kbar + csr
+
+
+def test_attention_flop_counts():
+    """Full count 4 b^2 d per selected block; the causally exact count keeps only the (query, key)
+    pairs with key <= query inside each diagonal block (counted here by enumeration)."""
+    for b, d, Hq, N, nnz in [(4, 2, 1, 1, 1), (8, 4, 2, 3, 9), (128, 128, 24, 1024, 175947)]:
+        c = SimpleNamespace(b=b, d=d, Hq=Hq, N=N)
+        full, exact = bench.attn_flops(c, nnz)
+        assert full == 4 * b * b * d * nnz
+        causal_pairs = sum(1 for q in range(b) for k in range(b) if k <= q)
+        # every pair costs a d-term dot product (2d) and a d-wide weighted sum (2d)
+        diag = Hq * N
+        assert exact == (nnz - diag) * 4 * b * b * d + diag * causal_pairs * 4 * d
+        assert exact < full
+    # the 128K headline: 1.4760e12 in full, 1.3737e12 causally exact
+    full, exact = bench.attn_flops(SimpleNamespace(b=128, d=128, Hq=24, N=1024), 175947)
+    assert round(full / 1e12, 4) == 1.4760 and round(exact / 1e12, 4) == 1.3737
+
+
+def test_w8a8_peak_is_the_time_sum_roofline():
+    """Half the operations on the int8 peak, half on the bf16 peak: time per 4b^2d operations is
+    2b^2d / P_i8 + 2b^2d / P_bf16."""
+    ops = 4.0
+    t = (ops / 2) / bench.PEAK_I8_TOPS + (ops / 2) / bench.PEAK_BF16_TFLOPS
+    assert bench.PEAK_W8A8_TOPS == pytest.approx(ops / t)
+    assert bench.PEAK_W8A8_TOPS == pytest.approx(3333.333, rel=1e-6)
+
+
+def test_full_size_parity_record_on_host_tensors():
+    """bench.compare_full on an index that is the oracle's own (as host tensors): every row equal,
+    and a row changed away from the boundary is counted outside the rule."""
+    import torch
+    import gen
+    import oracle
+    from oracle import index as oi
+    from tests import parity as P
+    c = gen.CONFIGS["tiny"].with_(S=1024)
+    L = gen.make(c)
+    Q, K, V = L.f32("q"), L.f32("k"), L.f32("v")
+    ref = oi.index(Q, K, c.b, c.gamma, c.tau)
+    rp, ci = ref.csr()
+    Oref = oracle.attn.attn(Q, K, V, rp, ci, c.b)
+
+    def fake(rp, ci):
+        return SimpleNamespace(row_ptr=torch.from_numpy(rp), col_idx=torch.from_numpy(ci),
+                               pattern=torch.from_numpy(ref.pattern), jsd=torch.from_numpy(ref.jsd.astype(np.float32)))
+    O = torch.from_numpy(Oref.astype(np.float32)).to(torch.bfloat16)
+    out = bench.compare_full(c, fake(rp, ci), ref, O, Oref, P, oi)
+    assert out["rows_equal"] == c.Hq * c.N and out["rows_outside_rule"] == 0 and out["gate"] == "pass"
+    assert out["attn_maxabs"] <= 2e-2 and out["attn_elements"] == Oref.size
+    # drop a middle block from the last row of head 0 (rows always keep 0 and i)
+    r = c.N - 1
+    row = ci[rp[r]:rp[r + 1]]
+    mid = [j for j in row if 0 < j < r]
+    assert mid
+    keep = np.concatenate([ci[:rp[r]], row[row != mid[0]], ci[rp[r + 1]:]]).astype(np.int32)
+    rp2 = rp.copy()
+    rp2[r + 1:] -= 1
+    out2 = bench.compare_full(c, fake(rp2, keep), ref, O, Oref, P, oi)
+    assert out2["rows_outside_rule"] == 1 and out2["gate"] == "fail"

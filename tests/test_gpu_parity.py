@@ -38,19 +38,26 @@ def cfg(name="tiny", **kw):
 
 
 # ------------------------------------------------------------------ int8 tile
-@pytest.mark.parametrize("b", [64, 128, 256])
-def test_probe_qk_i8_exact(b):
-    say(f"probe_qk_i8 b={b}")
+# (b, Hq, Hkv): the G = 3 shapes run the production workgroup sizes of the headline-like layers
+PROBE_SHAPES = [(64, 4, 2), (64, 6, 2), (128, 4, 2), (128, 6, 2), (256, 4, 2), (256, 6, 2)]
+
+
+@pytest.mark.parametrize("path", [fpa.PROBE_ATTN, fpa.PROBE_STATS], ids=["attn", "stats"])
+@pytest.mark.parametrize("b,Hq,Hkv", PROBE_SHAPES, ids=[f"b{b}-G{hq // hk}" for b, hq, hk in PROBE_SHAPES])
+def test_probe_qk_i8_exact(b, Hq, Hkv, path):
+    """The int32 Q8.K8^T tile through each W8A8 kernel's own staging and tile code equals the
+    exact integer product."""
+    say(f"probe_qk_i8 path={path} b={b} Hq={Hq} Hkv={Hkv}")
     rng = np.random.default_rng(11)
-    S, Hq, Hkv = 4 * b, 4, 2
+    S, G = 4 * b, Hq // Hkv
     q8 = rng.integers(-127, 128, size=(Hq, S, 128), dtype=np.int8)
     k8 = rng.integers(-127, 128, size=(Hkv, S, 128), dtype=np.int8)
     q8[1, b:b + 3] = -127
     k8[0, 2 * b:2 * b + 5] = -127
     Q8, K8 = P.dev(q8), P.dev(k8)
-    for h, i, j in [(0, 0, 0), (1, 1, 2), (3, 3, 1)]:
-        out = fpa.probe_qk_i8(Q8, K8, b, h, i, j).cpu().numpy().astype(np.int64)
-        ref = k8[h // 2, j * b:(j + 1) * b].astype(np.int64) @ q8[h, i * b:(i + 1) * b].astype(np.int64).T
+    for h, i, j in [(0, 0, 0), (1, 1, 2), (Hq - 1, 3, 1), (Hq - 1, 3, 3)]:
+        out = fpa.probe_qk_i8(Q8, K8, b, h, i, j, path=path).cpu().numpy().astype(np.int64)
+        ref = k8[h // G, j * b:(j + 1) * b].astype(np.int64) @ q8[h, i * b:(i + 1) * b].astype(np.int64).T
         np.testing.assert_array_equal(out, ref)
 
 
@@ -163,17 +170,23 @@ LARGE_N_CASES = [
 ]
 
 
-def _index_case(c, gamma, i8=False):
+def _index_case(c, gamma, i8=False, two_pass=False):
     L = gen.make(c)
     if i8:
         d = L.int8()
         ref = oi.index_i8(d["q8"], d["sq"], d["k8"], d["sk"], c.b, gamma, c.tau)
         t = P.layer_i8_on_device(L)
-        idx = fpa.index_i8(t["q8"], t["sq"], t["k8"], t["sk"], c.b, gamma, c.tau, stats=True)
+        if two_pass:
+            idx = fpa.index_two_pass(t["q8"], t["k8"], c.b, gamma, c.tau, sQ=t["sq"], sK=t["sk"], stats=True)
+        else:
+            idx = fpa.index_i8(t["q8"], t["sq"], t["k8"], t["sk"], c.b, gamma, c.tau, stats=True)
     else:
         ref = oi.index(L.f32("q"), L.f32("k"), c.b, gamma, c.tau)
         Qd, Kd, _ = P.layer_on_device(L)
-        idx = fpa.index(Qd, Kd, c.b, gamma, c.tau, stats=True)
+        if two_pass:
+            idx = fpa.index_two_pass(Qd, Kd, c.b, gamma, c.tau, stats=True)
+        else:
+            idx = fpa.index(Qd, Kd, c.b, gamma, c.tau, stats=True)
     torch.cuda.synchronize()
     s = P.compare_index(idx, ref, gamma, c.tau)
     pat = idx.pattern.cpu().numpy()
@@ -291,12 +304,11 @@ TWO_PASS_CASES = [c for c in INDEX_CASES if c[0] in ("tiny", "tiny-G16", "tiny-N
 
 @pytest.mark.parametrize("name,kw,gamma", TWO_PASS_CASES, ids=[c[0] for c in TWO_PASS_CASES])
 @pytest.mark.parametrize("i8", [False, True], ids=["bf16", "i8"])
-def test_index_two_pass_statistics(name, kw, gamma, i8, monkeypatch):
+def test_index_two_pass_statistics(name, kw, gamma, i8):
     """The two-pass statistics form (used when the single pass's partials do not fit in LDS)
-    forced at small sizes."""
+    forced at small sizes through the test entry point fp_index_two_pass."""
     say(f"index {'i8' if i8 else 'bf16'} two-pass statistics {name} gamma={gamma}")
-    monkeypatch.setenv("FPATTN_STATS_TWO_PASS", "1")
-    _index_case(cfg(**kw), gamma, i8=i8)
+    _index_case(cfg(**kw), gamma, i8=i8, two_pass=True)
 
 
 def test_index_deterministic_and_end_to_end():
