@@ -25,6 +25,8 @@ FP_ECAPACITY = -4
 FP_EHIP = -5
 FP_EJOBCAPACITY = -6
 FP_ETIMEOUT = -7
+FP_ESCRATCH = -8
+FP_STATIC_SCRATCH_BYTES = 32 << 20    # include/fpattn.h
 FP_STATUS_CSR_OVERFLOW = 1
 FP_STATUS_JOB_OVERFLOW = 2
 FP_STATUS_WAIT_TIMEOUT = 4
@@ -81,6 +83,7 @@ def lib() -> ctypes.CDLL:
         L.fp_attn_i8.argtypes = [sp, _P, _P, _P, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
         L.fp_probe_qk_i8.argtypes = [sp, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]
         L.fp_index_two_pass.argtypes = [sp, ctypes.c_int, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
+        L.fp_index_static.argtypes = [sp, _P, _P, f, f, op, _P]
         lp = ctypes.POINTER(ctypes.c_int32)
         L.fp_index_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_attn_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
@@ -88,7 +91,7 @@ def lib() -> ctypes.CDLL:
         L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
                                        ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_batch", "fp_attn_batch",
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_batch", "fp_attn_batch",
                      "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -233,6 +236,23 @@ def index_i8(Q8, sQ, K8, sK, b: int, gamma: float, tau: float, *, stats: bool = 
                            ctypes.byref(o), _ptr(ws.buf), ws.nbytes, _stream(stream))
     if rc:
         raise FpError(rc, "fp_index_i8")
+    return out
+
+
+def index_static(Q: torch.Tensor, K: torch.Tensor, b: int, gamma: float, tau: float, *, stats: bool = False,
+                 out: Optional[Index] = None, stream=None) -> Index:
+    """fp_index_static: fp_index with the library's per-GPU scratch buffer instead of a workspace
+    (for callers that cannot allocate device memory; out must then be supplied preallocated)."""
+    Hq, S, d = Q.shape
+    Hkv = K.shape[0]
+    shape = shape_of(S, b, Hq, Hkv, d)
+    _check(Q, "Q", torch.bfloat16, (Hq, S, d))
+    _check(K, "K", torch.bfloat16, (Hkv, S, d))
+    out = Index.empty(shape, Q.device, stats=stats) if out is None else out
+    o = out.c_struct()
+    rc = lib().fp_index_static(ctypes.byref(shape), _ptr(Q), _ptr(K), gamma, tau, ctypes.byref(o), _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_index_static")
     return out
 
 

@@ -4,7 +4,14 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fp_internal.hpp"
+
+// Scratch of fp_index_static: one buffer per GPU, held by the library's code object for the
+// life of the process.  Host code never uses this name as an address (on the host it is only a
+// stand-in for the symbol); the device address comes from hipGetSymbolAddress, per device.
+static __device__ __align__(256) unsigned char scratch[FP_STATIC_SCRATCH_BYTES];
 
 namespace fp {
 
@@ -36,7 +43,8 @@ int make_plan(const fp_shape *s, Plan *p) {
   p->off_kbar = o;   o = align_up(o + sizeof(float) * Hkv * N * 128);
   p->off_sel = o;    o = align_up(o + sizeof(uint32_t) * Hq * 2 * p->nw32);
   p->off_rowbits = o; o = align_up(o + sizeof(uint32_t) * Hq * (size_t)N * p->nw32);
-  p->off_qbar = o;   o = align_up(o + sizeof(float) * Hq * (size_t)N * 128);
+  // pooled queries go through the workspace only in the two-launch query-aware path (N > 2048)
+  p->off_qbar = o;   o = align_up(o + (N > 2048 ? sizeof(float) * Hq * (size_t)N * 128 : 0));
   p->off_pe = o;     o = align_up(o + sizeof(float) * Hq * (size_t)N);
   p->off_jwork = o;  o = align_up(o + sizeof(int32_t) * Hkv * N);
   p->off_bar = o;    o = align_up(o + 256);
@@ -104,6 +112,7 @@ const char *fp_strerror(int code) {
     case FP_EHIP: return "HIP launch or query failed";
     case FP_EJOBCAPACITY: return "job-list capacity exceeded (device status)";
     case FP_ETIMEOUT: return "a bounded device-side wait gave up (device status)";
+    case FP_ESCRATCH: return "shape needs more scratch than fp_index_static's buffer (FP_STATIC_SCRATCH_BYTES)";
     default: return "unknown fpattn error code";
   }
 }
@@ -163,6 +172,37 @@ int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ, const 
                 const float *sK, float gamma, float tau, fp_index_out *out, void *ws,
                 size_t ws_bytes, void *stream) {
   return index_common(shape, true, Q8, sQ, K8, sK, gamma, tau, out, ws, ws_bytes, stream);
+}
+
+// Device address of this GPU's scratch buffer, looked up once per device with that device
+// current; NULL if the lookup fails.
+static void *static_scratch() {
+  static std::mutex mu;
+  static void *ptr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
+int fp_index_static(const fp_shape *shape, const void *Q, const void *K, float gamma, float tau,
+                    fp_index_out *out, void *stream) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if (!Q || !K || !out) return FP_EINVAL;
+  if ((rc = check_params(gamma, tau))) return rc;
+  if ((rc = check_out(p, out, true))) return rc;
+  if (p.total > (size_t)FP_STATIC_SCRATCH_BYTES) return FP_ESCRATCH;
+  void *ws = static_scratch();
+  if (!ws) return FP_EHIP;
+  return index_common(shape, false, Q, nullptr, K, nullptr, gamma, tau, out, ws, FP_STATIC_SCRATCH_BYTES,
+                      stream);
 }
 
 int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const float *sQ,

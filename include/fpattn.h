@@ -74,6 +74,7 @@ extern "C" {
 #define FP_EHIP         (-5) /* a HIP launch or query failed */
 #define FP_EJOBCAPACITY (-6) /* (device status bit 2) job-list capacity exceeded */
 #define FP_ETIMEOUT     (-7) /* (device status bit 3) a bounded device-side wait gave up */
+#define FP_ESCRATCH     (-8) /* fp_index_static: shape needs more than FP_STATIC_SCRATCH_BYTES */
 
 /* Device status word bits (fp_index_out.status[0]); 0 = success. */
 #define FP_STATUS_CSR_OVERFLOW 1u
@@ -180,6 +181,26 @@ int fp_index(const fp_shape *shape, const void *Q, const void *K,
 int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
                 const int8_t *K8, const float *sK, float gamma, float tau,
                 fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): fp_index
+ * with its scratch in a buffer of FP_STATIC_SCRATCH_BYTES that the library
+ * holds on each GPU it runs on, from the first call on that GPU until the
+ * process ends, instead of a caller workspace.  The call itself allocates
+ * nothing and calls no allocating routine.  Arguments, outputs and errors
+ * as fp_index, plus FP_ESCRATCH (nothing enqueued) when
+ * fp_workspace_bytes(shape, 0) exceeds FP_STATIC_SCRATCH_BYTES (32 MiB covers
+ * the 3B-shaped layer at S = 131072 with b = 64 or 128).  The buffer keeps
+ * the last call's contents; what must start at zero is cleared by the call's
+ * own kernels.  Every call on one GPU uses the same buffer: calls that
+ * overlap on one GPU (different streams, or other host threads) race and
+ * must be serialised by the caller; calls on one stream are ordered.  The
+ * outputs equal fp_index's for the same inputs.
+ */
+#define FP_STATIC_SCRATCH_BYTES (32u << 20)
+int fp_index_static(const fp_shape *shape, const void *Q, const void *K,
+                    float gamma, float tau, fp_index_out *out, void *stream);
 
 /*
  * Test entry point: fp_index (variant 0; sQ, sK ignored) or fp_index_i8

@@ -176,3 +176,30 @@ def test_batch_rejects_bad_arguments():
     assert L.fp_index_i8_batch(ctypes.byref(sh), 3, ragged, P, P, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
     assert L.fp_attn_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, P, None, outs, P, P, big, None) == fpa.FP_EINVAL
     assert L.fp_attn_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, P, P, outs, P, P, need - 1, None) == fpa.FP_EWORKSPACE
+
+
+@no_gpu_only
+def test_static_scratch_entry_point_rejects_before_enqueuing():
+    """fp_index_static checks its arguments like fp_index, and a shape whose scratch exceeds the
+    library's static buffer gets FP_ESCRATCH before any device call."""
+    L = fpa.lib()
+    P = ctypes.c_void_p(0x1000)
+    sh = fpa.shape_of(2048, 128, 4, 2)
+    o = _dummy_out(sh)
+    assert L.fp_index_static(ctypes.byref(sh), None, P, 0.9, 0.1, ctypes.byref(o), None) == fpa.FP_EINVAL
+    assert L.fp_index_static(ctypes.byref(sh), P, P, 1.5, 0.1, ctypes.byref(o), None) == fpa.FP_EINVAL
+    assert L.fp_index_static(ctypes.byref(sh), P, P, 0.9, 0.1, None, None) == fpa.FP_EINVAL
+    big = fpa.shape_of(64 * 8192, 64, 24, 8)
+    assert fpa.workspace_bytes(big, 0) > fpa.binding.FP_STATIC_SCRATCH_BYTES
+    ob = _dummy_out(big)
+    assert L.fp_index_static(ctypes.byref(big), P, P, 0.9, 0.1, ctypes.byref(ob), None) == fpa.FP_ESCRATCH
+    assert "scratch" in fpa.strerror(fpa.FP_ESCRATCH)
+
+
+def test_static_scratch_size_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define FP_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == fpa.binding.FP_STATIC_SCRATCH_BYTES
+    # the 3B-shaped 128K layer fits with 64- and 128-token blocks
+    for b in (64, 128):
+        assert fpa.workspace_bytes(fpa.shape_of(131072, b, 24, 8), 0) <= fpa.binding.FP_STATIC_SCRATCH_BYTES
