@@ -15,9 +15,9 @@ After the timed steps of the main layer the script (unless --no-cpu) runs the
 float64 oracle once over the whole layer on the host cores -- every head's
 index and every query block's attention on the device's CSR -- which gives
 both the CPU baseline and a full-size parity record of the device output.
-Unless --no-extra it then times the other layers (the W8A8 form of the main
-layer, and the 32K, 8B-shaped and 64-token-block layers) by the same
-protocol, as sub-records of the same line.
+Unless --no-extra it then times the main layer with head-pattern sharing and
+the other layers (the W8A8 form of the main layer, and the 32K, 8B-shaped and
+64-token-block layers) by the same protocol, as sub-records of the same line.
 
 Measured HBM traffic of the attention kernel (the `traffic` field) comes from
 two rocprofv3 counter passes over this script, scaled by the same counters on
@@ -172,7 +172,7 @@ def upload(c, L, dev):
     return {"q": up16(L.q), "k": up16(L.k), "v": up16(L.v)}
 
 
-def time_layer(c, T, steps: int, warmup: int, dev):
+def time_layer(c, T, steps: int, warmup: int, dev, shared: bool = False):
     """Warm-up steps, then `steps` timed steps of fp_index + fp_attn with HIP events on the launch
     stream around each stage.  The device status word is checked after the warm-up and again after
     the timed steps (a bounded device-side wait that gave up would make the timing meaningless)."""
@@ -185,7 +185,12 @@ def time_layer(c, T, steps: int, warmup: int, dev):
     stream = torch.cuda.current_stream()
 
     def index():
-        if c.int8:
+        if shared:
+            if c.int8:
+                fpa.index_shared(T["q8"], T["k8"], c.b, c.gamma, c.tau, sQ=T["sq"], sK=T["sk"], out=idx, ws=ws)
+            else:
+                fpa.index_shared(T["q"], T["k"], c.b, c.gamma, c.tau, out=idx, ws=ws)
+        elif c.int8:
             fpa.index_i8(T["q8"], T["sq"], T["k8"], T["sk"], c.b, c.gamma, c.tau, out=idx, ws=ws)
         else:
             fpa.index(T["q"], T["k"], c.b, c.gamma, c.tau, out=idx, ws=ws)
@@ -255,6 +260,24 @@ def layer_summary(c, idx, ms_step, t_idx, t_att):
     }
 
 
+def reuse_stats(c, idx):
+    """Key-block reuse from the device use counters (fp_block_uses): how often the query-major
+    schedule stages each block against the once-per-block minimum."""
+    import dynamic_block_sparse_flexprefill_amd as fpa
+    uses, head_uses = fpa.block_uses(idx)
+    u = uses.cpu().numpy().astype(np.int64).ravel()
+    hu = head_uses.cpu().numpy().astype(np.int64).ravel()
+    used = u[u > 0]
+    blk_bytes = 2 * c.b * c.d * (1 if c.int8 else 2)            # K and V of one block
+    top = np.sort(used)[::-1]
+    k1 = max(1, int(round(0.01 * used.size)))
+    return {"blocks_used": int(used.size), "blocks_total": int(u.size), "job_entries": int(u.sum()),
+            "head_block_pairs": int(hu.sum()), "mean_uses": round(float(used.mean()), 2),
+            "max_uses": int(used.max()), "entries_on_top_1pct_blocks": int(top[:k1].sum()),
+            "kv_bytes_once_per_block": int(used.size) * blk_bytes,
+            "kv_bytes_query_major": int(u.sum()) * blk_bytes}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +315,8 @@ def main(argv=None):
     log(f"[bench] warmup {args.warmup}, timing {args.steps} steps")
     idx, O, ms_step, t_idx, t_att, status = time_layer(c, T, args.steps, args.warmup, dev)
     main_rec = layer_summary(c, idx, ms_step, t_idx, t_att)
+    reuse = reuse_stats(c, idx)
+    log(f"[bench] key-block reuse: {reuse}")
     log(f"[bench] index {main_rec['stages_ms']['index_median']:.3f} ms ({main_rec['index']['achieved']:.0f} GB/s "
         f"algorithmic), attn {main_rec['stages_ms']['attn_median']:.3f} ms ({main_rec['attn']['achieved']:.1f} "
         f"TFLOP/s), density {main_rec['density']:.4f}, patterns {main_rec['patterns']}")
@@ -323,6 +348,7 @@ def main(argv=None):
         "attn_flop": main_rec["attn_flop"],
         "attn_flop_causal_exact": main_rec["attn_flop_causal_exact"],
         "patterns": main_rec["patterns"],
+        "block_reuse": reuse,
         "cpu_baseline": None,
         "parity": None,
         "other_layers": {},
@@ -333,6 +359,15 @@ def main(argv=None):
     del idx, O
 
     if not args.no_extra:
+        # head-pattern sharing on the same layer: heads of a group with one pattern share their rows
+        log(f"[bench] {c.name} with head-pattern sharing")
+        ix, _, msx, tix, tax, _ = time_layer(c, T, args.steps, args.warmup, dev, shared=True)
+        r = layer_summary(c, ix, msx, tix, tax)
+        r["workload"] = CONFIG_TEXT[c.name] + ", head-pattern sharing (fp_index_shared)"
+        rec["other_layers"][c.name + "-shared"] = r
+        log(f"[bench]   {msx:.3f} ms/layer: index {r['stages_ms']['index_median']:.3f} ms, attn "
+            f"{r['stages_ms']['attn_median']:.3f} ms ({r['attn']['achieved']:.0f} TFLOP/s), density {r['density']:.4f}")
+        del ix
         for name in EXTRA_CONFIGS:
             if name == c.name:
                 continue

@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.fp_probe_qk_i8.argtypes = [sp, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]
         L.fp_index_two_pass.argtypes = [sp, ctypes.c_int, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_index_static.argtypes = [sp, _P, _P, f, f, op, _P]
+        L.fp_index_shared.argtypes = [sp, ctypes.c_int, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
+        L.fp_block_uses.argtypes = [sp, op, _P, _P, _P]
         lp = ctypes.POINTER(ctypes.c_int32)
         L.fp_index_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_attn_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
@@ -91,7 +93,7 @@ def lib() -> ctypes.CDLL:
         L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
                                        ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_batch", "fp_attn_batch",
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_index_batch", "fp_attn_batch",
                      "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -256,10 +258,7 @@ def index_static(Q: torch.Tensor, K: torch.Tensor, b: int, gamma: float, tau: fl
     return out
 
 
-def index_two_pass(Q, K, b: int, gamma: float, tau: float, *, sQ=None, sK=None, stats: bool = False,
-                   out: Optional[Index] = None, ws: Optional[Workspace] = None, stream=None) -> Index:
-    """fp_index_two_pass: fp_index (bf16 Q, K) or fp_index_i8 (int8 Q, K with scales sQ, sK) with the
-    last-block statistics forced onto their two-pass form (a test entry point)."""
+def _index_variant(fn: str, Q, K, b, gamma, tau, sQ, sK, stats, out, ws, stream) -> Index:
     Hq, S, d = Q.shape
     Hkv = K.shape[0]
     shape = shape_of(S, b, Hq, Hkv, d)
@@ -273,12 +272,40 @@ def index_two_pass(Q, K, b: int, gamma: float, tau: float, *, sQ=None, sK=None, 
     out = Index.empty(shape, Q.device, stats=stats) if out is None else out
     ws = _ws(shape, ws, Q.device)
     o = out.c_struct()
-    rc = lib().fp_index_two_pass(ctypes.byref(shape), 1 if i8 else 0, _ptr(Q), _ptr(sQ) if i8 else None, _ptr(K),
-                                 _ptr(sK) if i8 else None, gamma, tau, ctypes.byref(o), _ptr(ws.buf), ws.nbytes,
-                                 _stream(stream))
+    rc = getattr(lib(), fn)(ctypes.byref(shape), 1 if i8 else 0, _ptr(Q), _ptr(sQ) if i8 else None, _ptr(K),
+                            _ptr(sK) if i8 else None, gamma, tau, ctypes.byref(o), _ptr(ws.buf), ws.nbytes,
+                            _stream(stream))
     if rc:
-        raise FpError(rc, "fp_index_two_pass")
+        raise FpError(rc, fn)
     return out
+
+
+def index_shared(Q, K, b: int, gamma: float, tau: float, *, sQ=None, sK=None, stats: bool = False,
+                 out: Optional[Index] = None, ws: Optional[Workspace] = None, stream=None) -> Index:
+    """fp_index_shared: fp_index (bf16 Q, K) or fp_index_i8 (int8 Q, K with scales sQ, sK) with
+    head-pattern sharing: heads of a KV group with the same pattern take the union of their rows."""
+    return _index_variant("fp_index_shared", Q, K, b, gamma, tau, sQ, sK, stats, out, ws, stream)
+
+
+def index_two_pass(Q, K, b: int, gamma: float, tau: float, *, sQ=None, sK=None, stats: bool = False,
+                   out: Optional[Index] = None, ws: Optional[Workspace] = None, stream=None) -> Index:
+    """fp_index_two_pass: fp_index (bf16 Q, K) or fp_index_i8 (int8 Q, K with scales sQ, sK) with the
+    last-block statistics forced onto their two-pass form (a test entry point)."""
+    return _index_variant("fp_index_two_pass", Q, K, b, gamma, tau, sQ, sK, stats, out, ws, stream)
+
+
+def block_uses(idx: Index, *, heads: bool = True, stream=None):
+    """fp_block_uses: (uses, head_uses) int32 [Hkv, N] -- job entries and (head, query block) pairs
+    per key block of each KV group (head_uses is None when heads is False)."""
+    sh = idx.shape
+    N = sh.S // sh.b
+    uses = torch.empty(sh.Hkv, N, dtype=torch.int32, device=idx.job_ptr.device)
+    hu = torch.empty_like(uses) if heads else None
+    o = idx.c_struct()
+    rc = lib().fp_block_uses(ctypes.byref(sh), ctypes.byref(o), _ptr(uses), _ptr(hu), _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_block_uses")
+    return uses, hu
 
 
 def build_jobs(shape: FpShape, row_ptr: torch.Tensor, col_idx: torch.Tensor, *,

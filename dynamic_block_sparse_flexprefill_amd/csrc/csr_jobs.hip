@@ -47,6 +47,7 @@ __device__ __forceinline__ uint32_t causal_mask_word(int i, int w) {
 
 struct JobArgs {
   int N, G, Hkv, nw32;
+  int share;                // heads of a KV group with the same pattern share the union of their rows
   const uint8_t *pattern;   // NULL: every row comes from rowbits
   const uint32_t *sel;      // [Hq][2][nw32]
   const uint32_t *rowbits;  // [Hq][N][nw32]
@@ -120,6 +121,20 @@ __global__ void __launch_bounds__(64 * kJobWaves) k_jobs(JobArgs a) {
     for (int hh = 0; hh < GM; ++hh) {
       wd[hh] = (hh < G && w < nwi) ? row_word(a, g * G + hh, i, w) : 0u;
       U |= wd[hh];
+    }
+    if (a.share) {
+      // head-pattern sharing: each head takes the union of the rows of its group's heads
+      // that have its pattern
+      uint32_t uq = 0u, uv = 0u;
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh) {
+        if (hh >= G) continue;
+        if (a.pattern[g * G + hh] == FP_PATTERN_QUERY_AWARE) uq |= wd[hh];
+        else uv |= wd[hh];
+      }
+#pragma unroll
+      for (int hh = 0; hh < GM; ++hh)
+        if (hh < G) wd[hh] = a.pattern[g * G + hh] == FP_PATTERN_QUERY_AWARE ? uq : uv;
     }
     if (!WRITE) {
 #pragma unroll
@@ -343,9 +358,11 @@ hipError_t run_jobs(const Plan &p, const JobArgs &a, hipStream_t st, bool rows) 
   return hipGetLastError();
 }
 
-hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st, bool rows) {
+hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st, bool rows,
+                 bool share = false) {
   JobArgs a;
   a.N = p.N; a.G = p.G; a.Hkv = p.Hkv; a.nw32 = p.nw32;
+  a.share = rows && share;
   a.pattern = rows ? io->pattern : nullptr;
   a.sel = w.sel;
   a.rowbits = w.rowbits;
@@ -392,7 +409,41 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   return hipGetLastError();
 }
 
+// Use counters of the key blocks ([E] 3.2: each block's consumer count, kept while the job
+// list is built, drives the liveness of the block in the cache).  One thread per job (g, i)
+// adds 1 to uses[g][j] and the number of heads in the entry's mask to head_uses[g][j] for
+// every entry j of the job; integer atomics, so the counts do not depend on the order.
+__global__ void k_zero_uses(int32_t *uses, int32_t *head_uses, int n) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= n) return;
+  uses[k] = 0;
+  if (head_uses) head_uses[k] = 0;
+}
+__global__ void k_block_uses(const int32_t *job_ptr, const int32_t *job_blk, const uint32_t *job_mask, int N,
+                             int jobs, int32_t *uses, int32_t *head_uses) {
+  const int job = blockIdx.x * blockDim.x + threadIdx.x;
+  if (job >= jobs) return;
+  const int g = job / N, i = job % N;
+  for (int e = job_ptr[job]; e < job_ptr[job + 1]; ++e) {
+    const int j = job_blk[e];
+    if (j < 0 || j > i) continue;                  // not a key block this job may use
+    atomicAdd(uses + (size_t)g * N + j, 1);
+    if (head_uses) atomicAdd(head_uses + (size_t)g * N + j, __popc(job_mask[e]));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_block_uses(const Plan &p, const fp_index_out *jobs, int32_t *uses, int32_t *head_uses,
+                             hipStream_t st) {
+  const int n = p.Hkv * p.N;
+  hipLaunchKernelGGL(k_zero_uses, dim3((n + 255) / 256), dim3(256), 0, st, uses, head_uses, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_block_uses, dim3((n + 255) / 256), dim3(256), 0, st, jobs->job_ptr, jobs->job_blk,
+                     jobs->job_mask, p.N, n, uses, head_uses);
+  return hipGetLastError();
+}
 
 hipError_t launch_status_init(int32_t *status, unsigned int *bar, hipStream_t st) {
   hipLaunchKernelGGL(k_status_init, dim3(1), dim3(1), 0, st, status, bar);
@@ -400,8 +451,8 @@ hipError_t launch_status_init(int32_t *status, unsigned int *bar, hipStream_t st
 }
 
 hipError_t launch_rows_and_jobs(const Plan &p, const fp_index_out *out, const Work &w,
-                                hipStream_t st) {
-  return build(p, out, w, st, true);
+                                hipStream_t st, bool share) {
+  return build(p, out, w, st, true, share);
 }
 
 hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st) {

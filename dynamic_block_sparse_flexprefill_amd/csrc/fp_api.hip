@@ -143,7 +143,7 @@ int64_t fp_job_capacity(const fp_shape *shape) {
 static int index_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
                         const void *K, const float *sK, float gamma, float tau,
                         fp_index_out *out, void *ws, size_t ws_bytes, void *stream,
-                        bool two_pass = false) {
+                        bool two_pass = false, bool share = false) {
   Plan p;
   int rc = make_plan(shape, &p);
   if (rc) return rc;
@@ -158,7 +158,7 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st, two_pass, &have_pe));
   FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, have_pe));
   FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st));
-  FP_LAUNCH(launch_rows_and_jobs(p, out, w, st));
+  FP_LAUNCH(launch_rows_and_jobs(p, out, w, st, share));
   return FP_OK;
 }
 
@@ -210,6 +210,24 @@ int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const f
                       void *ws, size_t ws_bytes, void *stream) {
   if (variant != 0 && variant != 1) return FP_EINVAL;
   return index_common(shape, variant == 1, Q, sQ, K, sK, gamma, tau, out, ws, ws_bytes, stream, true);
+}
+
+int fp_index_shared(const fp_shape *shape, int variant, const void *Q, const float *sQ,
+                    const void *K, const float *sK, float gamma, float tau, fp_index_out *out,
+                    void *ws, size_t ws_bytes, void *stream) {
+  if (variant != 0 && variant != 1) return FP_EINVAL;
+  return index_common(shape, variant == 1, Q, sQ, K, sK, gamma, tau, out, ws, ws_bytes, stream, false,
+                      true);
+}
+
+int fp_block_uses(const fp_shape *shape, const fp_index_out *jobs, int32_t *uses, int32_t *head_uses,
+                  void *stream) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if (!jobs || !jobs->job_ptr || !jobs->job_blk || !jobs->job_mask || !uses) return FP_EINVAL;
+  FP_LAUNCH(launch_block_uses(p, jobs, uses, head_uses, (hipStream_t)stream));
+  return FP_OK;
 }
 
 int fp_build_jobs(const fp_shape *shape, fp_index_out *io, void *ws, size_t ws_bytes,

@@ -68,8 +68,13 @@ hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float
 hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
                         const uint8_t *pattern, const Work &w, hipStream_t st);
 // Row bit sets -> CSR rows, grouped-query job list and its work order.
+// share: heads of a KV group with the same pattern take the union of their rows.
 hipError_t launch_rows_and_jobs(const Plan &p, const fp_index_out *out, const Work &w,
-                                hipStream_t st);
+                                hipStream_t st, bool share = false);
+// Use counters of the key blocks from a job list: uses[g][j] job entries, head_uses[g][j] (or NULL)
+// (head, query block) pairs per key block.
+hipError_t launch_block_uses(const Plan &p, const fp_index_out *jobs, int32_t *uses, int32_t *head_uses,
+                             hipStream_t st);
 // Caller-supplied CSR -> grouped-query job list and its work order.
 hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st);
 // status[0] = 0 and, when bar is not NULL, bar[0] = 0

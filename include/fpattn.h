@@ -217,6 +217,22 @@ int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const f
                       fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Head-pattern sharing ([R] 5, item 1: compress the sparse pattern by letting
+ * similar heads share one).  As fp_index (variant 0; sQ, sK ignored) or
+ * fp_index_i8 (variant 1), except that every query head h of KV group g gets
+ * the union of the index sets of the heads of g whose pattern equals h's:
+ *   J'(h, i) = U { J(h', i) : h' in g, pattern(h') = pattern(h) }.
+ * Heads with the same pattern in a group then have identical rows, and every
+ * job-list entry of a group whose heads share one pattern carries all of
+ * them.  pattern, jsd and stats are those of fp_index; the rows, the job list
+ * and its order follow the shared sets.  Errors as fp_index; FP_EINVAL for
+ * another variant.
+ */
+int fp_index_shared(const fp_shape *shape, int variant, const void *Q, const float *sQ,
+                    const void *K, const float *sK, float gamma, float tau,
+                    fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Rebuild the grouped-query job list (job_ptr, job_blk, job_mask, job_order)
  * from a CSR already in io->row_ptr / io->col_idx (rows sorted ascending,
  * every column <= its query block).  fp_index calls this itself; it is
@@ -225,6 +241,19 @@ int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const f
  */
 int fp_build_jobs(const fp_shape *shape, fp_index_out *io,
                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Use counters of the key blocks ([E] 3.2: the consumer count of each KV
+ * block, the input of the liveness-driven cache), from the job list of an
+ * fp_index / fp_build_jobs result (job_ptr, job_blk, job_mask; read only):
+ *   uses[g * N + j]      = number of jobs (g, i) whose entry list holds j,
+ *   head_uses[g * N + j] = number of (head, query block) pairs of group g
+ *                          whose index set holds j (NULL: not computed).
+ *   uses, head_uses: device int32 [Hkv * N], every element written.
+ * Errors: FP_EINVAL, FP_EUNSUPPORTED, FP_EHIP.
+ */
+int fp_block_uses(const fp_shape *shape, const fp_index_out *jobs, int32_t *uses,
+                  int32_t *head_uses, void *stream);
 
 /*
  * Block-sparse causal attention, bf16 ([E] 1.1 and 1.2 figure 3).

@@ -20,7 +20,9 @@ generation) and section 1.2 (Flex-Prefill's two patterns) describe them:
      diagonal block;
   6. query-aware heads score every query block's pooled query against the
      pooled keys (re-telling 1.1, "block-level index generation for every query
-     block").
+     block");
+  7. optionally, heads share sparse patterns (re-telling section 5, item 1:
+     similar heads share one pattern): share_rows().
 
 This module computes each step in its materialised form (the b x S score
 matrix is built explicitly); the streamed form the hardware uses is pinned
@@ -292,3 +294,43 @@ def index_i8(Q8, sQ, K8, sK, b: int, gamma: float, tau: float, heads=None, force
                 lambda h: block_means(as64(sQ[h])[:, None] * as64(Q8[h]), b),
                 lambda g: block_means(as64(sK[g])[:, None] * as64(K8[g]), b),
                 Hq, Hkv, S, d, b, gamma, tau, heads, force_pattern)
+
+
+# ---------------------------------------------------------------- step 7 (optional)
+def share_rows(res: IndexResult) -> IndexResult:
+    """Head-pattern sharing: every head h of KV group g takes, per query block i, the union of the
+    index sets of the heads of g whose pattern equals h's (re-telling section 5, item 1: similar
+    heads share one sparse pattern; "similar" is read as same KV group and same pattern).
+
+    Returns a new IndexResult whose heads keep their statistics, pattern and selections and carry
+    the shared rows; the input is not modified."""
+    G = res.Hq // res.Hkv
+    N = res.N
+    heads = []
+    for h, hd in enumerate(res.heads):
+        g = h // G
+        peers = [res.heads[p] for p in range(g * G, (g + 1) * G) if res.heads[p].pattern == hd.pattern]
+        rows = [np.array(sorted(set().union(*(set(int(j) for j in pr.rows[i]) for pr in peers))), dtype=np.int64)
+                for i in range(N)]
+        heads.append(HeadIndex(v=hd.v, sl=hd.sl, p=hd.p, D=hd.D, pattern=hd.pattern, vsel=hd.vsel, ssel=hd.ssel,
+                               rows=rows, qa_p=hd.qa_p, qa_sel=hd.qa_sel))
+    return IndexResult(S=res.S, b=res.b, Hq=res.Hq, Hkv=res.Hkv, heads=heads)
+
+
+def block_uses(res: IndexResult):
+    """Use counters of the key blocks (explainer section 3.2: each KV block's number of consumers,
+    counted while the job list is built): uses[g, j] = number of query blocks i whose grouped job
+    (the union of J(h, i) over the heads h of KV group g) holds j; head_uses[g, j] = number of
+    (head, query block) pairs of group g whose index set holds j."""
+    G, N = res.Hq // res.Hkv, res.N
+    uses = np.zeros((res.Hkv, N), dtype=np.int64)
+    head_uses = np.zeros((res.Hkv, N), dtype=np.int64)
+    for g in range(res.Hkv):
+        for i in range(N):
+            union = set()
+            for h in range(g * G, (g + 1) * G):
+                row = res.heads[h].rows[i]
+                union.update(int(j) for j in row)
+                head_uses[g, row] += 1
+            uses[g, sorted(union)] += 1
+    return uses, head_uses

@@ -385,3 +385,77 @@ def test_capacity_overflow_sets_status():
     assert st & fpa.FP_STATUS_CSR_OVERFLOW
     rp = out.row_ptr.cpu().numpy()
     assert rp[-1] == c.Hq * c.N + 5 and np.all(np.diff(rp) >= 0)
+
+
+# ------------------------------------------------------------------ head-pattern sharing
+SHARED_CASES = [("tiny-G3", dict(S=2048, Hq=6, Hkv=2)), ("tiny-G4-b256", dict(S=4096, b=256, Hq=8, Hkv=2)),
+                ("tiny-b64-G3", dict(S=2048, b=64, Hq=6, Hkv=2))]
+
+
+@pytest.mark.parametrize("name,kw", SHARED_CASES, ids=[c[0] for c in SHARED_CASES])
+@pytest.mark.parametrize("i8", [False, True], ids=["bf16", "i8"])
+def test_index_shared(name, kw, i8):
+    """fp_index_shared: each head's rows are exactly the union of the plain rows of its group's heads
+    with the same pattern (the plain rows being oracle-checked); the oracle's shared rows agree
+    under the boundary rule; attention on the shared index matches the oracle on that CSR."""
+    say(f"index shared {'i8' if i8 else 'bf16'} {name}")
+    c = cfg(**kw)
+    idx, ref = _index_case(c, c.gamma, i8=i8)
+    L = gen.make(c)
+    if i8:
+        t = P.layer_i8_on_device(L)
+        sh = fpa.index_shared(t["q8"], t["k8"], c.b, c.gamma, c.tau, sQ=t["sq"], sK=t["sk"])
+    else:
+        Qd, Kd, Vd = P.layer_on_device(L)
+        sh = fpa.index_shared(Qd, Kd, c.b, c.gamma, c.tau)
+    torch.cuda.synchronize()
+    assert int(sh.status.item()) == 0
+    pat = idx.pattern.cpu().numpy()
+    assert np.array_equal(pat, sh.pattern.cpu().numpy())
+    rp, ci = P.gpu_rows(idx)
+    rs, cs = P.gpu_rows(sh)
+    N, G = c.N, c.G
+    for h in range(c.Hq):
+        peers = [p for p in range(h // G * G, h // G * G + G) if pat[p] == pat[h]]
+        for i in range(N):
+            want = sorted(set().union(*(set(ci[rp[p * N + i]:rp[p * N + i + 1]].tolist()) for p in peers)))
+            assert cs[rs[h * N + i]:rs[h * N + i + 1]].tolist() == want, (h, i)
+    P.check_jobs(sh, G)
+    # the oracle's shared rows, where no member's selection sits at an ambiguous boundary
+    shared_ref = oi.share_rows(ref)
+    same = sum(np.array_equal(cs[rs[h * N + i]:rs[h * N + i + 1]], shared_ref.heads[h].rows[i])
+               for h in range(c.Hq) for i in range(N))
+    say(f"  shared rows equal to the oracle's: {same} / {c.Hq * N}; density {sh.density():.3f} vs {idx.density():.3f}")
+    summ = P.compare_index(idx, ref, c.gamma, c.tau)
+    if summ["boundary_rows"] == 0 and summ["pattern_mismatch"] == 0:
+        assert same == c.Hq * N
+    assert sh.density() >= idx.density()
+    if i8:
+        d = L.int8()
+        O = fpa.attn_i8(t["q8"], t["sq"], t["k8"], t["sk"], t["v8"], t["sv"], sh)
+        Oref = oracle.attn.attn_i8(d["q8"], d["sq"], d["k8"], d["sk"], d["v8"], d["sv"], rs, cs, c.b)
+    else:
+        O = fpa.attn(Qd, Kd, Vd, sh)
+        Oref = oracle.attn.attn(L.f32("q"), L.f32("k"), L.f32("v"), rs, cs, c.b)
+    mx, rms = P.attn_errors(O, Oref)
+    say(f"  attention on the shared index: maxabs {mx:.2e} rms {rms:.2e}")
+    assert mx <= MAXABS and rms <= RMS
+
+
+def test_block_uses_match_oracle():
+    """fp_block_uses (consumer counts per key block) against the oracle's counts on the device CSR."""
+    say("block uses, tiny G3 and b256")
+    for kw in (dict(S=2048, Hq=6, Hkv=2), dict(S=4096, b=256, Hq=8, Hkv=2)):
+        c = cfg(**kw)
+        L = gen.make(c)
+        Qd, Kd, _ = P.layer_on_device(L)
+        idx = fpa.index(Qd, Kd, c.b, c.gamma, c.tau)
+        uses, head_uses = fpa.block_uses(idx)
+        torch.cuda.synchronize()
+        rp, ci = P.gpu_rows(idx)
+        N = c.N
+        heads = [oi.HeadIndex(v=None, sl=None, p=None, D=0.0, pattern=0,
+                              rows=[ci[rp[h * N + i]:rp[h * N + i + 1]] for i in range(N)]) for h in range(c.Hq)]
+        want_u, want_h = oi.block_uses(oi.IndexResult(S=c.S, b=c.b, Hq=c.Hq, Hkv=c.Hkv, heads=heads))
+        np.testing.assert_array_equal(uses.cpu().numpy(), want_u)
+        np.testing.assert_array_equal(head_uses.cpu().numpy(), want_h)

@@ -272,6 +272,74 @@ def test_qa_rows_match_brute_force(seed, gamma):
         assert tuple(row) in sets, (i, list(row), sets)
 
 
+def test_share_rows_by_hand():
+    """Head-pattern sharing on hand-written rows: one group of three heads (two query-aware, one
+    vertical-slash) and one group of a single head."""
+    def hd(pattern, rows):
+        return oi.HeadIndex(v=np.zeros(3), sl=np.zeros(3), p=np.zeros(3), D=0.0, pattern=pattern,
+                            rows=[np.array(r) for r in rows])
+    res = oi.IndexResult(S=6, b=2, Hq=4, Hkv=2, heads=[
+        hd(oi.QA, [[0], [0, 1], [0, 2]]),
+        hd(oi.VS, [[0], [0, 1], [0, 1, 2]]),
+        hd(oi.QA, [[0], [0, 1], [0, 1, 2]]),
+        hd(oi.VS, [[0], [0, 1], [0, 2]]),
+    ])
+    # G = 2: group 0 = heads 0, 1 (QA, VS: nothing shared), group 1 = heads 2, 3 (QA, VS)
+    sh = oi.share_rows(res)
+    assert [list(r) for r in sh.heads[0].rows] == [[0], [0, 1], [0, 2]]
+    assert [list(r) for r in sh.heads[1].rows] == [[0], [0, 1], [0, 1, 2]]
+    res.Hkv = 1   # G = 4: heads 0 and 2 share (QA), heads 1 and 3 share (VS)
+    sh = oi.share_rows(res)
+    assert [list(r) for r in sh.heads[0].rows] == [[0], [0, 1], [0, 1, 2]]
+    assert [list(r) for r in sh.heads[2].rows] == [[0], [0, 1], [0, 1, 2]]
+    assert [list(r) for r in sh.heads[1].rows] == [[0], [0, 1], [0, 1, 2]]
+    assert [list(r) for r in sh.heads[3].rows] == [[0], [0, 1], [0, 1, 2]]
+    assert [list(r) for r in res.heads[3].rows] == [[0], [0, 1], [0, 2]]     # input untouched
+
+
+def test_share_rows_invariants_on_planted_layer():
+    L = gen.make(gen.CONFIGS["tiny"].with_(S=1024, Hq=6, Hkv=2))
+    res = oi.index(L.f32("q"), L.f32("k"), 128, 0.9, 0.1)
+    sh = oi.share_rows(res)
+    G = 3
+    for h, (a, b_) in enumerate(zip(res.heads, sh.heads)):
+        peers = [p for p in range(h // G * G, h // G * G + G) if res.heads[p].pattern == a.pattern]
+        for i in range(res.N):
+            assert set(a.rows[i]) <= set(b_.rows[i])                   # a superset of the head's own row
+            assert set(b_.rows[i]) == set().union(*(set(res.heads[p].rows[i]) for p in peers))
+            assert np.all(np.diff(b_.rows[i]) > 0) and b_.rows[i][0] == 0 and b_.rows[i][-1] == i
+    assert sh.density() >= res.density()
+    # one head per group: sharing changes nothing
+    r1 = oi.index(L.f32("q")[:2], L.f32("k"), 128, 0.9, 0.1)
+    assert all(np.array_equal(x, y) for a, b_ in zip(r1.heads, oi.share_rows(r1).heads) for x, y in zip(a.rows, b_.rows))
+
+
+def test_block_uses_by_hand():
+    """Use counters on hand-written rows: G = 2, N = 3."""
+    def hd(rows):
+        return oi.HeadIndex(v=np.zeros(3), sl=np.zeros(3), p=np.zeros(3), D=0.0, pattern=oi.QA,
+                            rows=[np.array(r) for r in rows])
+    res = oi.IndexResult(S=6, b=2, Hq=2, Hkv=1, heads=[hd([[0], [0, 1], [0, 2]]), hd([[0], [0, 1], [0, 1, 2]])])
+    uses, head_uses = oi.block_uses(res)
+    # jobs: i=0 {0}, i=1 {0,1}, i=2 {0,1,2}
+    assert uses.tolist() == [[3, 2, 1]]
+    assert head_uses.tolist() == [[6, 3, 2]]
+
+
+def test_block_uses_totals_on_planted_layer():
+    L = gen.make(gen.CONFIGS["tiny"].with_(S=1024, Hq=6, Hkv=2))
+    res = oi.index(L.f32("q"), L.f32("k"), 128, 0.9, 0.1)
+    uses, head_uses = oi.block_uses(res)
+    rp, ci = res.csr()
+    assert head_uses.sum() == ci.size                          # every (h, i, j) counted once
+    G, N = 3, res.N
+    unions = sum(len(set().union(*(set(res.heads[h].rows[i]) for h in range(g * G, g * G + G))))
+                 for g in range(2) for i in range(N))
+    assert uses.sum() == unions                                # every job entry counted once
+    assert np.all(uses[:, 0] == N)                             # block 0 is in every row
+    assert np.all(uses <= head_uses) and np.all(head_uses <= G * uses)
+
+
 def test_single_block_sequence():
     rng = np.random.default_rng(2)
     Q, K, V = rand_layer(rng, 128, 128, 2, 1, 16)
