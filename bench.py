@@ -260,6 +260,60 @@ def layer_summary(c, idx, ms_step, t_idx, t_att):
     }
 
 
+def time_attn(c, T, idx, steps: int, warmup: int, split=None):
+    """Median ms of fp_attn (split None) or fp_attn_split (split = (nsplit, nseg)) on a fixed index."""
+    import torch
+    import dynamic_block_sparse_flexprefill_amd as fpa
+    O = torch.empty(c.Hq, c.S, c.d, dtype=torch.bfloat16, device=T["q"].device)
+    if split:
+        ws = fpa.SplitWorkspace(idx.shape, split[0], split[1], T["q"].device)
+        run = lambda: fpa.attn_split(T["q"], T["k"], T["v"], idx, split[0], split[1], out=O, ws=ws)
+    else:
+        ws = fpa.Workspace(idx.shape, T["q"].device)
+        run = lambda: fpa.attn(T["q"], T["k"], T["v"], idx, out=O, ws=ws)
+    for _ in range(warmup):
+        run()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b_ in ev:
+        a.record(stream)
+        run()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b_) for a, b_ in ev])), O
+
+
+def split_kv_records(c, T, idx, steps, warmup, dev):
+    """The split-KV schedule against the query-major one: on the main layer (the 256 longest jobs in
+    2 segments, and every job in 2), and on a layer with fewer jobs than compute units (one KV group
+    at S = 16384: 128 jobs), where splitting should pay."""
+    import gen
+    import dynamic_block_sparse_flexprefill_amd as fpa
+    out = {}
+    flops, _ = attn_flops(c, idx.nnz)
+    base, O0 = time_attn(c, T, idx, steps, warmup)
+    out[c.name] = {"query_major_ms": round(base, 4)}
+    for ns, sg in ((256, 2), (c.Hkv * c.N, 2)):
+        t, O1 = time_attn(c, T, idx, steps, warmup, split=(ns, sg))
+        diff = float((O1.float() - O0.float()).abs().max().item())
+        out[c.name][f"split_{ns}x{sg}_ms"] = round(t, 4)
+        out[c.name][f"split_{ns}x{sg}_maxabs_vs_query_major"] = diff
+    cs = gen.CONFIGS["3b-32k"].with_(name="1kv-16k", S=16384, Hq=3, Hkv=1)
+    Ls = gen.make(cs, seed=0)
+    Ts = upload(cs, Ls, dev)
+    ix = fpa.index(Ts["q"], Ts["k"], cs.b, cs.gamma, cs.tau)
+    rec = {"workload": "one KV group (Hq=3, Hkv=1), S=16384, b=128, d=128: 128 jobs for 256 compute units",
+           "density": round(ix.density(), 4)}
+    base, O0 = time_attn(cs, Ts, ix, steps, warmup)
+    rec["query_major_ms"] = round(base, 4)
+    for sg in (2, 4, 8):
+        t, O1 = time_attn(cs, Ts, ix, steps, warmup, split=(cs.Hkv * cs.N, sg))
+        rec[f"split_all_x{sg}_ms"] = round(t, 4)
+        rec[f"split_all_x{sg}_maxabs_vs_query_major"] = float((O1.float() - O0.float()).abs().max().item())
+    out["1kv-16k"] = rec
+    return out
+
+
 def reuse_stats(c, idx):
     """Key-block reuse from the device use counters (fp_block_uses): how often the query-major
     schedule stages each block against the once-per-block minimum."""
@@ -352,6 +406,7 @@ def main(argv=None):
         "cpu_baseline": None,
         "parity": None,
         "other_layers": {},
+        "split_kv": None,
     }
 
     if not args.no_cpu:
@@ -368,6 +423,12 @@ def main(argv=None):
         log(f"[bench]   {msx:.3f} ms/layer: index {r['stages_ms']['index_median']:.3f} ms, attn "
             f"{r['stages_ms']['attn_median']:.3f} ms ({r['attn']['achieved']:.0f} TFLOP/s), density {r['density']:.4f}")
         del ix
+        if not c.int8 and c.b >= 128:
+            log("[bench] split-KV schedule against the query-major one")
+            ix = __import__("dynamic_block_sparse_flexprefill_amd").index(T["q"], T["k"], c.b, c.gamma, c.tau)
+            rec["split_kv"] = split_kv_records(c, T, ix, args.steps, args.warmup, dev)
+            log(f"[bench]   {rec['split_kv']}")
+            del ix
         for name in EXTRA_CONFIGS:
             if name == c.name:
                 continue

@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.fp_index_static.argtypes = [sp, _P, _P, f, f, op, _P]
         L.fp_index_shared.argtypes = [sp, ctypes.c_int, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_block_uses.argtypes = [sp, op, _P, _P, _P]
+        L.fp_attn_split_workspace_bytes.argtypes = [sp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.fp_attn_split.argtypes = [sp, _P, _P, _P, op, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
         lp = ctypes.POINTER(ctypes.c_int32)
         L.fp_index_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_attn_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
@@ -93,7 +95,7 @@ def lib() -> ctypes.CDLL:
         L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
                                        ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_index_batch", "fp_attn_batch",
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_attn_split_workspace_bytes", "fp_attn_split", "fp_index_batch", "fp_attn_batch",
                      "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -344,6 +346,37 @@ def attn(Q, K, V, idx: Index, *, out: Optional[torch.Tensor] = None, ws: Optiona
                        _ptr(ws.buf), ws.nbytes, _stream(stream))
     if rc:
         raise FpError(rc, "fp_attn")
+    return O
+
+
+class SplitWorkspace:
+    """A device byte buffer sized by fp_attn_split_workspace_bytes."""
+
+    def __init__(self, shape: FpShape, nsplit: int, nseg: int, device):
+        n = ctypes.c_size_t(0)
+        rc = lib().fp_attn_split_workspace_bytes(ctypes.byref(shape), nsplit, nseg, ctypes.byref(n))
+        if rc:
+            raise FpError(rc, "fp_attn_split_workspace_bytes")
+        self.nbytes = n.value
+        self.buf = torch.empty(max(self.nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def attn_split(Q, K, V, idx: Index, nsplit: int, nseg: int, *, out: Optional[torch.Tensor] = None,
+               ws: Optional[SplitWorkspace] = None, stream=None) -> torch.Tensor:
+    """fp_attn_split: the attention with the nsplit longest jobs cut into nseg split-KV segments whose
+    partial results are merged by a keyed combine step (bf16, b >= 128)."""
+    shape = idx.shape
+    _check(Q, "Q", torch.bfloat16, (shape.Hq, shape.S, shape.d))
+    _check(K, "K", torch.bfloat16, (shape.Hkv, shape.S, shape.d))
+    _check(V, "V", torch.bfloat16, (shape.Hkv, shape.S, shape.d))
+    O = torch.empty_like(Q) if out is None else out
+    _check(O, "O", torch.bfloat16, (shape.Hq, shape.S, shape.d))
+    ws = SplitWorkspace(shape, nsplit, nseg, Q.device) if ws is None else ws
+    o = idx.c_struct()
+    rc = lib().fp_attn_split(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(V), ctypes.byref(o), nsplit, nseg, _ptr(O),
+                             _ptr(ws.buf), ws.nbytes, _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_attn_split")
     return O
 
 

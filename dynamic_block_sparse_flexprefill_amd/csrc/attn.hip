@@ -44,7 +44,12 @@ struct AttnArgs {
   uint16_t *O;
   int S, N, B, G, qpw, parts;
   float c2;
+  float *part;        // split-KV units only: fp32 partial outputs, [slot][G][b][kPartStride]
 };
+
+// Split-KV units (fp_attn_split): a partial output row holds the unnormalised O^T row (128 fp32), the
+// reference maximum m (log2 units) and the weight sum l, padded to 16 bytes.
+constexpr int kPartStride = 132;
 
 constexpr int kChunkDl = 128;                // keys per staged chunk
 constexpr int kVStride = kChunkDl + 8;       // bf16 elements per transposed int8-path V row (272 B)
@@ -289,6 +294,7 @@ __device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstla
 struct Unit {
   int u, g, i, part, p0, n, total, rot;        // n: job-list entries, total: chunks
   bool empty;                                  // no job-list entry: one chunk that computes nothing
+  int slot;                                    // split-KV unit: its partial-output slot (else -1)
 };
 
 // Job-list entry of one chunk: key block jv and head mask maskv (as loaded,
@@ -307,7 +313,12 @@ struct Ent {
 // continuous chunk stream across them, so the next unit's first chunk is
 // loaded while the current unit's last chunk is computed.  A workgroup stops
 // at the first unit index past the end; indices only grow, so none is lost.
-template <int NT, bool I8, bool PAIR>
+//
+// SPLIT (fp_attn_split): a unit may cover a contiguous range of its job's entries (a split-KV
+// segment).  Such a unit's table entry carries -1 - slot in place of the rotation, and instead of
+// normalising and writing O it writes its unnormalised rows with their (m, l) to partial slot
+// `slot`; k_attn_combine merges a job's slots afterwards.
+template <int NT, bool I8, bool PAIR, bool SPLIT>
 __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, int nunits, unsigned int *ctr) {
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][I8 ? dl::KBuf8 : dl::KBuf];
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][I8 ? dl::VBuf8 : dl::VBuf];
@@ -324,7 +335,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   const float qscale = a.c2;
 
   auto unit_from = [&](int u, const int4 &t) -> Unit {
-    Unit x{u, 0, 0, 0, 0, 0, 0, 0, true};
+    Unit x{u, 0, 0, 0, 0, 0, 0, 0, true, -1};
     if (u >= nunits) return x;
     const int job = sgpr(t.x);
     x.part = u % a.parts;
@@ -334,6 +345,12 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     x.n = sgpr(t.z);
     x.total = PAIR ? (x.n + 1) >> 1 : x.n * nck;
     x.rot = sgpr(t.w);
+    if constexpr (SPLIT) {
+      if (x.rot < 0) {
+        x.slot = -1 - x.rot;
+        x.rot = 0;
+      }
+    }
     x.empty = x.total == 0;
     if (x.empty) x.total = 1;
     return x;
@@ -390,7 +407,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   if ((int)blockIdx.x >= nunits) return;
   Unit cur = unit_from(blockIdx.x, vload(utab + blockIdx.x));
   int nxt_id = blockIdx.x + gridDim.x;                // claimed unit that follows cur
-  Unit nxt{nunits, 0, 0, 0, 0, 0, 0, 0, true};
+  Unit nxt{nunits, 0, 0, 0, 0, 0, 0, 0, true, -1};
   int parity = 0;
   Ent e0 = fetch(cur, 0), e1 = fetch(cur, 1);
   issue(e0, 0);
@@ -640,7 +657,24 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     l += xor32(l);
     const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     uint16_t *orow = a.O + tok * 128;
-    if (live) {
+    bool direct = live;
+    if constexpr (SPLIT) {
+      if (live && cur.slot >= 0) {
+        // split-KV segment: the unnormalised row (columns 32 dt + 8 j + 4 hf + (0..3) of this lane)
+        // and its (m, l), for the combine step
+        direct = false;
+        const int r = qtok - cur.i * B;                        // row within the query block
+        float *pr = a.part + (((size_t)cur.slot * a.G + hh) * B + r) * kPartStride;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *(f32x4 *)(pr + 32 * dt + 8 * j + 4 * hf) =
+                f32x4{o[dt][4 * j], o[dt][4 * j + 1], o[dt][4 * j + 2], o[dt][4 * j + 3]};
+        if (hf == 0) *(float2 *)(pr + 128) = make_float2(m, l);
+      }
+    }
+    if (direct) {
       // Lane (row, hf) holds columns 32 dt + 8 j + 4 hf + (0..3), j = 0..3, of its query row.
       // One swap with the other half-wave per 32-bit word (groups j = 0, 1 offered by the upper
       // half, j = 2, 3 by the lower) leaves each lane columns 32 dt + 16 hf + (0..15), stored as
@@ -680,6 +714,60 @@ __global__ void k_attn_prep(const int32_t *job_order, const int32_t *job_ptr, in
   // chunks start at a per-job offset so that workgroups do not all fetch the same (sink) blocks at once
   const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
   utab[u] = int4{job, p0, n, rot};
+}
+
+// Unit table of fp_attn_split: the nsplit longest jobs (the first in job order) are cut into nseg
+// segments of consecutive entries, unit (segment, part); the other jobs follow as in k_attn_prep.
+// A segment's entry carries -1 - slot (slot = job rank * nseg + segment) in place of the rotation.
+__global__ void k_attn_prep_split(const int32_t *job_order, const int32_t *job_ptr, int nunits, int parts,
+                                  int nck, int nsplit, int nseg, int4 *utab, unsigned int *ctr) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u == 0) ctr[0] = 0u;
+  if (u >= nunits) return;
+  const int nsu = nsplit * nseg * parts;
+  if (u < nsu) {
+    const int js = u / parts, k = js / nseg, seg = js % nseg;
+    const int job = job_order[k];
+    const int p0 = job_ptr[job], n = job_ptr[job + 1] - p0;
+    const int s0 = (int)((long)n * seg / nseg), s1 = (int)((long)n * (seg + 1) / nseg);
+    utab[u] = int4{job, p0 + s0, s1 - s0, -1 - (k * nseg + seg)};
+  } else {
+    const int job = job_order[nsplit + (u - nsu) / parts];
+    const int p0 = job_ptr[job], n = job_ptr[job + 1] - p0;
+    const int total = nck > 0 ? n * nck : (n + 1) >> 1;
+    const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
+    utab[u] = int4{job, p0, n, rot};
+  }
+}
+
+// Keyed combine of fp_attn_split: for every row of the nsplit split jobs, merge the nseg partial
+// rows (m_s, l_s, O_s): M = max m_s, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, as bf16.
+// One wave per (job rank, head, row); lane c covers columns 2c and 2c + 1.
+__global__ void __launch_bounds__(256) k_attn_combine(const float *part, const int32_t *job_order, int N, int S,
+                                                      int B, int G, int nsplit, int nseg, uint16_t *O) {
+  const int lane = threadIdx.x & 63;
+  const int rowid = blockIdx.x * 4 + (threadIdx.x >> 6);          // (k, hh, r)
+  if (rowid >= nsplit * G * B) return;
+  const int r = rowid % B, hh = (rowid / B) % G, k = rowid / (B * G);
+  const int job = job_order[k], g = job / N, i = job % N;
+  float M = -3.0e38f;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const float *pr = part + (((size_t)(k * nseg + sg) * G + hh) * B + r) * kPartStride;
+    M = fmaxf(M, pr[128]);
+  }
+  float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
+  for (int sg = 0; sg < nseg; ++sg) {
+    const float *pr = part + (((size_t)(k * nseg + sg) * G + hh) * B + r) * kPartStride;
+    const float2 ml = *(const float2 *)(pr + 128);
+    const float w = ml.y > 0.0f ? exp2f(ml.x - M) : 0.0f;
+    const float2 ov = *(const float2 *)(pr + 2 * lane);
+    L += w * ml.y;
+    o0 += w * ov.x;
+    o1 += w * ov.y;
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  uint16_t *orow = O + ((size_t)(g * G + hh) * S + (size_t)i * B + r) * 128;
+  *(uint32_t *)(orow + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
 }
 
 // Test hook: out[c * B + r] = Q8[h, i*B + r] . K8[g, j*B + c] through the W8A8 attention kernel's
@@ -735,35 +823,52 @@ static int attn_qpw(const Plan &p) {
   return qpw;
 }
 
-template <int NT, bool I8, bool PAIR>
-hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
-  const int nunits = p.Hkv * p.N * a.parts;
+// split: {nsplit, nseg} of fp_attn_split, or nullptr for the plain schedule.
+template <int NT, bool I8, bool PAIR, bool SPLIT>
+hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, const int *split,
+                       hipStream_t st) {
+  const int jobs = p.Hkv * p.N;
+  const int nsplit = SPLIT ? std::min(split[0], jobs) : 0, nseg = SPLIT ? split[1] : 1;
+  const int nunits = (jobs + nsplit * (nseg - 1)) * a.parts;
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT, I8, PAIR>, NT, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT, I8, PAIR, SPLIT>, NT, 0) != hipSuccess)
     per_cu = 0;
   const int cus = cu_count();
   const int grid = std::max(1, std::min(nunits, std::max(1, per_cu) * std::max(1, cus)));
-  hipLaunchKernelGGL(k_attn_prep, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
-                     nunits, a.parts, p.B / kChunkDl, utab, ctr);
-  hipLaunchKernelGGL((k_attn_dl<NT, I8, PAIR>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits, ctr);
+  if (SPLIT)
+    hipLaunchKernelGGL(k_attn_prep_split, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
+                       nunits, a.parts, p.B / kChunkDl, nsplit, nseg, utab, ctr);
+  else
+    hipLaunchKernelGGL(k_attn_prep, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
+                       nunits, a.parts, p.B / kChunkDl, utab, ctr);
+  hipLaunchKernelGGL((k_attn_dl<NT, I8, PAIR, SPLIT>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits,
+                     ctr);
+  if (SPLIT && nsplit > 0) {
+    const int rows = nsplit * p.G * p.B;
+    hipLaunchKernelGGL(k_attn_combine, dim3((rows + 3) / 4), dim3(256), 0, st, (const float *)a.part, a.job_order,
+                       p.N, p.S, p.B, p.G, nsplit, nseg, a.O);
+  }
   return hipGetLastError();
 }
 
-template <bool I8, bool PAIR>
-hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st) {
+template <bool I8, bool PAIR, bool SPLIT = false>
+hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4 *utab, hipStream_t st,
+                         const int *split = nullptr) {
   const int need = 64 * p.G * a.qpw;                 // G * qpw <= 16 (G <= 16, G * b <= 2048)
-  if (need <= 256) return run_attn_dl<256, I8, PAIR>(p, a, ctr, utab, st);
-  if (need <= 512) return run_attn_dl<512, I8, PAIR>(p, a, ctr, utab, st);
-  if (need <= 768) return run_attn_dl<768, I8, PAIR>(p, a, ctr, utab, st);
-  return run_attn_dl<1024, I8, PAIR>(p, a, ctr, utab, st);
+  if (need <= 256) return run_attn_dl<256, I8, PAIR, SPLIT>(p, a, ctr, utab, split, st);
+  if (need <= 512) return run_attn_dl<512, I8, PAIR, SPLIT>(p, a, ctr, utab, split, st);
+  if (need <= 768) return run_attn_dl<768, I8, PAIR, SPLIT>(p, a, ctr, utab, split, st);
+  return run_attn_dl<1024, I8, PAIR, SPLIT>(p, a, ctr, utab, split, st);
 }
 
 }  // namespace
 
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,
-                       void *O, unsigned int *ctr, int4 *utab, hipStream_t st) {
+                       void *O, unsigned int *ctr, int4 *utab, hipStream_t st, int nsplit, int nseg,
+                       float *part) {
   AttnArgs a;
+  a.part = part;
   a.Q = (const uint8_t *)Q; a.K = (const uint8_t *)K; a.V = (const uint8_t *)V;
   a.sQ = sQ; a.sK = sK; a.sV = sV;
   a.job_ptr = csr->job_ptr; a.job_blk = csr->job_blk; a.job_order = csr->job_order;
@@ -776,10 +881,16 @@ hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, c
   const int qpw = attn_qpw(p);
   a.qpw = qpw;
   a.parts = p.B / 32 / qpw;
+  if (nseg > 1) {   // split-KV schedule (bf16, b >= 128)
+    const int split[2] = {nsplit, nseg};
+    return dispatch_attn<false, false, true>(p, a, ctr, utab, st, split);
+  }
   if (p.B == 64)   // two 64-key blocks per 128-key chunk
     return i8 ? dispatch_attn<true, true>(p, a, ctr, utab, st) : dispatch_attn<false, true>(p, a, ctr, utab, st);
   return i8 ? dispatch_attn<true, false>(p, a, ctr, utab, st) : dispatch_attn<false, false>(p, a, ctr, utab, st);
 }
+
+size_t attn_split_slot_floats(const Plan &p) { return (size_t)p.G * p.B * kPartStride; }
 
 hipError_t launch_probe_attn_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i, int j,
                                 int32_t *out, hipStream_t st) {

@@ -267,6 +267,46 @@ int fp_attn(const fp_shape *shape, const void *Q, const void *K, const void *V,
                      stream);
 }
 
+// fp_attn_split workspace: fp_attn's, then the split unit table and the partial slots.
+static int split_layout(const Plan &p, int nsplit, int nseg, size_t *utab_off, size_t *part_off, size_t *total) {
+  if (nsplit < 0 || nseg < 2 || nseg > 64) return FP_EINVAL;
+  if (p.B < 128) return FP_EUNSUPPORTED;
+  const long jobs = (long)p.Hkv * p.N, ns = nsplit < jobs ? nsplit : jobs;
+  const size_t units = (size_t)(jobs + ns * (nseg - 1)) * (p.B / 32);
+  *utab_off = align_up(p.total);
+  *part_off = align_up(*utab_off + sizeof(int4) * units);
+  *total = align_up(*part_off + sizeof(float) * (size_t)ns * nseg * attn_split_slot_floats(p));
+  return FP_OK;
+}
+
+int fp_attn_split_workspace_bytes(const fp_shape *shape, int nsplit, int nseg, size_t *bytes) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if (!bytes) return FP_EINVAL;
+  size_t uo, po;
+  return split_layout(p, nsplit, nseg, &uo, &po, bytes);
+}
+
+int fp_attn_split(const fp_shape *shape, const void *Q, const void *K, const void *V,
+                  const fp_index_out *csr, int nsplit, int nseg, void *O, void *ws, size_t ws_bytes,
+                  void *stream) {
+  Plan p;
+  int rc = make_plan(shape, &p);
+  if (rc) return rc;
+  if (!Q || !K || !V || !O || !csr || !csr->row_ptr || !csr->col_idx || !csr->job_ptr || !csr->job_blk ||
+      !csr->job_mask || !csr->job_order)
+    return FP_EINVAL;
+  size_t uo, po, total;
+  if ((rc = split_layout(p, nsplit, nseg, &uo, &po, &total))) return rc;
+  if (!ws || ws_bytes < total) return ws ? FP_EWORKSPACE : FP_EINVAL;
+  const Work w = carve(p, ws);
+  char *b = (char *)ws;
+  FP_LAUNCH(launch_attn(p, false, Q, nullptr, K, nullptr, V, nullptr, csr, O, w.bar + 32, (int4 *)(b + uo),
+                        (hipStream_t)stream, nsplit, nseg, (float *)(b + po)));
+  return FP_OK;
+}
+
 int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ, const int8_t *K8,
                const float *sK, const int8_t *V8, const float *sV, const fp_index_out *csr,
                void *O, void *ws, size_t ws_bytes, void *stream) {

@@ -82,9 +82,14 @@ hipError_t launch_status_init(int32_t *status, unsigned int *bar, hipStream_t st
 // Block-sparse attention over the CSR rows.
 // compute units of the current device (cached; 0 if the query fails)
 int cu_count();
+// nseg > 1: split-KV schedule of fp_attn_split (bf16, b >= 128): the nsplit longest jobs in nseg
+// segments each, partial rows in `part`, merged by a combine kernel.
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,
-                       void *O, unsigned int *ctr, int4 *utab, hipStream_t st);
+                       void *O, unsigned int *ctr, int4 *utab, hipStream_t st, int nsplit = 0,
+                       int nseg = 1, float *part = nullptr);
+// Partial-output floats per split slot (G heads x b rows x padded row).
+size_t attn_split_slot_floats(const Plan &p);
 // One exact int8 score tile through the W8A8 attention kernel's staging and tile code.
 hipError_t launch_probe_attn_i8(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int i,
                                 int j, int32_t *out, hipStream_t st);

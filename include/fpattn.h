@@ -271,6 +271,28 @@ int fp_attn(const fp_shape *shape, const void *Q, const void *K, const void *V,
             void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Split-KV schedule of the same attention ([E] 3.2: the attention unit walks
+ * KV blocks and accumulates each query block's partial result under its key
+ * until every consumer is served).  The nsplit longest jobs (the first
+ * nsplit of job_order; clamped to the job count) are cut into nseg segments
+ * of consecutive job-list entries; each segment runs as its own work unit and
+ * writes every row's unnormalised partial output with its running maximum
+ * and weight sum (m, l) to a slot keyed by (job, segment); a combine step
+ * then merges a job's slots, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+ * with M = max_s m_s, and writes bf16 O.  The other jobs run as in fp_attn.
+ * The result is fp_attn's up to floating-point rounding order.
+ *   nsplit >= 0, 2 <= nseg <= 64; bf16 only, b in {128, 256}
+ *   (FP_EUNSUPPORTED for b = 64); ws: at least
+ *   fp_attn_split_workspace_bytes(shape, nsplit, nseg) bytes.
+ * Arguments otherwise as fp_attn.  Errors: FP_EINVAL, FP_EUNSUPPORTED,
+ * FP_EWORKSPACE, FP_EHIP.
+ */
+int fp_attn_split_workspace_bytes(const fp_shape *shape, int nsplit, int nseg, size_t *bytes);
+int fp_attn_split(const fp_shape *shape, const void *Q, const void *K, const void *V,
+                  const fp_index_out *csr, int nsplit, int nseg, void *O,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/*
  * W8A8 block-sparse attention ([E] 3.3, 4.2; [R] 3.3).  Scores use the exact
  * int8 dot product scaled by sigma * sQ * sK; P.V uses bf16 P against the
  * int8 values of V (exact in bf16) with the per-token scale sV folded into P.

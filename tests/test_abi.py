@@ -203,3 +203,28 @@ def test_static_scratch_size_matches_header():
     # the 3B-shaped 128K layer fits with 64- and 128-token blocks
     for b in (64, 128):
         assert fpa.workspace_bytes(fpa.shape_of(131072, b, 24, 8), 0) <= fpa.binding.FP_STATIC_SCRATCH_BYTES
+
+
+@no_gpu_only
+def test_attn_split_rejects_bad_arguments():
+    L = fpa.lib()
+    P = ctypes.c_void_p(0x1000)
+    sh = fpa.shape_of(2048, 128, 4, 2)
+    o = _dummy_out(sh)
+    n = ctypes.c_size_t(0)
+    assert L.fp_attn_split_workspace_bytes(ctypes.byref(sh), 4, 2, ctypes.byref(n)) == fpa.FP_OK
+    need = n.value
+    assert need > fpa.workspace_bytes(sh)
+    assert L.fp_attn_split_workspace_bytes(ctypes.byref(sh), 4, 1, ctypes.byref(n)) == fpa.FP_EINVAL      # nseg < 2
+    assert L.fp_attn_split_workspace_bytes(ctypes.byref(sh), -1, 2, ctypes.byref(n)) == fpa.FP_EINVAL
+    b64 = fpa.shape_of(2048, 64, 4, 2)
+    assert L.fp_attn_split_workspace_bytes(ctypes.byref(b64), 4, 2, ctypes.byref(n)) == fpa.FP_EUNSUPPORTED
+    assert L.fp_attn_split(ctypes.byref(sh), P, P, P, ctypes.byref(o), 4, 2, P, P, need - 1, None) == fpa.FP_EWORKSPACE
+    assert L.fp_attn_split(ctypes.byref(sh), P, P, None, ctypes.byref(o), 4, 2, P, P, need, None) == fpa.FP_EINVAL
+    assert L.fp_attn_split(ctypes.byref(sh), P, P, P, ctypes.byref(o), 4, 65, P, P, 1 << 30, None) == fpa.FP_EINVAL
+    # the partial slots grow with the split jobs and segments, clamped to the job count
+    a = ctypes.c_size_t(0)
+    b = ctypes.c_size_t(0)
+    L.fp_attn_split_workspace_bytes(ctypes.byref(sh), 1 << 20, 2, ctypes.byref(a))
+    L.fp_attn_split_workspace_bytes(ctypes.byref(sh), 32, 2, ctypes.byref(b))     # 32 = Hkv * N jobs
+    assert a.value == b.value > need

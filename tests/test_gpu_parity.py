@@ -459,3 +459,32 @@ def test_block_uses_match_oracle():
         want_u, want_h = oi.block_uses(oi.IndexResult(S=c.S, b=c.b, Hq=c.Hq, Hkv=c.Hkv, heads=heads))
         np.testing.assert_array_equal(uses.cpu().numpy(), want_u)
         np.testing.assert_array_equal(head_uses.cpu().numpy(), want_h)
+
+
+# ------------------------------------------------------------------ split-KV schedule
+SPLIT_CASES = [("tiny-all-2", {}, 1 << 20, 2), ("tiny-4-3", {}, 4, 3), ("tiny-b256-G4-5", dict(S=2048, b=256, Hq=8, Hkv=2), 3, 5),
+               ("tiny-G8-all-4", dict(S=1024, Hq=8, Hkv=1), 1 << 20, 4), ("tiny-N37-16-2", dict(S=128 * 37), 16, 2),
+               ("tiny-g1-all-3", dict(gamma=1.0), 1 << 20, 3)]
+
+
+@pytest.mark.parametrize("name,kw,nsplit,nseg", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_attn_split_on_oracle_csr(name, kw, nsplit, nseg):
+    """fp_attn_split (split-KV segments merged by the keyed combine) against the oracle on the oracle's
+    CSR, and against fp_attn on the same index."""
+    say(f"attn split {name}: nsplit={nsplit} nseg={nseg}")
+    c = cfg(**kw)
+    L = gen.make(c)
+    Q, K, V = L.f32("q"), L.f32("k"), L.f32("v")
+    ref = oi.index(Q, K, c.b, c.gamma, c.tau)
+    rp, ci = ref.csr()
+    idx = fpa.build_jobs(fpa.shape_of(c.S, c.b, c.Hq, c.Hkv), P.dev(rp), P.dev(ci))
+    Qd, Kd, Vd = P.layer_on_device(L)
+    Os = fpa.attn_split(Qd, Kd, Vd, idx, nsplit, nseg)
+    Op = fpa.attn(Qd, Kd, Vd, idx)
+    torch.cuda.synchronize()
+    Oref = oracle.attn.attn(Q, K, V, rp, ci, c.b)
+    mx, rms = P.attn_errors(Os, Oref)
+    dmx = float((Os.float() - Op.float()).abs().max().item())
+    say(f"  maxabs={mx:.3e} rms={rms:.3e}; vs fp_attn maxabs {dmx:.3e}")
+    assert mx <= MAXABS and rms <= RMS, (mx, rms)
+    assert dmx <= MAXABS
