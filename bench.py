@@ -314,6 +314,60 @@ def split_kv_records(c, T, idx, steps, warmup, dev):
     return out
 
 
+def time_call(fn, steps: int, warmup: int) -> float:
+    """Median ms of fn() over `steps` calls timed with events on the current stream."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b_ in ev:
+        a.record(stream)
+        fn()
+        b_.record(stream)
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b_) for a, b_ in ev]))
+
+
+def projection_records(c, steps, warmup, dev, D=3072):
+    """The QKV projection with its fused epilogue (fp_qkv_project) at the layer's shape with a model
+    dimension D (Llama-3.2-3B: 3072), and the index stage fed its pooled queries (fp_index_pooled)
+    against fp_index on the same projected Q, K: the drop of the index stage once Q is not read back."""
+    import torch
+    import gen
+    import dynamic_block_sparse_flexprefill_amd as fpa
+    inp = gen.projection_inputs(c.S, D, c.Hq, c.Hkv, seed=0)
+    up = lambda u: torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).to(dev)
+    X, W = up(inp["x"]), up(inp["w"])
+    cos, sin = torch.from_numpy(inp["cos"]).to(dev), torch.from_numpy(inp["sin"]).to(dev)
+    del inp
+    out = {}
+    timed = lambda fn: time_call(fn, steps, warmup)
+    res = {}
+    t_bf = timed(lambda: fpa.qkv_project(X, W, c.Hq, c.Hkv, c.b, rope_cos=cos, rope_sin=sin, out=out))
+    res8 = {}
+    t_i8 = timed(lambda: fpa.qkv_project(X, W, c.Hq, c.Hkv, c.b, rope_cos=cos, rope_sin=sin, int8=True, out=res8))
+    del res8
+    flop = 2.0 * c.S * D * (c.Hq + 2 * c.Hkv) * c.d
+    res["workload"] = (f"Y = X W^T, X [{c.S}, {D}], W [{(c.Hq + 2 * c.Hkv) * c.d}, {D}] bf16, with rotary "
+                       f"embedding, head-major bf16 store and b={c.b} block means (plus int8 codes and scales)")
+    res["project_ms"] = round(t_bf, 4)
+    res["project_tflops"] = round(flop / (t_bf * 1e-3) / 1e12, 1)
+    res["project_frac_of_bf16_peak"] = round(flop / (t_bf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+    res["project_with_int8_ms"] = round(t_i8, 4)
+    sh = fpa.shape_of(c.S, c.b, c.Hq, c.Hkv)
+    ws = fpa.Workspace(sh, dev)
+    idx = fpa.Index.empty(sh, dev)
+    t_plain = timed(lambda: fpa.index(out["q"], out["k"], c.b, c.gamma, c.tau, out=idx, ws=ws))
+    t_pooled = timed(lambda: fpa.index_pooled(out["q"], out["k"], out["qbar"], c.b, c.gamma, c.tau, out=idx, ws=ws))
+    res["index_ms_reading_q"] = round(t_plain, 4)
+    res["index_ms_with_upstream_qbar"] = round(t_pooled, 4)
+    res["patterns"] = np.bincount(idx.pattern.cpu().numpy(), minlength=2).tolist()
+    del X, W, out, idx, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def reuse_stats(c, idx):
     """Key-block reuse from the device use counters (fp_block_uses): how often the query-major
     schedule stages each block against the once-per-block minimum."""
@@ -407,6 +461,8 @@ def main(argv=None):
         "parity": None,
         "other_layers": {},
         "split_kv": None,
+        "projection": None,
+        "index_with_upstream_qbar": None,
     }
 
     if not args.no_cpu:
@@ -429,6 +485,26 @@ def main(argv=None):
             rec["split_kv"] = split_kv_records(c, T, ix, args.steps, args.warmup, dev)
             log(f"[bench]   {rec['split_kv']}")
             del ix
+        if not c.int8 and c.b in (64, 128):
+            # the index stage fed pooled queries from upstream, on the planted layer itself: qbar is
+            # made here with a torch mean outside the timed region, standing in for what the
+            # projection epilogue emits (fp_qkv_project, timed below on random X, W)
+            qbar = T["q"].view(c.Hq, c.N, c.b, c.d).float().mean(dim=2).contiguous()
+            import dynamic_block_sparse_flexprefill_amd as fpa
+            sh = fpa.shape_of(c.S, c.b, c.Hq, c.Hkv)
+            ws_ = fpa.Workspace(sh, dev)
+            ix_ = fpa.Index.empty(sh, dev)
+            t_pl = time_call(lambda: fpa.index(T["q"], T["k"], c.b, c.gamma, c.tau, out=ix_, ws=ws_), args.steps, args.warmup)
+            t_po = time_call(lambda: fpa.index_pooled(T["q"], T["k"], qbar, c.b, c.gamma, c.tau, out=ix_, ws=ws_),
+                             args.steps, args.warmup)
+            rec["index_with_upstream_qbar"] = {"index_ms_reading_q": round(t_pl, 4), "index_ms_with_upstream_qbar": round(t_po, 4),
+                                               "patterns": np.bincount(ix_.pattern.cpu().numpy(), minlength=2).tolist()}
+            log(f"[bench] index stage with upstream pooled queries: {rec['index_with_upstream_qbar']}")
+            del T, qbar, ws_, ix_
+            torch.cuda.empty_cache()
+            log(f"[bench] QKV projection with the fused epilogue at {c.name}'s shape (D = 3072)")
+            rec["projection"] = projection_records(c, args.steps, args.warmup, dev)
+            log(f"[bench]   {rec['projection']}")
         for name in EXTRA_CONFIGS:
             if name == c.name:
                 continue

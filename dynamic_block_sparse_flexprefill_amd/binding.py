@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.fp_block_uses.argtypes = [sp, op, _P, _P, _P]
         L.fp_attn_split_workspace_bytes.argtypes = [sp, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
         L.fp_attn_split.argtypes = [sp, _P, _P, _P, op, ctypes.c_int, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]
+        L.fp_qkv_project.argtypes = [sp, ctypes.c_int] + [_P] * 16
+        L.fp_index_pooled.argtypes = [sp, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         lp = ctypes.POINTER(ctypes.c_int32)
         L.fp_index_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_attn_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
                                        ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_attn_split_workspace_bytes", "fp_attn_split", "fp_index_batch", "fp_attn_batch",
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_attn_split_workspace_bytes", "fp_attn_split", "fp_qkv_project", "fp_index_pooled", "fp_index_batch", "fp_attn_batch",
                      "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -279,6 +281,55 @@ def _index_variant(fn: str, Q, K, b, gamma, tau, sQ, sK, stats, out, ws, stream)
                             _stream(stream))
     if rc:
         raise FpError(rc, fn)
+    return out
+
+
+def qkv_project(X: torch.Tensor, W: torch.Tensor, Hq: int, Hkv: int, b: int, *, rope_cos=None, rope_sin=None,
+                pooled: bool = True, int8: bool = False, out=None, stream=None) -> dict:
+    """fp_qkv_project: Q, K, V (bf16, head-major) = rotary(X W^T) split by heads, with the block means
+    qbar / kbar (pooled=True) and the per-(head, token) int8 codes and scales (int8=True) from the
+    same epilogue.  X: bf16 [S, D]; W: bf16 [(Hq + 2 Hkv) * 128, D]; rope tables fp32 [S, 64]."""
+    S, D = X.shape
+    d = 128
+    _check(X, "X", torch.bfloat16, (S, D))
+    _check(W, "W", torch.bfloat16, ((Hq + 2 * Hkv) * d, D))
+    if rope_cos is not None:
+        _check(rope_cos, "rope_cos", torch.float32, (S, d // 2))
+        _check(rope_sin, "rope_sin", torch.float32, (S, d // 2))
+    dev = X.device
+    o = {} if out is None else out
+    mk = lambda key, shp, dt: o.setdefault(key, torch.empty(*shp, dtype=dt, device=dev))
+    Q, K, V = mk("q", (Hq, S, d), torch.bfloat16), mk("k", (Hkv, S, d), torch.bfloat16), mk("v", (Hkv, S, d), torch.bfloat16)
+    qb = mk("qbar", (Hq, S // b, d), torch.float32) if pooled else None
+    kb = mk("kbar", (Hkv, S // b, d), torch.float32) if pooled else None
+    i8 = [mk("q8", (Hq, S, d), torch.int8), mk("sq", (Hq, S), torch.float32), mk("k8", (Hkv, S, d), torch.int8),
+          mk("sk", (Hkv, S), torch.float32), mk("v8", (Hkv, S, d), torch.int8),
+          mk("sv", (Hkv, S), torch.float32)] if int8 else [None] * 6
+    shape = shape_of(S, b, Hq, Hkv, d)
+    rc = lib().fp_qkv_project(ctypes.byref(shape), D, _ptr(X), _ptr(W), _ptr(rope_cos), _ptr(rope_sin), _ptr(Q),
+                              _ptr(K), _ptr(V), _ptr(qb), _ptr(kb), *[_ptr(t) for t in i8], _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_qkv_project")
+    return o
+
+
+def index_pooled(Q: torch.Tensor, K: torch.Tensor, qbar: torch.Tensor, b: int, gamma: float, tau: float, *,
+                 stats: bool = False, out: Optional[Index] = None, ws: Optional[Workspace] = None,
+                 stream=None) -> Index:
+    """fp_index_pooled: fp_index with the pooled query blocks qbar (fp32 [Hq, N, 128]) from upstream."""
+    Hq, S, d = Q.shape
+    Hkv = K.shape[0]
+    shape = shape_of(S, b, Hq, Hkv, d)
+    _check(Q, "Q", torch.bfloat16, (Hq, S, d))
+    _check(K, "K", torch.bfloat16, (Hkv, S, d))
+    _check(qbar, "qbar", torch.float32, (Hq, S // b, d))
+    out = Index.empty(shape, Q.device, stats=stats) if out is None else out
+    ws = _ws(shape, ws, Q.device)
+    o = out.c_struct()
+    rc = lib().fp_index_pooled(ctypes.byref(shape), _ptr(Q), _ptr(K), _ptr(qbar), gamma, tau, ctypes.byref(o),
+                               _ptr(ws.buf), ws.nbytes, _stream(stream))
+    if rc:
+        raise FpError(rc, "fp_index_pooled")
     return out
 
 

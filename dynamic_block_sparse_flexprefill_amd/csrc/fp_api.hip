@@ -143,7 +143,7 @@ int64_t fp_job_capacity(const fp_shape *shape) {
 static int index_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
                         const void *K, const float *sK, float gamma, float tau,
                         fp_index_out *out, void *ws, size_t ws_bytes, void *stream,
-                        bool two_pass = false, bool share = false) {
+                        bool two_pass = false, bool share = false, const float *qbar_in = nullptr) {
   Plan p;
   int rc = make_plan(shape, &p);
   if (rc) return rc;
@@ -157,7 +157,7 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   bool have_pe = false;
   FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st, two_pass, &have_pe));
   FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, have_pe));
-  FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st));
+  FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st, qbar_in));
   FP_LAUNCH(launch_rows_and_jobs(p, out, w, st, share));
   return FP_OK;
 }
@@ -203,6 +203,30 @@ int fp_index_static(const fp_shape *shape, const void *Q, const void *K, float g
   if (!ws) return FP_EHIP;
   return index_common(shape, false, Q, nullptr, K, nullptr, gamma, tau, out, ws, FP_STATIC_SCRATCH_BYTES,
                       stream);
+}
+
+int fp_index_pooled(const fp_shape *shape, const void *Q, const void *K, const float *qbar, float gamma,
+                    float tau, fp_index_out *out, void *ws, size_t ws_bytes, void *stream) {
+  if (!qbar) return FP_EINVAL;
+  return index_common(shape, false, Q, nullptr, K, nullptr, gamma, tau, out, ws, ws_bytes, stream, false, false,
+                      qbar);
+}
+
+int fp_qkv_project(const fp_shape *shape, int D, const void *X, const void *W, const float *rope_cos,
+                   const float *rope_sin, void *Q, void *K, void *V, float *qbar, float *kbar, int8_t *Q8,
+                   float *sQ, int8_t *K8, float *sK, int8_t *V8, float *sV, void *stream) {
+  if (!shape) return FP_EINVAL;
+  const fp_shape &s = *shape;
+  if (s.S <= 0 || s.Hq <= 0 || s.Hkv <= 0 || s.Hq % s.Hkv != 0 || D <= 0 || s.b <= 0) return FP_EINVAL;
+  if (!X || !W || !Q || !K || !V || (!rope_cos) != (!rope_sin)) return FP_EINVAL;
+  const bool any8 = Q8 || sQ || K8 || sK || V8 || sV, all8 = Q8 && sQ && K8 && sK && V8 && sV;
+  if (any8 && !all8) return FP_EINVAL;
+  if (s.d != 128 || s.S % 128 != 0 || D % 64 != 0) return FP_EUNSUPPORTED;
+  if ((qbar || kbar) && s.b != 64 && s.b != 128) return FP_EUNSUPPORTED;
+  if ((long)s.S * D >= (1L << 31) || (long)(s.Hq + 2 * s.Hkv) * 128 * D >= (1L << 31)) return FP_EUNSUPPORTED;
+  FP_LAUNCH(launch_qkv_proj(s.S, D, s.Hq, s.Hkv, s.b, X, W, rope_cos, rope_sin, Q, K, V, qbar, kbar, Q8, sQ, K8, sK,
+                            V8, sV, (hipStream_t)stream));
+  return FP_OK;
 }
 
 int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const float *sQ,

@@ -65,8 +65,14 @@ hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float
                               float gamma, float tau, const fp_index_out *out,
                               const Work &w, hipStream_t st, bool have_pe);
 // Query-aware rows: pooled queries of every block against pooled keys.
+// qbar_in (or NULL): pooled queries [Hq][N][128] from the caller, so Q is not read.
 hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
-                        const uint8_t *pattern, const Work &w, hipStream_t st);
+                        const uint8_t *pattern, const Work &w, hipStream_t st, const float *qbar_in = nullptr);
+// QKV projection Y = X W^T with the fused epilogue (rotation, bf16 head-major store, block means,
+// optional int8 codes and scales); see qkv_proj.hip.
+hipError_t launch_qkv_proj(int S, int D, int Hq, int Hkv, int b, const void *X, const void *W, const float *cosT,
+                           const float *sinT, void *Q, void *K, void *V, float *qbar, float *kbar, int8_t *Q8,
+                           float *sQ, int8_t *K8, float *sK, int8_t *V8, float *sV, hipStream_t st);
 // Row bit sets -> CSR rows, grouped-query job list and its work order.
 // share: heads of a KV group with the same pattern take the union of their rows.
 hipError_t launch_rows_and_jobs(const Plan &p, const fp_index_out *out, const Work &w,

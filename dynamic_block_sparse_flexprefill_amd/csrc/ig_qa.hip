@@ -146,7 +146,9 @@ __device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev,
 // Used while 16 rows of logits fit in LDS (N <= 2048); WIDE (N > 1024) selects rows
 // of up to 2048 blocks in registers.
 constexpr int kQa16Threads = 512;
-template <int B, bool I8, bool WIDE>
+// PRE: the pooled queries come from the caller (a.qbar, [Hq][N][128], e.g. from the projection
+// epilogue) instead of being pooled here from Q.
+template <int B, bool I8, bool WIDE, bool PRE>
 __global__ void __launch_bounds__(kQa16Threads) k_qa_rows16(QaArgs a) {
   const int h = blockIdx.y;
   if (a.pattern[h] != FP_PATTERN_QUERY_AWARE) return;
@@ -160,7 +162,10 @@ __global__ void __launch_bounds__(kQa16Threads) k_qa_rows16(QaArgs a) {
   uint32_t *words = (uint32_t *)(qs + 16 * 128);      // [8 waves][nw32]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, q = lane >> 4, rl = lane & 15;
 
-  {
+  if constexpr (PRE) {
+    for (int k = threadIdx.x; k < rows * 32; k += kQa16Threads)
+      ((float4 *)qs)[k] = ((const float4 *)(a.qbar + ((size_t)h * N + i0) * 128))[k];
+  } else {
     using PG = PoolGeo<B, I8>;
     const int ch = lane % PG::CPR, rr = lane / PG::CPR;
     for (int r = wave; r < rows; r += kQa16Threads / 64) {
@@ -259,25 +264,25 @@ hipError_t run_pool(const Plan &p, const PoolArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int B, bool I8, bool WIDE>
+template <int B, bool I8, bool WIDE, bool PRE>
 hipError_t launch_qa16(const Plan &p, const QaArgs &a, hipStream_t st) {
   const size_t lds = sizeof(float) * ((size_t)16 * p.N + 16 * 128) + sizeof(uint32_t) * 8 * p.nw32;
-  const void *fn = (const void *)k_qa_rows16<B, I8, WIDE>;
+  const void *fn = (const void *)k_qa_rows16<B, I8, WIDE, PRE>;
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_qa_rows16<B, I8, WIDE>), dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
+  hipLaunchKernelGGL((k_qa_rows16<B, I8, WIDE, PRE>), dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
   return hipGetLastError();
 }
 
-template <int B, bool I8>
+template <int B, bool I8, bool PRE = false>
 hipError_t run_qa16(const Plan &p, const QaArgs &a, hipStream_t st) {
-  return p.N > 1024 ? launch_qa16<B, I8, true>(p, a, st) : launch_qa16<B, I8, false>(p, a, st);
+  return p.N > 1024 ? launch_qa16<B, I8, true, PRE>(p, a, st) : launch_qa16<B, I8, false, PRE>(p, a, st);
 }
 
 }  // namespace
 
 hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, float gamma,
-                        const uint8_t *pattern, const Work &w, hipStream_t st) {
+                        const uint8_t *pattern, const Work &w, hipStream_t st, const float *qbar_in) {
   QaArgs a;
   a.Q = (const uint8_t *)Q;
   a.sQ = sQ;
@@ -289,6 +294,19 @@ hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, 
   a.qbar = w.qbar;
   a.kbar = w.kbar;
   a.rowbits = w.rowbits;
+  if (qbar_in) {   // pooled queries from the caller: no read of Q at all
+    a.qbar = qbar_in;
+    if (p.N <= 2048) {
+      if (p.B == 64) return run_qa16<64, false, true>(p, a, st);
+      if (p.B == 128) return run_qa16<128, false, true>(p, a, st);
+      return run_qa16<256, false, true>(p, a, st);
+    }
+    const size_t lds = sizeof(float) * ((size_t)a.R * p.N + a.R * 128) + sizeof(uint32_t) * 4 * p.nw32;
+    hipError_t e = hipFuncSetAttribute((const void *)k_qa_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_qa_rows, dim3((p.N + a.R - 1) / a.R, p.Hq), dim3(kQaThreads), lds, st, a);
+    return hipGetLastError();
+  }
   if (p.N <= 2048) {   // pooling fused into the row kernel
     if (p.B == 64) return i8 ? run_qa16<64, true>(p, a, st) : run_qa16<64, false>(p, a, st);
     if (p.B == 128) return i8 ? run_qa16<128, true>(p, a, st) : run_qa16<128, false>(p, a, st);

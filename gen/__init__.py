@@ -14,4 +14,6 @@ from .planted import (  # noqa: F401
     bf16_bits_from_f32,
     f32_from_bf16_bits,
     quantize_rows,
+    rope_tables,
+    projection_inputs,
 )

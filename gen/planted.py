@@ -225,3 +225,19 @@ def make(cfg, seed: int = 0) -> Layer:
     kb = _bf16_bits_fast(k)
     vb = _bf16_bits_fast(v)
     return Layer(cfg=cfg, seed=seed, q=qb, k=kb, v=vb, planted=planted, spikes=spikes)
+
+
+def rope_tables(S: int, d: int = 128, base: float = 500000.0):
+    """The rotary embedding's cos / sin tables [S, d/2] (float32) for positions 0..S-1."""
+    return _rope_tables(S, d, base)
+
+
+def projection_inputs(S: int, D: int, Hq: int, Hkv: int, seed: int = 0, d: int = 128):
+    """Seeded inputs of a QKV projection: X [S, D] ~ N(0, 1) and W [(Hq + 2 Hkv) * d, D] ~ N(0, 1/D)
+    (so every projected value is about N(0, 1)), both rounded to bf16 (uint16 bit patterns), and the
+    rotary tables [S, d/2] (float32, base 500000)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = rng.standard_normal((S, D), dtype=np.float32)
+    W = rng.standard_normal(((Hq + 2 * Hkv) * d, D), dtype=np.float32) * np.float32(1.0 / math.sqrt(D))
+    cos, sin = _rope_tables(S, d, 500000.0)
+    return {"x": _bf16_bits_fast(X), "w": _bf16_bits_fast(W), "cos": cos, "sin": sin}

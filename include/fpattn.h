@@ -217,6 +217,54 @@ int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const f
                       fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * The QKV projection that precedes the path, with the later stages' pooling
+ * and quantisation fused into its epilogue ([E] 1.1: Q, K, V are
+ * projections of the input; [E] 3.1: one fused streaming pipeline; [E] 3.3,
+ * 4.2: W8A8 activations).  Y = X W^T on the bf16 matrix cores with fp32
+ * accumulation, then per 128-token x 128-column output tile (one head):
+ *   - the rotary embedding on the Q and K heads (rotate-half pairs (c, c+64):
+ *     y_c' = y_c cos - y_{c+64} sin, y_{c+64}' = y_{c+64} cos + y_c sin);
+ *   - rounding to bf16 (nearest even) and the head-major store;
+ *   - qbar / kbar (or NULL): the fp32 mean of each b-token block of the
+ *     rounded Q / K values, i.e. the pooled vectors fp_index would otherwise
+ *     compute by reading Q and K back (fp_index_pooled takes qbar);
+ *   - optionally Q8/sQ, K8/sK, V8/sV: symmetric per-(head, token) int8 codes
+ *     of the rounded values, s = max|x| / 127 (1 for a zero row), codes
+ *     rint(x / s) clamped to +-127, fp32 arithmetic (the inputs of
+ *     fp_index_i8 / fp_attn_i8); all six NULL or all six set.
+ *   shape: S, b, Hq, Hkv, d of the layer (d = 128; S a multiple of 128;
+ *          b in {64, 128} when qbar or kbar is requested);
+ *   D: model dimension, a positive multiple of 64;
+ *   X: device bf16 [S, D];  W: device bf16 [(Hq + 2 Hkv) * 128, D], rows in
+ *      the order Q heads, K heads, V heads (row h*128 + c is output column c
+ *      of head h);
+ *   rope_cos, rope_sin: device fp32 [S, 64] (position t, frequency c), or
+ *      both NULL for no rotation;
+ *   Q: device bf16 [Hq, S, 128]; K, V: device bf16 [Hkv, S, 128];
+ *   qbar: device fp32 [Hq, S / b, 128]; kbar: device fp32 [Hkv, S / b, 128];
+ *   Q8: device int8 [Hq, S, 128], sQ: fp32 [Hq, S]; K8, V8, sK, sV likewise
+ *      over Hkv.
+ * Errors: FP_EINVAL (null or inconsistent pointers, non-positive sizes,
+ * Hq % Hkv != 0), FP_EUNSUPPORTED (d, S, D or b outside the above, or an
+ * operand of 2^31 elements or more), FP_EHIP.
+ */
+int fp_qkv_project(const fp_shape *shape, int D, const void *X, const void *W,
+                   const float *rope_cos, const float *rope_sin, void *Q, void *K, void *V,
+                   float *qbar, float *kbar, int8_t *Q8, float *sQ, int8_t *K8, float *sK,
+                   int8_t *V8, float *sV, void *stream);
+
+/*
+ * fp_index with the pooled query blocks supplied by the caller (for example
+ * by fp_qkv_project's epilogue): qbar is device fp32 [Hq, N, 128], the mean
+ * of each block of b queries of each head.  The query-aware rows then score
+ * qbar against the pooled keys without reading Q; Q is read only for the
+ * last query block.  Otherwise as fp_index (bf16); FP_EINVAL if qbar is NULL.
+ */
+int fp_index_pooled(const fp_shape *shape, const void *Q, const void *K, const float *qbar,
+                    float gamma, float tau, fp_index_out *out,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/*
  * Head-pattern sharing ([R] 5, item 1: compress the sparse pattern by letting
  * similar heads share one).  As fp_index (variant 0; sQ, sK ignored) or
  * fp_index_i8 (variant 1), except that every query head h of KV group g gets

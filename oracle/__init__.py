@@ -14,5 +14,7 @@ Modules:
   index  -- last-block statistics, divergence test, cumulative selection, CSR rows
   attn   -- block-sparse causal attention over a CSR (bf16-valued and W8A8 inputs)
   brute  -- independent brute-force forms used only to pin the two modules above
+  project -- the QKV projection with the rotary embedding, block means and int8 codes its
+             epilogue emits
 """
-from . import index, attn, brute  # noqa: F401
+from . import index, attn, brute, project  # noqa: F401
