@@ -26,7 +26,7 @@ FP_EHIP = -5
 FP_EJOBCAPACITY = -6
 FP_ETIMEOUT = -7
 FP_ESCRATCH = -8
-FP_STATIC_SCRATCH_BYTES = 32 << 20    # include/fpattn.h
+FP_STATIC_SCRATCH_BYTES = 64 << 20    # include/fpattn.h
 FP_STATUS_CSR_OVERFLOW = 1
 FP_STATUS_JOB_OVERFLOW = 2
 FP_STATUS_WAIT_TIMEOUT = 4
@@ -82,7 +82,6 @@ def lib() -> ctypes.CDLL:
         L.fp_attn.argtypes = [sp, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
         L.fp_attn_i8.argtypes = [sp, _P, _P, _P, _P, _P, _P, op, _P, _P, ctypes.c_size_t, _P]
         L.fp_probe_qk_i8.argtypes = [sp, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]
-        L.fp_index_two_pass.argtypes = [sp, ctypes.c_int, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_index_static.argtypes = [sp, _P, _P, f, f, op, _P]
         L.fp_index_shared.argtypes = [sp, ctypes.c_int, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_block_uses.argtypes = [sp, op, _P, _P, _P]
@@ -97,7 +96,7 @@ def lib() -> ctypes.CDLL:
         L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
                                        ctypes.c_size_t, _P]
         for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
-                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_two_pass", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_attn_split_workspace_bytes", "fp_attn_split", "fp_qkv_project", "fp_index_pooled", "fp_index_batch", "fp_attn_batch",
+                     "fp_attn_i8", "fp_probe_qk_i8", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_attn_split_workspace_bytes", "fp_attn_split", "fp_qkv_project", "fp_index_pooled", "fp_index_batch", "fp_attn_batch",
                      "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -340,13 +339,6 @@ def index_shared(Q, K, b: int, gamma: float, tau: float, *, sQ=None, sK=None, st
     return _index_variant("fp_index_shared", Q, K, b, gamma, tau, sQ, sK, stats, out, ws, stream)
 
 
-def index_two_pass(Q, K, b: int, gamma: float, tau: float, *, sQ=None, sK=None, stats: bool = False,
-                   out: Optional[Index] = None, ws: Optional[Workspace] = None, stream=None) -> Index:
-    """fp_index_two_pass: fp_index (bf16 Q, K) or fp_index_i8 (int8 Q, K with scales sQ, sK) with the
-    last-block statistics forced onto their two-pass form (a test entry point)."""
-    return _index_variant("fp_index_two_pass", Q, K, b, gamma, tau, sQ, sK, stats, out, ws, stream)
-
-
 def block_uses(idx: Index, *, heads: bool = True, stream=None):
     """fp_block_uses: (uses, head_uses) int32 [Hkv, N] -- job entries and (head, query block) pairs
     per key block of each KV group (head_uses is None when heads is False)."""
@@ -359,6 +351,7 @@ def block_uses(idx: Index, *, heads: bool = True, stream=None):
     if rc:
         raise FpError(rc, "fp_block_uses")
     return uses, hu
+
 
 
 def build_jobs(shape: FpShape, row_ptr: torch.Tensor, col_idx: torch.Tensor, *,

@@ -142,19 +142,6 @@ static_assert(kChunkDl == 128, "the scale load covers 128 keys");
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-// One direct load: the 64 lanes' 16 B from g fill LDS bytes [lds, lds + 1024).
-// Issued from inline assembly: the compiler then neither tracks the LDS write
-// (so it inserts no wait for it before unrelated LDS reads) nor reuses M0; the
-// caller waits for vmcnt(0) before the barrier that publishes the buffer.
-__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_u8 *)p);
-}
 
 // Issue this wave's share of the direct loads of one chunk (rows from kg/vg).
 __device__ __forceinline__ void dl_issue(const uint8_t *kg, const uint8_t *vg, uint32_t kb, uint32_t vb,
@@ -258,9 +245,6 @@ __device__ __forceinline__ void widen_v8(const uint8_t *vs, uint32_t *vt32) {
   }
 }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as a builtin
-// so that the compiler's own wait placement knows of it.
-constexpr int kWaitVm0 = 0x0f70;
 
 // An LDS byte address the compiler cannot fold constants into (keeps the
 // per-read offsets small enough for the instruction's immediate field).

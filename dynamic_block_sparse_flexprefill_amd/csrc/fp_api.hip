@@ -28,16 +28,13 @@ int make_plan(const fp_shape *s, Plan *p) {
   p->S = s->S; p->B = s->b; p->Hq = s->Hq; p->Hkv = s->Hkv; p->d = s->d;
   p->N = N; p->G = G;
   p->nw32 = (N + 31) / 32;
-  // About two statistics workgroups per compute unit (256 CUs) in total.
-  int nch = (512 + s->Hkv - 1) / s->Hkv;
-  if (nch > N) nch = N;
-  if (nch < 1) nch = 1;
-  p->cpb = (N + nch - 1) / nch;
-  p->nch = (N + p->cpb - 1) / p->cpb;
+  p->nch = stats_chunks(s->b, G, N);
   size_t o = 0;
   const size_t Hq = s->Hq, Hkv = s->Hkv, B = s->b;
-  p->off_part = o;   o = align_up(o + sizeof(float2) * Hq * B * p->nch);
+  p->off_lohi = o;   o = align_up(o + sizeof(float2) * Hq * (size_t)N * B);
+  p->off_ml = o;     o = align_up(o + sizeof(float2) * Hq * B * p->nch);
   p->off_rowml = o;  o = align_up(o + sizeof(float2) * Hq * B);
+  p->off_qlast = o;  o = align_up(o + sizeof(float) * Hq * 128);
   p->off_lo = o;     o = align_up(o + sizeof(float) * Hq * N);
   p->off_hi = o;     o = align_up(o + sizeof(float) * Hq * N);
   p->off_kbar = o;   o = align_up(o + sizeof(float) * Hkv * N * 128);
@@ -57,8 +54,10 @@ int make_plan(const fp_shape *s, Plan *p) {
 Work carve(const Plan &p, void *ws) {
   char *b = (char *)ws;
   Work w;
-  w.part = (float2 *)(b + p.off_part);
+  w.lohi = (float2 *)(b + p.off_lohi);
+  w.ml = (float2 *)(b + p.off_ml);
   w.rowml = (float2 *)(b + p.off_rowml);
+  w.qlast = (float *)(b + p.off_qlast);
   w.lo = (float *)(b + p.off_lo);
   w.hi = (float *)(b + p.off_hi);
   w.kbar = (float *)(b + p.off_kbar);
@@ -143,7 +142,7 @@ int64_t fp_job_capacity(const fp_shape *shape) {
 static int index_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
                         const void *K, const float *sK, float gamma, float tau,
                         fp_index_out *out, void *ws, size_t ws_bytes, void *stream,
-                        bool two_pass = false, bool share = false, const float *qbar_in = nullptr) {
+                        bool share = false, const float *qbar_in = nullptr) {
   Plan p;
   int rc = make_plan(shape, &p);
   if (rc) return rc;
@@ -153,10 +152,9 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   Work w = carve(p, ws);
-  FP_LAUNCH(launch_status_init(out->status, w.bar, st));
-  bool have_pe = false;
-  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, out->status, st, two_pass, &have_pe));
-  FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, have_pe));
+  FP_LAUNCH(launch_status_init(out->status, nullptr, st));
+  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, st));
+  FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, true));
   FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st, qbar_in));
   FP_LAUNCH(launch_rows_and_jobs(p, out, w, st, share));
   return FP_OK;
@@ -208,8 +206,7 @@ int fp_index_static(const fp_shape *shape, const void *Q, const void *K, float g
 int fp_index_pooled(const fp_shape *shape, const void *Q, const void *K, const float *qbar, float gamma,
                     float tau, fp_index_out *out, void *ws, size_t ws_bytes, void *stream) {
   if (!qbar) return FP_EINVAL;
-  return index_common(shape, false, Q, nullptr, K, nullptr, gamma, tau, out, ws, ws_bytes, stream, false, false,
-                      qbar);
+  return index_common(shape, false, Q, nullptr, K, nullptr, gamma, tau, out, ws, ws_bytes, stream, false, qbar);
 }
 
 int fp_qkv_project(const fp_shape *shape, int D, const void *X, const void *W, const float *rope_cos,
@@ -229,19 +226,11 @@ int fp_qkv_project(const fp_shape *shape, int D, const void *X, const void *W, c
   return FP_OK;
 }
 
-int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const float *sQ,
-                      const void *K, const float *sK, float gamma, float tau, fp_index_out *out,
-                      void *ws, size_t ws_bytes, void *stream) {
-  if (variant != 0 && variant != 1) return FP_EINVAL;
-  return index_common(shape, variant == 1, Q, sQ, K, sK, gamma, tau, out, ws, ws_bytes, stream, true);
-}
-
 int fp_index_shared(const fp_shape *shape, int variant, const void *Q, const float *sQ,
                     const void *K, const float *sK, float gamma, float tau, fp_index_out *out,
                     void *ws, size_t ws_bytes, void *stream) {
   if (variant != 0 && variant != 1) return FP_EINVAL;
-  return index_common(shape, variant == 1, Q, sQ, K, sK, gamma, tau, out, ws, ws_bytes, stream, false,
-                      true);
+  return index_common(shape, variant == 1, Q, sQ, K, sK, gamma, tau, out, ws, ws_bytes, stream, true);
 }
 
 int fp_block_uses(const fp_shape *shape, const fp_index_out *jobs, int32_t *uses, int32_t *head_uses,

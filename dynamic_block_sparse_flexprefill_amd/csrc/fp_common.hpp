@@ -66,6 +66,27 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // the attention.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- direct-to-LDS loads
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// One direct load: the 64 lanes' 16 B from g fill LDS bytes [lds, lds + 1024),
+// lane L writing bytes [16 L, 16 L + 16).  Issued from inline assembly: the
+// compiler then neither tracks the LDS write (so it inserts no wait for it
+// before unrelated LDS reads) nor reuses M0; the caller waits for vmcnt(0)
+// before the barrier that publishes the buffer.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+// Wave-uniform LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(const lds_u8 *)p);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima), as a builtin
+// so that the compiler's own wait placement knows of it.
+constexpr int kWaitVm0 = 0x0f70;
+
 // ---------------------------------------------------------------- reductions
 // Butterfly partners without LDS traffic: steps 0-3 are DPP moves inside each
 // 16-lane row (lane ^ 1, lane ^ 2, then the mirrors i <-> 7 - i and

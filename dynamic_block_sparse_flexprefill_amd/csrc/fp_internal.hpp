@@ -14,11 +14,12 @@ namespace fp {
 struct Plan {
   int S, B, Hq, Hkv, d, N, G;
   int nw32;          // 32-bit words per row bitmask: ceil(N / 32)
-  int nch;           // key-block chunks per KV group in the statistics pass
-  int cpb;           // key blocks per chunk: ceil(N / nch)
+  int nch;           // key-block chunks of the statistics (stats_chunks)
   // workspace layout (byte offsets from the workspace base)
-  size_t off_part;   // float2 [Hq*B*nch]  per-chunk row (max, sum) partials
-  size_t off_rowml;  // float2 [Hq*B]      per-row (max, sum) of the last block
+  size_t off_lohi;   // float2 [Hq*N*B]    per-(row, key block) split sums of the statistics
+  size_t off_ml;     // float2 [Hq*nch*B]  per-(row, chunk) (reference max, sum)
+  size_t off_rowml;  // float2 [Hq*B]      per-row (max, 1 / (b * sum))
+  size_t off_qlast;  // float  [Hq*128]    mean of each head's last query block
   size_t off_lo;     // float  [Hq*N]      lower-split block mass
   size_t off_hi;     // float  [Hq*N]      upper-split block mass
   size_t off_kbar;   // float  [Hkv*N*d]   mean-pooled key blocks
@@ -27,8 +28,7 @@ struct Plan {
   size_t off_qbar;   // float  [Hq*N*d]    mean-pooled query blocks (query-aware heads)
   size_t off_pe;     // float  [Hq*N]      pooled-estimate logits sigma * qbar_last . kbar_j
   size_t off_jwork;  // int32  [Hkv*N]     work per grouped job
-  size_t off_bar;    // u32    [64]        [0]: grid-barrier counter of the single-pass statistics;
-                     //                     [32]: unit counter of the persistent attention kernel
+  size_t off_bar;    // u32    [64]        [32]: unit counter of the persistent attention kernel
   size_t off_jkeys;  // u64    [Hkv*N]     per-group sorted job keys
   size_t off_utab;   // int4   [Hkv*N*b/32] attention work units {job, first entry, chunks, start}
   size_t total;
@@ -39,7 +39,8 @@ int make_plan(const fp_shape *s, Plan *p);
 
 // Typed views of the workspace.
 struct Work {
-  float2 *part, *rowml;
+  float2 *lohi, *ml, *rowml;
+  float *qlast;
   float *lo, *hi, *kbar;
   uint32_t *sel, *rowbits;
   float *qbar;
@@ -52,13 +53,12 @@ struct Work {
 Work carve(const Plan &p, void *ws);
 
 // ---- launchers: each returns hipSuccess or the launch error.
-// Statistics of the last query block against every key block
-// (two passes over K: row max / sum, then block mass).
-// two_pass: use the two-pass form even where the single pass fits (test entry point).
-// *have_pe: whether the statistics also wrote the pooled-estimate logits (w.pe).
+// Key-block chunks of the statistics for a shape (chunk boundaries depend on the shape only).
+int stats_chunks(int B, int G, int N);
+// Statistics of the last query block against every key block (K streamed once), then merged:
+// lo, hi, kbar and the pooled-estimate logits pe in the workspace.
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ,
-                           const void *K, const float *sK, const Work &w, int32_t *status,
-                           hipStream_t st, bool two_pass, bool *have_pe);
+                           const void *K, const float *sK, const Work &w, hipStream_t st);
 // Per head: pooled estimate, divergence, pattern, vertical / slash selection.
 // have_pe: the pooled-estimate logits are in w.pe (else they are computed here).
 hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,

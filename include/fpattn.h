@@ -45,13 +45,10 @@
  *    capacity exceeded) cannot be known on the host: the kernels set bits in
  *    the device status word (fp_index_out.status) and stop writing past the
  *    capacity; read it after the stream synchronises.
- *  - Identical inputs on the same device configuration give bit-identical
- *    outputs (no floating-point atomics).  The statistics of fp_index split
- *    the key blocks into one chunk per compute unit and KV group, and use the
- *    single-pass form only where its partials fit in LDS at one workgroup per
- *    compute unit; both follow the device's CU count, so results from devices
- *    with different CU counts can differ in the last bits of v, sl and p (and,
- *    where that moves a selection boundary, in the index sets).
+ *  - Identical inputs give bit-identical outputs (no floating-point atomics),
+ *    on any device: the statistics of fp_index cut the key blocks into
+ *    chunks whose boundaries depend on the shape only, whatever number of
+ *    workgroups runs them.
  *  - Supported shapes: d = 128; b in {64, 128, 256}; S a positive multiple
  *    of b with S / b <= 8192; Hq a multiple of Hkv; G <= 16 and G * b <= 2048
  *    where G = Hq / Hkv; gamma in (0, 1]; tau >= 0.
@@ -73,13 +70,13 @@ extern "C" {
 #define FP_ECAPACITY    (-4) /* (device status bit 1) CSR capacity exceeded */
 #define FP_EHIP         (-5) /* a HIP launch or query failed */
 #define FP_EJOBCAPACITY (-6) /* (device status bit 2) job-list capacity exceeded */
-#define FP_ETIMEOUT     (-7) /* (device status bit 3) a bounded device-side wait gave up */
+#define FP_ETIMEOUT     (-7) /* (device status bit 3, no longer set) a bounded device-side wait gave up */
 #define FP_ESCRATCH     (-8) /* fp_index_static: shape needs more than FP_STATIC_SCRATCH_BYTES */
 
 /* Device status word bits (fp_index_out.status[0]); 0 = success. */
 #define FP_STATUS_CSR_OVERFLOW 1u
 #define FP_STATUS_JOB_OVERFLOW 2u
-#define FP_STATUS_WAIT_TIMEOUT 4u
+#define FP_STATUS_WAIT_TIMEOUT 4u   /* reserved: no kernel waits on another workgroup */
 
 /* Pattern codes written to fp_index_out.pattern ([E] 1.2, [R] 1.1). */
 #define FP_PATTERN_VERTICAL_SLASH 0
@@ -190,7 +187,7 @@ int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
  * process ends, instead of a caller workspace.  The call itself allocates
  * nothing and calls no allocating routine.  Arguments, outputs and errors
  * as fp_index, plus FP_ESCRATCH (nothing enqueued) when
- * fp_workspace_bytes(shape, 0) exceeds FP_STATIC_SCRATCH_BYTES (32 MiB covers
+ * fp_workspace_bytes(shape, 0) exceeds FP_STATIC_SCRATCH_BYTES (64 MiB covers
  * the 3B-shaped layer at S = 131072 with b = 64 or 128).  The buffer keeps
  * the last call's contents; what must start at zero is cleared by the call's
  * own kernels.  Every call on one GPU uses the same buffer: calls that
@@ -198,23 +195,9 @@ int fp_index_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
  * must be serialised by the caller; calls on one stream are ordered.  The
  * outputs equal fp_index's for the same inputs.
  */
-#define FP_STATIC_SCRATCH_BYTES (32u << 20)
+#define FP_STATIC_SCRATCH_BYTES (64u << 20)
 int fp_index_static(const fp_shape *shape, const void *Q, const void *K,
                     float gamma, float tau, fp_index_out *out, void *stream);
-
-/*
- * Test entry point: fp_index (variant 0; sQ, sK ignored) or fp_index_i8
- * (variant 1) with the last-block statistics forced onto their two-pass form,
- * which streams K twice (row maxima and sums first, block mass second)
- * instead of keeping per-row partials on chip until a grid-wide barrier.
- * fp_index uses that form by itself only where the partials do not fit in
- * LDS; this call lets tests check it at any size.  The results equal
- * fp_index's up to floating-point rounding order.  Arguments, errors and
- * outputs as fp_index / fp_index_i8; FP_EINVAL for another variant.
- */
-int fp_index_two_pass(const fp_shape *shape, int variant, const void *Q, const float *sQ,
-                      const void *K, const float *sK, float gamma, float tau,
-                      fp_index_out *out, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * The QKV projection that precedes the path, with the later stages' pooling
@@ -400,8 +383,9 @@ int fp_attn_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
  * workgroup size that kernel runs with for this shape:
  *   path FP_PROBE_ATTN:  fp_attn_i8's kernel (direct-to-LDS loads, key rows
  *                        in its permuted LDS order, mapped back to keys);
- *   path FP_PROBE_STATS: fp_index_i8's single-pass statistics kernel
- *                        (register-staged block, padded LDS rows).
+ *   path FP_PROBE_STATS: fp_index_i8's streaming statistics kernel
+ *                        (direct loads into padded LDS rows, up to 128
+ *                        keys per staging unit).
  *   out: device int32 [b, b] (key-major: out[c * b + r]).
  * Errors: FP_EINVAL (null pointer, h, i or j out of range, unknown path),
  * FP_EUNSUPPORTED, FP_EHIP.

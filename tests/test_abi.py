@@ -30,7 +30,8 @@ def test_header_declares_expected_entry_points():
     for n in ("fp_index", "fp_index_i8", "fp_attn", "fp_attn_i8", "fp_build_jobs",
               "fp_workspace_bytes", "fp_csr_capacity", "fp_job_capacity", "fp_strerror",
               "fp_version", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch",
-              "fp_index_i8_batch", "fp_attn_i8_batch", "fp_index_two_pass"):
+              "fp_index_i8_batch", "fp_attn_i8_batch", "fp_index_static", "fp_index_shared",
+              "fp_index_pooled", "fp_qkv_project", "fp_attn_split", "fp_block_uses"):
         assert n in names
 
 
@@ -127,12 +128,21 @@ def test_attn_and_probe_reject_bad_arguments():
     assert L.fp_probe_qk_i8(ctypes.byref(sh), P, P, 0, 16, 0, 0, P, None) == fpa.FP_EINVAL  # i out of range
     assert L.fp_probe_qk_i8(ctypes.byref(sh), P, P, 0, 0, 0, 2, P, None) == fpa.FP_EINVAL   # unknown path
     assert L.fp_probe_qk_i8(ctypes.byref(sh), P, None, 0, 0, 0, 1, P, None) == fpa.FP_EINVAL
-    # the two-pass test entry point: unknown variant, missing int8 scales, and fp_index's own checks
+    # head-pattern sharing: unknown variant, missing int8 scales, and fp_index's own checks
     big = 1 << 30
-    assert L.fp_index_two_pass(ctypes.byref(sh), 2, P, None, P, None, 0.9, 0.1, ctypes.byref(o), P, big, None) == fpa.FP_EINVAL
-    assert L.fp_index_two_pass(ctypes.byref(sh), 1, P, None, P, P, 0.9, 0.1, ctypes.byref(o), P, big, None) == fpa.FP_EINVAL
-    assert L.fp_index_two_pass(ctypes.byref(sh), 0, P, None, P, None, 1.5, 0.1, ctypes.byref(o), P, big, None) == fpa.FP_EINVAL
-    assert L.fp_index_two_pass(ctypes.byref(sh), 0, P, None, P, None, 0.9, 0.1, ctypes.byref(o), P, 8, None) == fpa.FP_EWORKSPACE
+    assert L.fp_index_shared(ctypes.byref(sh), 2, P, None, P, None, 0.9, 0.1, ctypes.byref(o), P, big, None) == fpa.FP_EINVAL
+    assert L.fp_index_shared(ctypes.byref(sh), 1, P, None, P, P, 0.9, 0.1, ctypes.byref(o), P, big, None) == fpa.FP_EINVAL
+    assert L.fp_index_shared(ctypes.byref(sh), 0, P, None, P, None, 1.5, 0.1, ctypes.byref(o), P, big, None) == fpa.FP_EINVAL
+    assert L.fp_index_shared(ctypes.byref(sh), 0, P, None, P, None, 0.9, 0.1, ctypes.byref(o), P, 8, None) == fpa.FP_EWORKSPACE
+    # the projection and the pooled-query index
+    assert L.fp_index_pooled(ctypes.byref(sh), P, P, None, 0.9, 0.1, ctypes.byref(o), P, big, None) == fpa.FP_EINVAL
+    nul = [None] * 6
+    assert L.fp_qkv_project(ctypes.byref(sh), 256, None, P, None, None, P, P, P, None, None, *nul, None) == fpa.FP_EINVAL
+    assert L.fp_qkv_project(ctypes.byref(sh), 256, P, P, P, None, P, P, P, None, None, *nul, None) == fpa.FP_EINVAL   # cos without sin
+    assert L.fp_qkv_project(ctypes.byref(sh), 100, P, P, None, None, P, P, P, None, None, *nul, None) == fpa.FP_EUNSUPPORTED
+    assert L.fp_qkv_project(ctypes.byref(sh), 256, P, P, None, None, P, P, P, None, None, P, None, None, None, None, None, None) == fpa.FP_EINVAL
+    sh256 = fpa.shape_of(2048, 256, 4, 2)
+    assert L.fp_qkv_project(ctypes.byref(sh256), 256, P, P, None, None, P, P, P, P, None, *nul, None) == fpa.FP_EUNSUPPORTED
     o2 = _dummy_out(sh)
     o2.job_ptr = None
     assert L.fp_build_jobs(ctypes.byref(sh), ctypes.byref(o2), P, 1 << 30, None) == fpa.FP_EINVAL

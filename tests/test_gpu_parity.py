@@ -152,6 +152,7 @@ INDEX_CASES = [
     ("tiny-G1", dict(Hq=2, Hkv=2), 0.9),
     ("tiny-N37", dict(S=128 * 37), 0.9),
     ("tiny-b256-G4", dict(S=4096, b=256, Hq=8, Hkv=2, vs_frac=0.5), 0.95),
+    ("tiny-b256-G8", dict(S=4096, b=256, Hq=8, Hkv=1), 0.9),       # 64 query tiles: four per wave
     ("tiny-G8", dict(S=2048, Hq=8, Hkv=1), 0.9),
     ("tiny-G16", dict(S=1024, Hq=16, Hkv=1), 0.9),
     ("tiny-N70", dict(S=128 * 70, Hq=4, Hkv=2), 0.9),
@@ -170,23 +171,17 @@ LARGE_N_CASES = [
 ]
 
 
-def _index_case(c, gamma, i8=False, two_pass=False):
+def _index_case(c, gamma, i8=False):
     L = gen.make(c)
     if i8:
         d = L.int8()
         ref = oi.index_i8(d["q8"], d["sq"], d["k8"], d["sk"], c.b, gamma, c.tau)
         t = P.layer_i8_on_device(L)
-        if two_pass:
-            idx = fpa.index_two_pass(t["q8"], t["k8"], c.b, gamma, c.tau, sQ=t["sq"], sK=t["sk"], stats=True)
-        else:
-            idx = fpa.index_i8(t["q8"], t["sq"], t["k8"], t["sk"], c.b, gamma, c.tau, stats=True)
+        idx = fpa.index_i8(t["q8"], t["sq"], t["k8"], t["sk"], c.b, gamma, c.tau, stats=True)
     else:
         ref = oi.index(L.f32("q"), L.f32("k"), c.b, gamma, c.tau)
         Qd, Kd, _ = P.layer_on_device(L)
-        if two_pass:
-            idx = fpa.index_two_pass(Qd, Kd, c.b, gamma, c.tau, stats=True)
-        else:
-            idx = fpa.index(Qd, Kd, c.b, gamma, c.tau, stats=True)
+        idx = fpa.index(Qd, Kd, c.b, gamma, c.tau, stats=True)
     torch.cuda.synchronize()
     s = P.compare_index(idx, ref, gamma, c.tau)
     pat = idx.pattern.cpu().numpy()
@@ -297,18 +292,6 @@ def test_ragged_batch_i8():
         mx, rms = P.attn_errors(Oc, Oref)
         say(f"  S={c.S}: density {idx.density():.3f}, attention maxabs {mx:.2e} rms {rms:.2e}")
         assert mx <= MAXABS and rms <= RMS
-
-
-TWO_PASS_CASES = [c for c in INDEX_CASES if c[0] in ("tiny", "tiny-G16", "tiny-N70", "tiny-b256-G4", "tiny-b64-G3")]
-
-
-@pytest.mark.parametrize("name,kw,gamma", TWO_PASS_CASES, ids=[c[0] for c in TWO_PASS_CASES])
-@pytest.mark.parametrize("i8", [False, True], ids=["bf16", "i8"])
-def test_index_two_pass_statistics(name, kw, gamma, i8):
-    """The two-pass statistics form (used when the single pass's partials do not fit in LDS)
-    forced at small sizes through the test entry point fp_index_two_pass."""
-    say(f"index {'i8' if i8 else 'bf16'} two-pass statistics {name} gamma={gamma}")
-    _index_case(cfg(**kw), gamma, i8=i8, two_pass=True)
 
 
 def test_index_deterministic_and_end_to_end():
