@@ -292,10 +292,14 @@ __global__ void __launch_bounds__(NT) k_ig_stream(StreamArgs a) {
               elo = 0.0f;
               ehi = 0.0f;
               if (pos + 1 < QT) {
-                // all keys of the tile lie on one side of the wave's query rows
-                float e = 0.0f;
+                // all keys of the tile lie on one side of the wave's query rows; four partial sums
+                // (a shorter dependency chain), combined in a fixed order
+                float e4[4];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) e += fast_exp2(fmaf(x[r], qs, mneg));
+                for (int q = 0; q < 4; ++q) e4[q] = fast_exp2(fmaf(x[q], qs, mneg));
+#pragma unroll
+                for (int r = 4; r < 16; ++r) e4[r & 3] += fast_exp2(fmaf(x[r], qs, mneg));
+                const float e = (e4[0] + e4[1]) + (e4[2] + e4[3]);
                 (kt < tq ? elo : ehi) = e;
               } else {
 #pragma unroll
