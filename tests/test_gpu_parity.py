@@ -102,6 +102,8 @@ ATTN_CASES = [
     ("tiny-G7-b256", dict(S=2048, b=256, Hq=7, Hkv=1), 0.9),
     ("tiny-b64", dict(S=1024, b=64, Hq=4, Hkv=2), 0.9),     # two 64-key blocks per staged chunk
     ("tiny-b64-G3", dict(S=2048, b=64, Hq=6, Hkv=2), 0.9),
+    ("tiny-G3", dict(Hq=6, Hkv=2), 0.9),                    # one wave per query tile for all three heads
+    ("tiny-G3-b256", dict(S=2048, b=256, Hq=3, Hkv=1), 0.9),
 ]
 
 
@@ -141,6 +143,38 @@ def test_attn_gamma_one_is_dense_causal():
                     for h in range(c.Hq)])
     mx, rms = P.attn_errors(O, ref)
     assert mx <= MAXABS and rms <= RMS, (mx, rms)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (6, 2)], ids=["G1", "G2", "G3"])
+def test_attn_score_spike(Hq, Hkv):
+    """Keys of block 0 scaled by 3: rows that meet them after other keys see scores 80 to 140
+    (log2 units) above everything before, far beyond the headroom the kernel allows before it
+    rescales O to a raised reference maximum; dense causal index, oracle attention."""
+    say(f"attn score spike Hq={Hq} Hkv={Hkv}")
+    c = cfg(S=1024, Hq=Hq, Hkv=Hkv)
+    L = gen.make(c)
+    kf = L.f32("k")
+    kf[:, :c.b] *= 3.0
+    kbits = gen.bf16_bits_from_f32(kf)
+    K = gen.f32_from_bf16_bits(kbits)
+    Q, V = L.f32("q"), L.f32("v")
+    sh = fpa.shape_of(c.S, c.b, c.Hq, c.Hkv)
+    N = c.N
+    rp = np.zeros(c.Hq * N + 1, dtype=np.int32)
+    cols = []
+    for h in range(c.Hq):
+        for i in range(N):
+            cols.extend(range(i + 1))
+            rp[h * N + i + 1] = len(cols)
+    idx = fpa.build_jobs(sh, P.dev(rp), P.dev(np.array(cols, dtype=np.int32)))
+    O = fpa.attn(P.dev_bf16(L.q), P.dev_bf16(kbits), P.dev_bf16(L.v), idx)
+    from oracle import brute
+    ref = np.stack([brute.dense_masked_attention(Q[h], K[h // c.G], V[h // c.G], brute.causal_mask(c.S))
+                    for h in range(c.Hq)])
+    torch.cuda.synchronize()
+    mx, rms = P.attn_errors(O, ref)
+    say(f"  maxabs={mx:.3e} rms={rms:.3e}")
+    assert np.isfinite(mx) and mx <= MAXABS and rms <= RMS, (mx, rms)
 
 
 # ------------------------------------------------------------------ index generation
