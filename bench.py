@@ -24,8 +24,8 @@ two rocprofv3 counter passes over this script, scaled by the same counters on
 a copy of known size:
     rocprofv3 --pmc FETCH_SIZE --output-format csv -d D -o copy_FETCH_SIZE -- python3 bench.py --copy-calibration
     rocprofv3 --pmc WRITE_SIZE --output-format csv -d D -o copy_WRITE_SIZE -- python3 bench.py --copy-calibration
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D -o bench_FETCH_SIZE -- python3 bench.py --steps 1 --warmup 0 --no-cpu
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D -o bench_WRITE_SIZE -- python3 bench.py --steps 1 --warmup 0 --no-cpu
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d D -o bench_FETCH_SIZE -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-extra
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d D -o bench_WRITE_SIZE -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-extra
     python bench.py --traffic-from D        # writes profiles/traffic_<config>.json
 The file records a hash of the attention source; once the kernel changes the
 field reads null until the passes are taken again.
@@ -124,7 +124,7 @@ def traffic_from(d: str, config: str):
            "commands": [
                f"rocprofv3 --pmc {c} --output-format csv -d D -o copy_{c} -- python3 bench.py --copy-calibration"
                for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
-               f"rocprofv3 --pmc {c} --output-format csv -d D -o bench_{c} -- python3 bench.py --steps 1 --warmup 0 --no-cpu --config {config}"
+               f"rocprofv3 --pmc {c} --output-format csv -d D -o bench_{c} -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-extra --config {config}"
                for c in ("FETCH_SIZE", "WRITE_SIZE")]}
     os.makedirs(os.path.dirname(traffic_file(config)), exist_ok=True)
     json.dump(rec, open(traffic_file(config), "w"), indent=1)
