@@ -11,7 +11,9 @@
 //
 // W8A8 (explainer sections 3.3 and 4.2): Q.K^T on the int8 matrix cores with
 // int32 accumulation, scaled by sigma * sQ[t] * sK[k]; P.V in bf16 with the
-// int8 values of V (exact in bf16) and sV folded into P.
+// int8 values of V (exact in bf16) and sV folded into P.  The int8 V codes are
+// widened to bf16 once per call (k_widen_v8), so the chunk stream stages V
+// exactly as in the bf16 form.
 //
 // Kernel layout.  The explainer's section 2.2 notes that grouped-query heads
 // re-fetch the same K/V blocks; section 3.2 schedules sparse attention from a
@@ -26,8 +28,7 @@
 // other by direct global-to-LDS loads.  Scores are computed transposed,
 // S^T = K Q^T, on the 32x32x16 matrix cores so that every lane owns one query
 // row; its softmax weights are then already the operand of O^T += V^T P^T,
-// whose V^T operand comes from LDS transpose reads of the key-major V rows
-// (int8: V is widened to bf16 and stored transposed after its chunk arrives).
+// whose V^T operand comes from LDS transpose reads of the key-major V rows.
 #include <algorithm>
 
 #include "fp_common.hpp"
@@ -52,7 +53,6 @@ struct AttnArgs {
 constexpr int kPartStride = 132;
 
 constexpr int kChunkDl = 128;                // keys per staged chunk
-constexpr int kVStride = kChunkDl + 8;       // bf16 elements per transposed int8-path V row (272 B)
 // Lazy-rescale headroom: weights stay below 2^24 before a rescale, so O^T (at
 // most 2^24 times the key count times max |V|) stays far inside fp32.
 constexpr float kRescaleDl = 24.0f;
@@ -60,12 +60,6 @@ constexpr float kRescaleDl = 24.0f;
 template <bool I8> struct KL {
   static constexpr int Stride = I8 ? 144 : 272;        // LDS bytes per staged key row (padded)
 };
-
-// K rows are staged in a permuted order: LDS row rho holds key swap23(rho)
-// (bits 2 and 3 of the index exchanged, an involution).  In the transposed
-// score tile a lane then owns, for each 16-key step of the P.V product, 8
-// consecutive keys, so its V^T operand is one 16-byte LDS read.
-__device__ __forceinline__ int swap23(int x) { return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1); }
 
 // Q fragments (operand B of S^T = K Q^T) for query token `tok` of this lane.
 template <bool I8>
@@ -128,13 +122,12 @@ constexpr int VBuf = kChunkDl * 256;                  // 32768 B
 constexpr int KLoads = kChunkDl * KSlots / 64;        // 34 one-KiB loads
 constexpr int VLoads = VBuf / 1024;                 // 32
 static_assert(kChunkDl * KSlots % 64 == 0, "K staging must be whole 1 KiB spans");
-// int8 form: K rows of 128 B staged as 9 slots (144 B); V is staged as int8 and
-// then widened to bf16 and stored transposed (rows of kVStride bf16); one more
-// load carries the chunk's K and V scales.
+// int8 form: K rows of 128 B staged as 9 slots (144 B); V rows of the widened
+// bf16 copy staged as in the bf16 form; one more load carries the chunk's K and
+// V scales.
 constexpr int KSlots8 = 9;
 constexpr int KRow8 = KSlots8 * 16;                 // 144 B
 constexpr int KBuf8 = kChunkDl * KRow8;             // 18432 B
-constexpr int VBuf8 = 128 * kVStride * 2;           // 34816 B (V^T, 128 columns)
 constexpr int KLoads8 = kChunkDl * KSlots8 / 64;    // 18
 static_assert(kChunkDl * KSlots8 % 64 == 0, "K staging must be whole 1 KiB spans");
 static_assert(kChunkDl == 128, "the scale load covers 128 keys");
@@ -158,19 +151,20 @@ __device__ __forceinline__ void dl_issue(const uint8_t *kg, const uint8_t *vg, u
   }
 }
 
-// int8: this wave's share of the direct loads of one chunk: K rows (LDS row
-// rho holding key swap23(rho), see raw_scores), V rows into the staging area,
-// and the scales (sK then sV, 128 each, one load).
+// int8: this wave's share of the direct loads of one chunk: the int8 K rows (9-slot rows, as
+// dl_issue's 17-slot ones), the bf16 V rows of the widened copy (exactly as dl_issue; none when vg
+// is null, for the probe) and the scales (sK then sV, 128 each, one load).
 __device__ __forceinline__ void dl_issue8(const uint8_t *kg, const uint8_t *vg, const float *skg, const float *svg,
-                                          uint32_t kb, uint32_t vsb, uint32_t sb, int wave, int nw) {
+                                          uint32_t kb, uint32_t vb, uint32_t sb, int wave, int nw) {
   const int lane = threadIdx.x & 63;
-  for (int u = wave; u < dl::KLoads8 + 17; u += nw) {
+  const int nv = vg ? dl::VLoads : 0;
+  for (int u = wave; u < dl::KLoads8 + nv + 1; u += nw) {
     if (u < dl::KLoads8) {
-      const int s = 64 * u + lane, rho = s / dl::KSlots8, c = min(s - rho * dl::KSlots8, 7);
-      lds_dma16(kg + swap23(rho) * 128 + 16 * c, kb + 1024 * u);
-    } else if (u < dl::KLoads8 + 16) {
-      const int r = 8 * (u - dl::KLoads8) + (lane >> 3);   // V row r: one full row per 8 lanes
-      lds_dma16(vg + r * 128 + 16 * ((lane & 7) ^ ((r >> 2) & 7)), vsb + 1024 * (u - dl::KLoads8));
+      const int s = 64 * u + lane, row = s / dl::KSlots8, c = min(s - row * dl::KSlots8, 7);
+      lds_dma16(kg + row * 128 + 16 * c, kb + 1024 * u);
+    } else if (u < dl::KLoads8 + nv) {
+      const int v = u - dl::KLoads8, row = 4 * v + (lane >> 4), c = (lane & 15) ^ (4 * (lane >> 4));
+      lds_dma16(vg + row * 256 + 16 * c, vb + 1024 * v);
     } else {
       lds_dma16(lane < 32 ? skg + 4 * lane : svg + 4 * (lane - 32), sb);
     }
@@ -194,18 +188,17 @@ __device__ __forceinline__ void dl_issue2(const uint8_t *ka, const uint8_t *va, 
 }
 __device__ __forceinline__ void dl_issue8_2(const uint8_t *ka, const uint8_t *va, const float *ska,
                                             const float *sva, const uint8_t *kb_, const uint8_t *vb_,
-                                            const float *skb, const float *svb, uint32_t kb, uint32_t vsb,
+                                            const float *skb, const float *svb, uint32_t kb, uint32_t vb,
                                             uint32_t sb, int wave, int nw) {
   const int lane = threadIdx.x & 63;
-  for (int u = wave; u < dl::KLoads8 + 17; u += nw) {
+  const int nv = va ? dl::VLoads : 0;
+  for (int u = wave; u < dl::KLoads8 + nv + 1; u += nw) {
     if (u < dl::KLoads8) {
-      // key swap23(rho) lies in the same 64-row half as row rho (the swap stays inside groups of 16)
-      const int s = 64 * u + lane, rho = s / dl::KSlots8, c = min(s - rho * dl::KSlots8, 7), key = swap23(rho);
-      lds_dma16((key < 64 ? ka + key * 128 : kb_ + (key - 64) * 128) + 16 * c, kb + 1024 * u);
-    } else if (u < dl::KLoads8 + 16) {
-      const int r = 8 * (u - dl::KLoads8) + (lane >> 3);
-      lds_dma16((r < 64 ? va + r * 128 : vb_ + (r - 64) * 128) + 16 * ((lane & 7) ^ ((r >> 2) & 7)),
-                vsb + 1024 * (u - dl::KLoads8));
+      const int s = 64 * u + lane, row = s / dl::KSlots8, c = min(s - row * dl::KSlots8, 7);
+      lds_dma16((row < 64 ? ka + row * 128 : kb_ + (row - 64) * 128) + 16 * c, kb + 1024 * u);
+    } else if (u < dl::KLoads8 + nv) {
+      const int v = u - dl::KLoads8, row = 4 * v + (lane >> 4), c = (lane & 15) ^ (4 * (lane >> 4));
+      lds_dma16((row < 64 ? va + row * 256 : vb_ + (row - 64) * 256) + 16 * c, vb + 1024 * v);
     } else {
       // lanes 0..15 / 16..31: sK of the two blocks, 32..47 / 48..63: sV
       const int q = lane >> 4, o = 4 * (lane & 15);
@@ -214,37 +207,23 @@ __device__ __forceinline__ void dl_issue8_2(const uint8_t *ka, const uint8_t *va
   }
 }
 
-// int8: V of one chunk arrives by direct loads in a 16 KB LDS staging area:
-// row r (128 B, eight 16-byte pieces) sits at offset 128 r, with piece c at
-// slot c ^ ((r >> 2) & 7). All threads then widen it to bf16 and store it
-// transposed (column d, key pair kp: one bf16x2 word), the layout the int8 P.V
-// reads. Lane = key pair and odd pairs read their second row first, so both
-// the 16-byte staging reads and the transposed 4-byte writes are free of bank
-// conflicts.
-__device__ __forceinline__ uint32_t vstage_off(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 2) & 7)); }
-
-template <int NT>
-__device__ __forceinline__ void widen_v8(const uint8_t *vs, uint32_t *vt32) {
-  constexpr int ITEMS = (128 / 2) * 8;                     // (key pair, 16-byte column)
-  for (int idx = threadIdx.x; idx < ITEMS; idx += NT) {
-    const int kp = idx & 63, dc = idx >> 6, odd = kp & 1;
-    const u32x4 ra = *(const u32x4 *)(vs + vstage_off(2 * kp + odd, dc));
-    const u32x4 rb = *(const u32x4 *)(vs + vstage_off(2 * kp + 1 - odd, dc));
-    u32x4 va, vb;                                          // rows 2kp and 2kp + 1
+// fp_attn_i8: the int8 V codes widened to bf16 once per call (exact: |v| <= 127), in the key-major
+// layout the chunk stream stages from; the value scales stay separate (folded into P).  Thread t
+// converts the 16 codes at byte 16 t.
+__global__ void __launch_bounds__(256) k_widen_v8(const uint8_t *v8, uint16_t *vw, size_t n16) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n16) return;
+  const u32x4 in = *(const u32x4 *)(v8 + 16 * t);
+  uint32_t w[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      va[w] = odd ? rb[w] : ra[w];
-      vb[w] = odd ? ra[w] : rb[w];
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float lo = (float)(int8_t)((va[e >> 2] >> (8 * (e & 3))) & 0xffu);
-      const float hi = (float)(int8_t)((vb[e >> 2] >> (8 * (e & 3))) & 0xffu);
-      vt32[((dc * 16 + e) * kVStride >> 1) + kp] = pack_bf16x2(lo, hi);
-    }
+  for (int k = 0; k < 8; ++k) {
+    const uint32_t word = in[k >> 1] >> (16 * (k & 1));
+    w[k] = pack_bf16x2((float)(int8_t)(word & 0xffu), (float)(int8_t)((word >> 8) & 0xffu));
   }
+  u32x4 *o = (u32x4 *)(vw + 16 * t);
+  o[0] = u32x4{w[0], w[1], w[2], w[3]};
+  o[1] = u32x4{w[4], w[5], w[6], w[7]};
 }
-
 
 // An LDS byte address the compiler cannot fold constants into (keeps the
 // per-read offsets small enough for the instruction's immediate field).
@@ -305,9 +284,8 @@ struct Ent {
 template <int NT, bool I8, bool PAIR, bool SPLIT>
 __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, int nunits, unsigned int *ctr) {
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][I8 ? dl::KBuf8 : dl::KBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][I8 ? dl::VBuf8 : dl::VBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][dl::VBuf];
   __shared__ __attribute__((aligned(16))) float sbuf[2][I8 ? 2 * kChunkDl : 4];   // int8: sK, sV of the chunk
-  __shared__ __attribute__((aligned(1024))) uint8_t vstage[I8 ? kChunkDl * 128 : 16];   // int8: V rows in flight
   __shared__ int s_claim[2];
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -364,30 +342,19 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
         dl_issue2(a.K + ra * 256, a.V + ra * 256, a.K + rb * 256, a.V + rb * 256, lds_addr(kbuf[b]),
                   lds_addr(vbuf[b]), wave, NW);
       } else {
-        dl_issue8_2(a.K + ra * 128, a.V + ra * 128, a.sK + ra, a.sV + ra, a.K + rb * 128, a.V + rb * 128,
-                    a.sK + rb, a.sV + rb, lds_addr(kbuf[b]), lds_addr(vstage), lds_addr(sbuf[b]), wave, NW);
+        dl_issue8_2(a.K + ra * 128, a.V + ra * 256, a.sK + ra, a.sV + ra, a.K + rb * 128, a.V + rb * 256,
+                    a.sK + rb, a.sV + rb, lds_addr(kbuf[b]), lds_addr(vbuf[b]), lds_addr(sbuf[b]), wave, NW);
       }
     } else if (!PAIR && j >= 0 && j < N) {
       const size_t row0 = (size_t)en.g * S + (size_t)j * B + en.kc * kChunkDl;
       if constexpr (!I8) {
         dl_issue(a.K + row0 * 256, a.V + row0 * 256, lds_addr(kbuf[b]), lds_addr(vbuf[b]), wave, NW);
       } else {
-        dl_issue8(a.K + row0 * 128, a.V + row0 * 128, a.sK + row0, a.sV + row0, lds_addr(kbuf[b]),
-                  lds_addr(vstage), lds_addr(sbuf[b]), wave, NW);
+        dl_issue8(a.K + row0 * 128, a.V + row0 * 256, a.sK + row0, a.sV + row0, lds_addr(kbuf[b]),
+                  lds_addr(vbuf[b]), lds_addr(sbuf[b]), wave, NW);
       }
     }
   };
-  // int8: once every wave's loads of entry en have arrived (the caller waits and
-  // synchronises), its staged V is widened into buffer b; the barrier after it
-  // publishes buffer b and frees the staging area
-  auto put_v = [&](const Ent &en, int b) {
-    if constexpr (I8) {
-      const int j = sgpr(en.jv);
-      if (j >= 0 && j < N) widen_v8<NT>(vstage, (uint32_t *)vbuf[b]);
-      __syncthreads();
-    }
-  };
-
   if ((int)blockIdx.x >= nunits) return;
   Unit cur = unit_from(blockIdx.x, vload(utab + blockIdx.x));
   int nxt_id = blockIdx.x + gridDim.x;                // claimed unit that follows cur
@@ -395,11 +362,6 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   int parity = 0;
   Ent e0 = fetch(cur, 0), e1 = fetch(cur, 1);
   issue(e0, 0);
-  if constexpr (I8) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    __syncthreads();
-    put_v(e0, 0);
-  }
 
   // per-lane operand offsets: K rows (lane % 32) at column half hf; V^T per 32-column tile
   const int kl = (lane & 31) * dl::KRow + 16 * hf;
@@ -547,12 +509,12 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = acc[r];
           } else {
-            // int32 tile (LDS rows permuted: accumulator r of this lane is key kb + swap23(acc_row(r))),
-            // times the key scales; the query scale enters with sigma below
+            // int32 tile (accumulator r of this lane is key kb + acc_row(r) = kb + 8 (r / 4) + 4 hf +
+            // r % 4), times the key scales; the query scale enters with sigma below
             raw_scores<true>(kbuf[buf], kb, qf, x);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const f32x4 s4 = *(const f32x4 *)(sks + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
+              const f32x4 s4 = *(const f32x4 *)(sks + kb + 8 * q + 4 * hf);
 #pragma unroll
               for (int e = 0; e < 4; ++e) x[4 * q + e] *= s4[e];
             }
@@ -566,7 +528,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int row = 8 * (r >> 2) + hw4 + (r & 3);
-              if (key_t + (I8 ? swap23(row) : row) > qtok) x[r] = -INFINITY;
+              if (key_t + row > qtok) x[r] = -INFINITY;
             }
           }
           float mx = x[0];
@@ -604,7 +566,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
               for (int s2 = 0; s2 < 2; ++s2)
                 o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
           } else {
-            // weights (summed into l) times the value scales, then P.V against the widened V^T
+            // weights (summed into l) times the value scales, then P.V as in the bf16 form
             float pv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -613,7 +575,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const f32x4 s4 = *(const f32x4 *)(svs + kb + 16 * (q >> 1) + 8 * hf + 4 * (q & 1));
+              const f32x4 s4 = *(const f32x4 *)(svs + kb + 8 * q + 4 * hf);
 #pragma unroll
               for (int e = 0; e < 4; ++e) pv[4 * q + e] *= s4[e];
             }
@@ -621,19 +583,16 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             for (int s2 = 0; s2 < 2; ++s2)
               pf[s2] = u32x4{pack_bf16x2(pv[8 * s2 + 0], pv[8 * s2 + 1]), pack_bf16x2(pv[8 * s2 + 2], pv[8 * s2 + 3]),
                              pack_bf16x2(pv[8 * s2 + 4], pv[8 * s2 + 5]), pack_bf16x2(pv[8 * s2 + 6], pv[8 * s2 + 7])};
-            const uint16_t *vt = (const uint16_t *)vbuf[buf];
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const uint16_t *vrow = vt + (dt * 32 + (lane & 31)) * kVStride + kb + 8 * hf;
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-              for (int s2 = 0; s2 < 2; ++s2) o[dt] = mfma_bf16(*(const u32x4 *)(vrow + 16 * s2), pf[s2], o[dt]);
-            }
+              for (int s2 = 0; s2 < 2; ++s2)
+                o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
           }
         }
       }
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
-      put_v(e1, buf ^ 1);                          // int8: the next chunk's V, widened and transposed
       e0 = e1;
       e1 = e2;
     }
@@ -755,15 +714,14 @@ __global__ void __launch_bounds__(256) k_attn_combine(const float *part, const i
 }
 
 // Test hook: out[c * B + r] = Q8[h, i*B + r] . K8[g, j*B + c] through the W8A8 attention kernel's
-// own staging (direct-to-LDS loads of dl_issue8, or dl_issue8_2 for 64-key blocks, with K rows in
-// the swap23 order) and its int8 tile code, at the workgroup size the kernel runs with for this
-// shape; the accumulator rows are mapped back to keys as the kernel's masking does.  The V and
-// scale slots of the loads read bytes of the same key block (in bounds, never used).
+// own staging (direct-to-LDS loads of dl_issue8, or dl_issue8_2 for 64-key blocks, without the V
+// rows) and its int8 tile code, at the workgroup size the kernel runs with for this shape; the
+// accumulator rows are mapped back to keys as the kernel's masking does.  The scale slot of the
+// loads reads bytes of the same key block (in bounds, never used).
 template <int NT>
 __global__ void __launch_bounds__(NT) k_probe_attn_i8(const uint8_t *Q, const uint8_t *K, int S, int B, int h,
                                                       int g, int i, int j, int32_t *out) {
   __shared__ __attribute__((aligned(1024))) uint8_t kbuf[dl::KBuf8];
-  __shared__ __attribute__((aligned(1024))) uint8_t vstage[kChunkDl * 128];
   __shared__ __attribute__((aligned(16))) float sbuf[2 * kChunkDl];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -774,9 +732,9 @@ __global__ void __launch_bounds__(NT) k_probe_attn_i8(const uint8_t *Q, const ui
     const uint8_t *kg = K + ((size_t)g * S + (size_t)j * B + kc * kChunkDl) * 128;
     const float *junk = (const float *)kg;
     if (B >= kChunkDl)
-      dl_issue8(kg, kg, junk, junk, lds_addr(kbuf), lds_addr(vstage), lds_addr(sbuf), wave, NW);
+      dl_issue8(kg, nullptr, junk, junk, lds_addr(kbuf), 0u, lds_addr(sbuf), wave, NW);
     else   // 64-key blocks: both halves of the chunk carry block j
-      dl_issue8_2(kg, kg, junk, junk, kg, kg, junk, junk, lds_addr(kbuf), lds_addr(vstage), lds_addr(sbuf),
+      dl_issue8_2(kg, nullptr, junk, junk, kg, nullptr, junk, junk, lds_addr(kbuf), 0u, lds_addr(sbuf),
                   wave, NW);
     __builtin_amdgcn_s_waitcnt(kWaitVm0);
     __syncthreads();
@@ -790,7 +748,7 @@ __global__ void __launch_bounds__(NT) k_probe_attn_i8(const uint8_t *Q, const ui
         raw_scores<true>(kbuf, kb, qf, x);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kc * kChunkDl + kb + swap23(acc_row(r, lane));
+          const int key = kc * kChunkDl + kb + acc_row(r, lane);
           out[(size_t)key * B + qr] = (int32_t)x[r];
         }
       }
@@ -850,10 +808,16 @@ hipError_t dispatch_attn(const Plan &p, const AttnArgs &a, unsigned int *ctr, in
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,
                        void *O, unsigned int *ctr, int4 *utab, hipStream_t st, int nsplit, int nseg,
-                       float *part) {
+                       float *part, uint16_t *vw) {
   AttnArgs a;
   a.part = part;
   a.Q = (const uint8_t *)Q; a.K = (const uint8_t *)K; a.V = (const uint8_t *)V;
+  if (i8) {   // the chunk stream reads V from its bf16 widening
+    if (!vw) return hipErrorInvalidValue;
+    const size_t n16 = (size_t)p.Hkv * p.S * 128 / 16;
+    hipLaunchKernelGGL(k_widen_v8, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st, (const uint8_t *)V, vw, n16);
+    a.V = (const uint8_t *)vw;
+  }
   a.sQ = sQ; a.sK = sK; a.sV = sV;
   a.job_ptr = csr->job_ptr; a.job_blk = csr->job_blk; a.job_order = csr->job_order;
   a.job_mask = csr->job_mask;

@@ -48,6 +48,8 @@ int make_plan(const fp_shape *s, Plan *p) {
   p->off_jkeys = o;  o = align_up(o + sizeof(unsigned long long) * Hkv * N);
   p->off_utab = o;   o = align_up(o + sizeof(int4) * Hkv * N * (B / 32));
   p->total = o;
+  p->off_vw = o;     o = align_up(o + sizeof(uint16_t) * Hkv * (size_t)s->S * 128);
+  p->total_i8 = o;
   return FP_OK;
 }
 
@@ -121,7 +123,7 @@ int fp_workspace_bytes(const fp_shape *shape, int variant, size_t *bytes) {
   Plan p;
   int rc = make_plan(shape, &p);
   if (rc) return rc;
-  *bytes = p.total;
+  *bytes = variant == 1 ? p.total_i8 : p.total;
   return FP_OK;
 }
 
@@ -268,9 +270,11 @@ static int attn_common(const fp_shape *shape, bool i8, const void *Q, const floa
   if (!csr || !csr->row_ptr || !csr->col_idx || !csr->job_ptr || !csr->job_blk ||
       !csr->job_mask || !csr->job_order)
     return FP_EINVAL;
-  if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
+  const size_t need = i8 ? p.total_i8 : p.total;
+  if (!ws || ws_bytes < need) return ws ? FP_EWORKSPACE : FP_EINVAL;
   const Work w = carve(p, ws);
-  FP_LAUNCH(launch_attn(p, i8, Q, sQ, K, sK, V, sV, csr, O, w.bar + 32, w.utab, (hipStream_t)stream));
+  FP_LAUNCH(launch_attn(p, i8, Q, sQ, K, sK, V, sV, csr, O, w.bar + 32, w.utab, (hipStream_t)stream, 0, 1,
+                        nullptr, i8 ? (uint16_t *)((char *)ws + p.off_vw) : nullptr));
   return FP_OK;
 }
 
@@ -327,9 +331,10 @@ int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ, const i
 }
 
 // Ragged batches: every sequence is checked before anything is enqueued; the
-// workspace must cover the longest sequence's plan and is reused in order.
+// workspace must cover the longest sequence's plan (its int8 attention form for
+// fp_attn_i8_batch) and is reused in order.
 static int batch_check(const fp_shape *shape, int nseq, const int32_t *seqlens, size_t ws_bytes,
-                       const fp_index_out *outs, bool need_pattern) {
+                       const fp_index_out *outs, bool need_pattern, bool i8_attn = false) {
   if (!shape || nseq < 1 || !seqlens || !outs) return FP_EINVAL;
   size_t need = 0;
   for (int s = 0; s < nseq; ++s) {
@@ -344,7 +349,8 @@ static int batch_check(const fp_shape *shape, int nseq, const int32_t *seqlens, 
     } else if (!o->row_ptr || !o->col_idx || !o->job_ptr || !o->job_blk || !o->job_mask || !o->job_order) {
       return FP_EINVAL;
     }
-    need = p.total > need ? p.total : need;
+    const size_t t = i8_attn ? p.total_i8 : p.total;
+    need = t > need ? t : need;
   }
   return ws_bytes < need ? FP_EWORKSPACE : FP_OK;
 }
@@ -377,7 +383,7 @@ static int attn_batch_common(const fp_shape *shape, bool i8, int nseq, const int
                              const float *sQ, const void *K, const float *sK, const void *V, const float *sV,
                              const fp_index_out *csrs, void *O, void *ws, size_t ws_bytes, void *stream) {
   if (!Q || !K || !V || !O || !ws || (i8 && (!sQ || !sK || !sV))) return FP_EINVAL;
-  int rc = batch_check(shape, nseq, seqlens, ws_bytes, csrs, false);
+  int rc = batch_check(shape, nseq, seqlens, ws_bytes, csrs, false, i8);
   if (rc) return rc;
   const size_t eb = i8 ? 1 : 2;
   const uint8_t *q = (const uint8_t *)Q, *k = (const uint8_t *)K, *v = (const uint8_t *)V;

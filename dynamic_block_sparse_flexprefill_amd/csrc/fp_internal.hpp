@@ -31,7 +31,9 @@ struct Plan {
   size_t off_bar;    // u32    [64]        [32]: unit counter of the persistent attention kernel
   size_t off_jkeys;  // u64    [Hkv*N]     per-group sorted job keys
   size_t off_utab;   // int4   [Hkv*N*b/32] attention work units {job, first entry, chunks, start}
-  size_t total;
+  size_t total;      // bytes every call but fp_attn_i8 needs
+  size_t off_vw;     // bf16   [Hkv*S*d]   fp_attn_i8: the int8 V codes widened to bf16
+  size_t total_i8;   // bytes fp_attn_i8 needs (fp_workspace_bytes variant 1)
 };
 
 // Validates the shape (FP_EINVAL / FP_EUNSUPPORTED) and fills *p.
@@ -93,7 +95,7 @@ int cu_count();
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
                        const float *sK, const void *V, const float *sV, const fp_index_out *csr,
                        void *O, unsigned int *ctr, int4 *utab, hipStream_t st, int nsplit = 0,
-                       int nseg = 1, float *part = nullptr);
+                       int nseg = 1, float *part = nullptr, uint16_t *vw = nullptr);
 // Partial-output floats per split slot (G heads x b rows x padded row).
 size_t attn_split_slot_floats(const Plan &p);
 // One exact int8 score tile through the W8A8 attention kernel's staging and tile code.

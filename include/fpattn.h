@@ -127,9 +127,10 @@ int fp_version(void);
 const char *fp_strerror(int code);
 
 /*
- * Scratch bytes that fp_index / fp_index_i8 (variant 0 / 1), fp_build_jobs
- * and fp_attn / fp_attn_i8 need for this shape.  One workspace of the size
- * returned for variant 1 serves every call.  Writes *bytes (host).
+ * Scratch bytes for this shape: variant 0 covers fp_index, fp_index_i8,
+ * fp_build_jobs and fp_attn; variant 1 also fp_attn_i8, which keeps a bf16
+ * widening of V8 there (2 * Hkv * S * d bytes more).  One workspace of the
+ * size returned for variant 1 serves every call.  Writes *bytes (host).
  */
 int fp_workspace_bytes(const fp_shape *shape, int variant, size_t *bytes);
 
@@ -328,6 +329,8 @@ int fp_attn_split(const fp_shape *shape, const void *Q, const void *K, const voi
  * int8 dot product scaled by sigma * sQ * sK; P.V uses bf16 P against the
  * int8 values of V (exact in bf16) with the per-token scale sV folded into P.
  *   V8: device int8 [Hkv, S, d], sV: device fp32 [Hkv, S]; O: device bf16.
+ *   ws: at least fp_workspace_bytes(shape, 1) bytes (the call first widens V8
+ *   to bf16 in it).
  */
 int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
                const int8_t *K8, const float *sK, const int8_t *V8,
@@ -381,8 +384,8 @@ int fp_attn_i8_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
  * int32) for r, c in [0, b), computed through the staging and int8
  * matrix-core tile code of one of the two kernels that use it, at the
  * workgroup size that kernel runs with for this shape:
- *   path FP_PROBE_ATTN:  fp_attn_i8's kernel (direct-to-LDS loads, key rows
- *                        in its permuted LDS order, mapped back to keys);
+ *   path FP_PROBE_ATTN:  fp_attn_i8's kernel (direct-to-LDS loads of the
+ *                        int8 key rows into padded LDS rows);
  *   path FP_PROBE_STATS: fp_index_i8's streaming statistics kernel
  *                        (direct loads into padded LDS rows, up to 128
  *                        keys per staging unit).

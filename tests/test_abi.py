@@ -149,11 +149,14 @@ def test_attn_and_probe_reject_bad_arguments():
 
 
 def test_workspace_grows_with_shape():
-    a = fpa.workspace_bytes(fpa.shape_of(2048, 128, 4, 2))
-    b = fpa.workspace_bytes(fpa.shape_of(131072, 128, 24, 8))
+    a = fpa.workspace_bytes(fpa.shape_of(2048, 128, 4, 2), 0)
+    b = fpa.workspace_bytes(fpa.shape_of(131072, 128, 24, 8), 0)
     assert b > a > 0
     # nothing of size Hq x S x b: the 128K workspace stays far below the b x S score matrix of one head
     assert b < 128 * 131072 * 4
+    # variant 1 adds fp_attn_i8's bf16 widening of V8 (Hkv x S x d), 256-byte aligned
+    b1 = fpa.workspace_bytes(fpa.shape_of(131072, 128, 24, 8), 1)
+    assert b1 == b + 2 * 8 * 131072 * 128
 
 
 @no_gpu_only
@@ -174,8 +177,10 @@ def test_batch_rejects_bad_arguments():
     assert L.fp_index_batch(ctypes.byref(sh), 3, ragged, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
     small = (fpa.FpIndexOut * 3)(outs[0], _dummy_out(fpa.shape_of(384, 128, 4, 2), col_cap=4), outs[2])
     assert L.fp_index_batch(ctypes.byref(sh), 3, arr, P, P, 0.9, 0.1, small, P, big, None) == fpa.FP_EINVAL
-    # the workspace must cover the longest sequence
-    need = fpa.workspace_bytes(fpa.shape_of(2048, 128, 4, 2))
+    # the workspace must cover the longest sequence (its int8 attention form for fp_attn_i8_batch)
+    need = fpa.workspace_bytes(fpa.shape_of(2048, 128, 4, 2), 0)
+    need_i8 = fpa.workspace_bytes(fpa.shape_of(2048, 128, 4, 2), 1)
+    assert need_i8 > need
     assert L.fp_attn_batch(ctypes.byref(sh), 3, arr, P, P, P, outs, P, P, need - 1, None) == fpa.FP_EWORKSPACE
     assert L.fp_attn_batch(ctypes.byref(sh), 3, arr, P, P, None, outs, P, P, big, None) == fpa.FP_EINVAL
     bad = fpa.shape_of(2048, 128, 4, 2, 64)
@@ -185,7 +190,8 @@ def test_batch_rejects_bad_arguments():
     assert L.fp_index_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, 0.9, 0.1, outs, P, 64, None) == fpa.FP_EWORKSPACE
     assert L.fp_index_i8_batch(ctypes.byref(sh), 3, ragged, P, P, P, P, 0.9, 0.1, outs, P, big, None) == fpa.FP_EINVAL
     assert L.fp_attn_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, P, None, outs, P, P, big, None) == fpa.FP_EINVAL
-    assert L.fp_attn_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, P, P, outs, P, P, need - 1, None) == fpa.FP_EWORKSPACE
+    assert L.fp_attn_i8_batch(ctypes.byref(sh), 3, arr, P, P, P, P, P, P, outs, P, P, need_i8 - 1, None) == fpa.FP_EWORKSPACE
+    assert L.fp_attn_i8(ctypes.byref(sh), P, P, P, P, P, P, ctypes.byref(outs[2]), P, P, need_i8 - 1, None) == fpa.FP_EWORKSPACE
 
 
 @no_gpu_only
