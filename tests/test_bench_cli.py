@@ -37,7 +37,7 @@ def test_traffic_from_counter_passes(tmp_path, monkeypatch):
     _counters(tmp_path / "copy_WRITE_SIZE_counter_collection.csv", [("__amd_rocclr_copyBuffer", kib)] * 3)
     attn = "void fp::(anonymous namespace)::k_attn_dl<768, false>(fp::AttnArgs, int)"
     _counters(tmp_path / "bench_FETCH_SIZE_counter_collection.csv",
-              [(attn, 1000.0), (attn, 1200.0), ("void fp::k_ig_stats1<128>(args)", 5.0)])
+              [(attn, 1000.0), (attn, 1200.0), ("void fp::k_ig_stream<128, 768, 1, false>(args)", 5.0)])
     _counters(tmp_path / "bench_WRITE_SIZE_counter_collection.csv", [(attn, 300.0), (attn, 300.0)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "traffic_file", lambda name: str(out))
