@@ -154,8 +154,7 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
   hipStream_t st = (hipStream_t)stream;
   Work w = carve(p, ws);
-  FP_LAUNCH(launch_status_init(out->status, nullptr, st));
-  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, st));
+  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, st, out->status));   // also clears the status word
   FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, true));
   FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st, qbar_in));
   FP_LAUNCH(launch_rows_and_jobs(p, out, w, st, share));

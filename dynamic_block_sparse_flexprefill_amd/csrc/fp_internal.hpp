@@ -60,7 +60,8 @@ int stats_chunks(int B, int G, int N);
 // Statistics of the last query block against every key block (K streamed once), then merged:
 // lo, hi, kbar and the pooled-estimate logits pe in the workspace.
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ,
-                           const void *K, const float *sK, const Work &w, hipStream_t st);
+                           const void *K, const float *sK, const Work &w, hipStream_t st,
+                           int32_t *status = nullptr);
 // Per head: pooled estimate, divergence, pattern, vertical / slash selection.
 // have_pe: the pooled-estimate logits are in w.pe (else they are computed here).
 hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float *sQ,

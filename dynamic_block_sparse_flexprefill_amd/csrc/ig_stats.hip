@@ -62,6 +62,7 @@ struct StreamArgs {
   float2 *lohi;       // [Hq][N][B]   (lo, hi) sums of every row and key block, against the chunk's m
   float2 *ml;         // [Hq][nch][B] (m, sum) of every row and chunk (log2 units)
   float *kbar;        // [Hkv][N][128]
+  int32_t *status;    // the call's status word, cleared here (the index stage's first kernel); or null
 };
 
 constexpr float kHeadroom = 16.0f;   // a row's reference maximum is raised once a score exceeds it by this
@@ -193,6 +194,7 @@ __global__ void __launch_bounds__(NT) k_ig_stream(StreamArgs a) {
   __shared__ __attribute__((aligned(16))) float skb[2][I8 ? 256 : 4];
   __shared__ float part[NTL][CB][64];        // (lo, hi) per row of each tile slot and block of the chunk
   __shared__ float kpart[I8 ? 2 : 1][I8 ? NW : 1][128];   // int8: per-wave column sums of a block (by parity)
+  if (a.status && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.status[0] = 0;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = blockIdx.y, G = a.G, S = a.S, N = a.N;
@@ -699,8 +701,9 @@ int cu_count() {
 }
 
 hipError_t launch_ig_stats(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,
-                           const float *sK, const Work &w, hipStream_t st) {
+                           const float *sK, const Work &w, hipStream_t st, int32_t *status) {
   StreamArgs a;
+  a.status = status;
   a.Q = (const uint8_t *)Q;
   a.sQ = sQ;
   a.K = (const uint8_t *)K;
