@@ -56,6 +56,7 @@ constexpr int kChunkDl = 128;                // keys per staged chunk
 // Lazy-rescale headroom: weights stay below 2^24 before a rescale, so O^T (at
 // most 2^24 times the key count times max |V|) stays far inside fp32.
 constexpr float kRescaleDl = 24.0f;
+constexpr float kRescaleSumDl = 16777216.0f;   // 2^kRescaleDl
 
 template <bool I8> struct KL {
   static constexpr int Stride = I8 ? 144 : 272;        // LDS bytes per staged key row (padded)
@@ -441,29 +442,47 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
                                 qf[s], acc);
               return acc;
             };
-            // softmax weights of one tile (bf16 pairs) against the raised reference maximum
+            // softmax weights of one tile (bf16 pairs), first against the current reference
+            // maximum m with no maximum pass: a score above m + kRescaleDl gives a weight above
+            // 2^kRescaleDl, so the tile's sum reaching that bound (or infinity, as while m is
+            // unset) is the only case that can need a new maximum.  Only then is the tile's
+            // maximum taken and, where it exceeds m + kRescaleDl, m raised and the weights redone;
+            // m therefore moves exactly as under a maximum pass of every tile.
             auto weights = [&](const f32x16 &sc, u32x4 pf[2], float &alpha) {
-              float mx = fmaxf(sc[0], sc[1]);
+              auto eval = [&]() {
+                float lt = 0.0f;
 #pragma unroll
-              for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-              const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-              mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qsc;
-              const bool grow = mx > m + kRescaleDl;
-              const float mnew = grow ? mx : m;
-              alpha = fast_exp2(m - mnew);               // exactly 1 where the maximum stays
-              m = mnew;
-              l *= alpha;
+                for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-              for (int s2 = 0; s2 < 2; ++s2)
+                  for (int w = 0; w < 4; ++w) {
+                    const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(sc[8 * s2 + 2 * w], qsc, -m)),
+                                                    fast_exp2(fmaf(sc[8 * s2 + 2 * w + 1], qsc, -m)));
+                    pf[s2][w] = pw;
+                    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
+                                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lt, false);
+                  }
+                return lt;
+              };
+              float lt = eval();
+              bool grew = false;
+              if (__any(!(lt < kRescaleSumDl))) {
+                float mx = fmaxf(sc[0], sc[1]);
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                  const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(sc[8 * s2 + 2 * w], qsc, -m)),
-                                                  fast_exp2(fmaf(sc[8 * s2 + 2 * w + 1], qsc, -m)));
-                  pf[s2][w] = pw;
-                  l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
-                                                      __builtin_bit_cast(bf16x2_t, 0x3f803f80u), l, false);
+                for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qsc;
+                const bool grow = mx > m + kRescaleDl;
+                if (__any(grow)) {
+                  const float mnew = grow ? mx : m;
+                  alpha = fast_exp2(m - mnew);           // exactly 1 where the maximum stays
+                  m = mnew;
+                  l *= alpha;
+                  lt = eval();
+                  grew = true;
                 }
-              return __any(grow);
+              }
+              l += lt;
+              return grew;
             };
             auto pv = [&](int kb, const u32x4 pf[2]) {
 #pragma unroll
