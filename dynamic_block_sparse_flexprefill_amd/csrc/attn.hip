@@ -448,7 +448,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             // unset) is the only case that can need a new maximum.  Only then is the tile's
             // maximum taken and, where it exceeds m + kRescaleDl, m raised and the weights redone;
             // m therefore moves exactly as under a maximum pass of every tile.
-            auto weights = [&](const f32x16 &sc, u32x4 pf[2], float &alpha) {
+            auto weights = [&](const f32x16 &sc, u32x4 pf[2], float &alpha, bool ilv) {
               auto eval = [&]() {
                 float lt = 0.0f;
 #pragma unroll
@@ -464,6 +464,26 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
                 return lt;
               };
               float lt = eval();
+              if (ilv) {
+                // one basic block holds this tile's products, the previous tile's P.V products and
+                // this tile's weights: the products each follow their operand reads (one ahead),
+                // and the weights fill the P.V products' read waits
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int s = 0; s < 7; ++s) {
+                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int s = 0; s < 7; ++s) {
+                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                  __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              }
               bool grew = false;
               if (__any(!(lt < kRescaleSumDl))) {
                 float mx = fmaxf(sc[0], sc[1]);
@@ -493,7 +513,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             };
             u32x4 pp[2];
             float alpha;
-            if (weights(qk(0), pp, alpha)) {
+            if (weights(qk(0), pp, alpha, false)) {
 #pragma unroll
               for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
             }
@@ -502,7 +522,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
               const f32x16 sc = qk(32 * kt);
               pv(32 * (kt - 1), pp);
               u32x4 pn[2];
-              if (weights(sc, pn, alpha)) {
+              if (weights(sc, pn, alpha, true)) {
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
               }
