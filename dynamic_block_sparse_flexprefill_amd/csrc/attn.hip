@@ -252,6 +252,38 @@ __device__ __forceinline__ T vload(const T *p) {
 }
 __device__ __forceinline__ int sgpr(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// A job-list entry (key block and head mask) by two scalar loads, waited for inside the same asm
+// statement, so the chunk loop holds no vector load the compiler tracks (its own wait for one
+// would also wait for the prefetch below).  Issued right after a chunk barrier, where no LDS read
+// is outstanding; consecutive entries share a scalar-cache line.
+__device__ __forceinline__ void sload_entry(const int *pb, const uint32_t *pm, int &jv, uint32_t &mv) {
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=s"(jv), "=s"(mv)
+               : "s"(pb), "s"(pm)
+               : "memory");
+}
+
+// One dword per lane from global memory into LDS (M0 + 4 * lane), by a direct load.
+__device__ __forceinline__ void lds_dma4(const void *g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+// L2 prefetch of the K rows of a chunk a step ahead of its own loads: one dword of every 128-byte
+// line (kbytes from kg) is read into a small LDS sink that nothing reads, so the HBM fetch of chunk
+// c + 2 overlaps chunk c and the loads of c + 2, issued during chunk c + 1, find its K rows in L2.
+// (K is read first in a chunk; prefetching V as well, or touching every 64 or 32 bytes, measured
+// slower.)  Wave w covers lines 64 w .. 64 w + 63; returns whether this wave issued a load
+// (uniform in the wave).
+constexpr int kPfLine = 128;
+__device__ __forceinline__ bool dl_prefetch(const uint8_t *kg, int kbytes, uint32_t sink, int wave) {
+  const int lane = threadIdx.x & 63;
+  const int nl = kbytes / kPfLine;
+  if (64 * wave >= nl) return false;
+  lds_dma4(kg + (size_t)kPfLine * min(64 * wave + lane, nl - 1), sink);
+  return true;
+}
+constexpr int kWaitVm1 = 0x0f71;     // s_waitcnt vmcnt(1): all but the youngest vector memory op
+
 // One unit of work: job (KV group g, query block i) in the job order, query
 // tile share `part` of it, its first job-list entry p0, chunk count and the
 // chunk the rotated visiting order starts from.
@@ -288,6 +320,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
   __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][dl::VBuf];
   __shared__ __attribute__((aligned(16))) float sbuf[2][I8 ? 2 * kChunkDl : 4];   // int8: sK, sV of the chunk
   __shared__ int s_claim[2];
+  __shared__ __attribute__((aligned(256))) uint32_t s_sink[64];   // prefetch sink (never read)
   const int lane = threadIdx.x & 63, hf = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   constexpr int NW = NT / 64;
@@ -328,8 +361,11 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
       return Ent{vload(a.job_blk + e), vload(a.job_mask + e), 0, x.g, two ? vload(a.job_blk + e + 1) : -1,
                  two ? vload(a.job_mask + e + 1) : 0u};
     } else {
-      const int e = x.p0 + cr / nck;
-      return Ent{vload(a.job_blk + e), vload(a.job_mask + e), cr % nck, x.g, -1, 0u};
+      const int e = sgpr(x.p0 + cr / nck);
+      int jv;
+      uint32_t mv;
+      sload_entry(a.job_blk + e, a.job_mask + e, jv, mv);
+      return Ent{jv, mv, cr % nck, x.g, -1, 0u};
     }
   };
   auto issue = [&](const Ent &en, int b) {
@@ -354,6 +390,17 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
         dl_issue8(a.K + row0 * 128, a.V + row0 * 256, a.sK + row0, a.sV + row0, lds_addr(kbuf[b]),
                   lds_addr(vbuf[b]), lds_addr(sbuf[b]), wave, NW);
       }
+    }
+  };
+  // the L2 prefetch of an entry's chunk (K rows; not for 64-key blocks); whether this wave issued a load
+  auto prefetch = [&](const Ent &en) -> bool {
+    if constexpr (PAIR) {
+      return false;
+    } else {
+      const int j = sgpr(en.jv);
+      if (!(j >= 0 && j < N)) return false;
+      const size_t row0 = (size_t)en.g * S + (size_t)j * B + en.kc * kChunkDl;
+      return dl_prefetch(a.K + row0 * (I8 ? 128 : 256), kChunkDl * (I8 ? 128 : 256), lds_addr(s_sink), wave);
     }
   };
   if ((int)blockIdx.x >= nunits) return;
@@ -405,6 +452,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
       const int buf = kk & 1;
       issue(e1, buf ^ 1);                          // the next chunk of the stream (no-op past its end)
       const Ent e2 = stream(c + 2);
+      const bool pf = prefetch(e2);                // after the loads above: the youngest op of the wave
       const int j0 = sgpr(e0.jv);
       const uint32_t mask0 = (uint32_t)sgpr((int)e0.maskv);
       const int key0 = j0 * B + e0.kc * kChunkDl;
@@ -630,7 +678,9 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
           }
         }
       }
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      // this wave's loads of the next chunk have landed; its prefetch may still be in flight
+      if (pf) __builtin_amdgcn_s_waitcnt(kWaitVm1);
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
       __syncthreads();
       e0 = e1;
       e1 = e2;
@@ -682,6 +732,7 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     nxt_id = s_claim[parity];
     parity ^= 1;
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);          // no prefetch outlives the workgroup's LDS
 }
 
 // Unit table {job, first job-list entry, entry count, rotated start chunk} and a zeroed claim counter.
