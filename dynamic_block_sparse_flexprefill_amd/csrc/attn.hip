@@ -282,6 +282,16 @@ __device__ __forceinline__ bool dl_prefetch(const uint8_t *kg, int kbytes, uint3
   lds_dma4(kg + (size_t)kPfLine * min(64 * wave + lane, nl - 1), sink);
   return true;
 }
+// The same for the K rows of two 64-key blocks (kbytes each; the second from kg2 unless null).
+__device__ __forceinline__ bool dl_prefetch2(const uint8_t *kg1, const uint8_t *kg2, int kbytes, uint32_t sink,
+                                             int wave) {
+  const int lane = threadIdx.x & 63;
+  const int n1 = kbytes / kPfLine, nl = kg2 ? 2 * n1 : n1;
+  if (64 * wave >= nl) return false;
+  const int line = min(64 * wave + lane, nl - 1);
+  lds_dma4(line < n1 ? kg1 + (size_t)kPfLine * line : kg2 + (size_t)kPfLine * (line - n1), sink);
+  return true;
+}
 constexpr int kWaitVm1 = 0x0f71;     // s_waitcnt vmcnt(1): all but the youngest vector memory op
 
 // One unit of work: job (KV group g, query block i) in the job order, query
@@ -356,10 +366,12 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
     int cr = c + x.rot;
     cr = cr >= x.total ? cr - x.total : cr;
     if constexpr (PAIR) {
-      const int e = x.p0 + 2 * cr;
-      const bool two = 2 * cr + 1 < x.n;
-      return Ent{vload(a.job_blk + e), vload(a.job_mask + e), 0, x.g, two ? vload(a.job_blk + e + 1) : -1,
-                 two ? vload(a.job_mask + e + 1) : 0u};
+      const int e = sgpr(x.p0 + 2 * cr);
+      int jv, jv2 = -1;
+      uint32_t mv, mv2 = 0u;
+      sload_entry(a.job_blk + e, a.job_mask + e, jv, mv);
+      if (2 * cr + 1 < x.n) sload_entry(a.job_blk + e + 1, a.job_mask + e + 1, jv2, mv2);
+      return Ent{jv, mv, 0, x.g, jv2, mv2};
     } else {
       const int e = sgpr(x.p0 + cr / nck);
       int jv;
@@ -392,10 +404,16 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
       }
     }
   };
-  // the L2 prefetch of an entry's chunk (K rows; not for 64-key blocks); whether this wave issued a load
+  // the L2 prefetch of an entry's chunk (its K rows); whether this wave issued a load
   auto prefetch = [&](const Ent &en) -> bool {
     if constexpr (PAIR) {
-      return false;
+      // both 64-key blocks of the chunk (a missing or out-of-range second one is not touched)
+      const int j = sgpr(en.jv), j2 = sgpr(en.jv2);
+      if (!(j >= 0 && j < N)) return false;
+      const int rb = B * (I8 ? 128 : 256);
+      const uint8_t *k1 = a.K + ((size_t)en.g * S + (size_t)j * B) * (I8 ? 128 : 256);
+      const uint8_t *k2 = j2 >= 0 && j2 < N ? a.K + ((size_t)en.g * S + (size_t)j2 * B) * (I8 ? 128 : 256) : nullptr;
+      return dl_prefetch2(k1, k2, rb, lds_addr(s_sink), wave);
     } else {
       const int j = sgpr(en.jv);
       if (!(j >= 0 && j < N)) return false;

@@ -42,8 +42,36 @@ __global__ void __launch_bounds__(256) k_qkv_proj(ProjArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sm[2 * 2 * 128 * kRow];
   static_assert(sizeof(uint16_t) * 2 * 2 * 128 * kRow >= sizeof(float) * 128 * kTileRow, "epilogue tile fits");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int it = blockIdx.x, ct = blockIdx.y;               // token tile, column tile (= head)
   const int D = a.D, S = a.S;
+  // Tile order: column tiles (heads) in bands of 8; within a band the workgroups that share a token
+  // tile (its 786 KB of X at D = 3072) run back to back on one XCD, so X is read from HBM about
+  // once per band instead of once per head.  Workgroup ids reach the XCDs round robin (id mod 8);
+  // with S / 128 not a multiple of 8 the band is simply walked token tile by token tile.
+  int it, ct;
+  {
+    const int nt = S / 128, nc = a.Hq + 2 * a.Hkv, per_band = nt * 8;
+    const int id = blockIdx.x, nfull = nc / 8;
+    int band, r, w;
+    if (id < nfull * per_band) {
+      band = id / per_band;
+      r = id - band * per_band;
+      w = 8;
+    } else {
+      band = nfull;
+      r = id - nfull * per_band;
+      w = nc - 8 * nfull;
+    }
+    int hl;
+    if (nt % 8 == 0) {
+      const int j = r >> 3, x = r & 7;
+      it = 8 * (j / w) + x;
+      hl = j % w;
+    } else {
+      it = r / w;
+      hl = r % w;
+    }
+    ct = 8 * band + hl;                                      // token tile it, column tile (= head) ct
+  }
   const int wr = (wave & 1) * 64, wc = (wave >> 1) * 64;
   const uint8_t *xg = a.X + (size_t)it * 128 * D * 2;
   const uint8_t *wg = a.W + (size_t)ct * 128 * D * 2;
@@ -221,7 +249,7 @@ hipError_t launch_qkv_proj(int S, int D, int Hq, int Hkv, int b, const void *X, 
   a.Q8 = Q8; a.K8 = K8; a.V8 = V8;
   a.sQ = sQ; a.sK = sK; a.sV = sV;
   a.S = S; a.D = D; a.Hq = Hq; a.Hkv = Hkv; a.b = b;
-  hipLaunchKernelGGL(k_qkv_proj, dim3(S / 128, Hq + 2 * Hkv), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_qkv_proj, dim3((S / 128) * (Hq + 2 * Hkv)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

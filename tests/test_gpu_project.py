@@ -54,7 +54,10 @@ def _check_bf16(got: torch.Tensor, want: np.ndarray, name: str):
 
 CASES = [("small-b128-rope-i8", 1024, 256, 4, 2, 128, True, True),
          ("small-b64-norope", 1024, 256, 4, 2, 64, False, True),
-         ("3b-dims-b128", 4096, 3072, 6, 2, 128, True, True)]
+         ("3b-dims-b128", 4096, 3072, 6, 2, 128, True, True),
+         # an odd number of 64-wide k-steps, 9 token tiles (not a multiple of 8) and 5 column tiles
+         # (a partial band of heads): the other branches of the tile order and of the load pipeline
+         ("odd-ksteps-ragged-tiles", 1152, 320, 3, 1, 128, True, True)]
 
 
 @pytest.mark.parametrize("name,S,D,Hq,Hkv,b,rot,i8", CASES, ids=[c[0] for c in CASES])
