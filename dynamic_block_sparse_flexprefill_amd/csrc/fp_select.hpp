@@ -77,17 +77,16 @@ constexpr int kGreedySteps = 24;
 // in slot k), so every pass of the search is unrolled register work.  Per-lane
 // sums visit the elements in the same order for any VPL (absent slots add 0),
 // so the selection does not depend on which VPL serves a row.
+// wave_select_vals takes the values already in registers: v[k] = element lane + 64 k, or -1 for
+// the slots past n.
 template <int VPL>
-__device__ __forceinline__ void wave_select_reg(const float *x, int n, float gamma, uint32_t *words) {
+__device__ __forceinline__ void wave_select_vals(const float (&v)[VPL], int n, float gamma, uint32_t *words) {
   static_assert(VPL >= 1 && VPL <= 32, "one bit of `taken` per slot");
   const int lane = threadIdx.x & 63;
-  float v[VPL];
   float part = 0.0f, mxl = 0.0f;
 #pragma unroll
   for (int k = 0; k < VPL; ++k) {
-    const int j = lane + 64 * k;
-    v[k] = j < n ? x[j] : -1.0f;             // -1: not an element
-    if (j < n) {
+    if (lane + 64 * k < n) {
       part += v[k];
       mxl = fmaxf(mxl, v[k]);
     }
@@ -164,6 +163,19 @@ __device__ __forceinline__ void wave_select_reg(const float *x, int n, float gam
     if (v[k] > th || (is_eq && rank < c)) atomicOr(&words[j >> 5], 1u << (j & 31));
     carried += __popcll(eqm);
   }
+}
+
+
+template <int VPL>
+__device__ __forceinline__ void wave_select_reg(const float *x, int n, float gamma, uint32_t *words) {
+  const int lane = threadIdx.x & 63;
+  float v[VPL];
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int j = lane + 64 * k;
+    v[k] = j < n ? x[j] : -1.0f;             // -1: not an element
+  }
+  wave_select_vals<VPL>(v, n, gamma, words);
 }
 
 // The register form sized to the row (the cost of a search pass grows with VPL),

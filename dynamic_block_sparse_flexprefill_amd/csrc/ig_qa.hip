@@ -110,9 +110,30 @@ struct QaArgs {
   uint32_t *rowbits;
 };
 
+// Softmax weights and selection of one row of n logits (LDS) whose values fit the register form:
+// one LDS read per value, the maximum, the exponentials and the search all in registers.
+template <int VPL>
+__device__ __forceinline__ void select_row_reg(const float *x, int n, float gamma, uint32_t *wd) {
+  const int lane = threadIdx.x & 63;
+  float v[VPL];
+  float mx = kNegBig;
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) {
+    const int j = lane + 64 * k;
+    v[k] = j < n ? x[j] : kNegBig;
+    mx = fmaxf(mx, v[k]);
+  }
+  mx = wave_max(mx);
+#pragma unroll
+  for (int k = 0; k < VPL; ++k) v[k] = lane + 64 * k < n ? __expf(v[k] - mx) : -1.0f;   // -1: not an element
+  wave_select_vals<VPL>(v, n, gamma, wd);
+}
+
 // One wave per row of logits ev[r][0..i0+r]: softmax weights, selection
 // ([E] 3.1 cumulative-gamma rule), block 0 and the diagonal forced in, and the
 // row's bit set written to rowbits.  words: LDS, (blockDim / 64) * nw32 words.
+// Rows of up to 64 * MAXV values select in registers (the form sized to the row); longer rows
+// keep their weights in LDS.
 template <int MAXV>
 __device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev, uint32_t *words) {
   const int N = a.N, lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwv = blockDim.x >> 6;
@@ -120,15 +141,25 @@ __device__ void select_rows(const QaArgs &a, int h, int i0, int rows, float *ev,
   for (int r = wave; r < rows; r += nwv) {
     const int i = i0 + r, n = i + 1;
     float *x = ev + (size_t)r * N;
-    float mx = kNegBig;
-#pragma unroll 8
-    for (int j = lane; j < n; j += 64) mx = fmaxf(mx, x[j]);
-    mx = wave_max(mx);
-#pragma unroll 8
-    for (int j = lane; j < n; j += 64) x[j] = expf(x[j] - mx);
     const int nwr = (i >> 5) + 1;
     for (int w = lane; w < nwr; w += 64) wd[w] = 0u;
-    wave_select<MAXV>(x, n, a.gamma, wd);
+    if (n <= 256) {
+      select_row_reg<4>(x, n, a.gamma, wd);
+    } else if (n <= 512) {
+      select_row_reg<8>(x, n, a.gamma, wd);
+    } else if (n <= 1024) {
+      select_row_reg<16>(x, n, a.gamma, wd);
+    } else if (MAXV == 32 && n <= 2048) {
+      select_row_reg<32>(x, n, a.gamma, wd);
+    } else {
+      float mx = kNegBig;
+#pragma unroll 8
+      for (int j = lane; j < n; j += 64) mx = fmaxf(mx, x[j]);
+      mx = wave_max(mx);
+#pragma unroll 8
+      for (int j = lane; j < n; j += 64) x[j] = __expf(x[j] - mx);
+      wave_select_lds(x, n, a.gamma, wd);
+    }
     if (lane == 0) {
       atomicOr(&wd[0], 1u);
       atomicOr(&wd[i >> 5], 1u << (i & 31));
