@@ -145,13 +145,15 @@ def test_attn_gamma_one_is_dense_causal():
     assert mx <= MAXABS and rms <= RMS, (mx, rms)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(2, 2), (4, 2), (6, 2)], ids=["G1", "G2", "G3"])
-def test_attn_score_spike(Hq, Hkv):
+@pytest.mark.parametrize("b,Hq,Hkv", [(128, 2, 2), (128, 4, 2), (128, 6, 2), (64, 4, 2), (64, 6, 2)],
+                         ids=["G1", "G2", "G3", "b64-G2", "b64-G3"])
+def test_attn_score_spike(b, Hq, Hkv):
     """Keys of block 0 scaled by 3: rows that meet them after other keys see scores 80 to 140
     (log2 units) above everything before, far beyond the headroom the kernel allows before it
-    rescales O to a raised reference maximum; dense causal index, oracle attention."""
-    say(f"attn score spike Hq={Hq} Hkv={Hkv}")
-    c = cfg(S=1024, Hq=Hq, Hkv=Hkv)
+    rescales O to a raised reference maximum; dense causal index, oracle attention.  With b = 64
+    and two or three heads per group the chunks hold one 64-key block."""
+    say(f"attn score spike b={b} Hq={Hq} Hkv={Hkv}")
+    c = cfg(S=1024, b=b, Hq=Hq, Hkv=Hkv)
     L = gen.make(c)
     kf = L.f32("k")
     kf[:, :c.b] *= 3.0
