@@ -498,7 +498,7 @@ struct MergeArgs {
   float sigma;
 };
 constexpr int kMergeThreads = 256;
-constexpr int kMergeBlocks = 64;
+constexpr int kMergeBlocks = 16;      // key blocks per k_ig_merge workgroup: four per wave
 constexpr int kRowSplit = 4;          // threads per row in k_ig_rows
 
 template <int B, bool I8>
@@ -561,43 +561,42 @@ __global__ void __launch_bounds__(kMergeThreads) k_ig_merge(MergeArgs a) {
     w[c - c_lo][r] = exp2f(a.ml[((size_t)h * a.nch + c) * B + r].x - rm.x) * rm.y;
   }
   __syncthreads();
-  // block masses: one wave per block, each lane RPL consecutive rows (one 16- or 8-byte load),
-  // four blocks in flight per wave
+  // block masses and pooled-estimate logits: one wave per block, each lane RPL consecutive rows
+  // (one 16- or 8-byte load) and two columns of the block's K-bar row; the wave's four blocks
+  // have all their loads in flight together
   constexpr int RPL = B / 64;
-  for (int k0 = wave * 4; k0 < nb; k0 += NWV * 4) {
-    float lo[4], hi[4];
+  static_assert(kMergeBlocks == 4 * NWV, "four blocks per wave");
+  const float2 qv = *(const float2 *)(a.qlast + (size_t)h * 128 + 2 * lane);
+  float lo[4], hi[4], dq[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      lo[q] = 0.0f;
-      hi[q] = 0.0f;
-      const int k = k0 + q;
-      if (k < nb) {
-        const int j = j0 + k, c = j / a.CB - c_lo;
-        const float2 *src = a.lohi + ((size_t)h * N + j) * B + RPL * lane;
+  for (int q = 0; q < 4; ++q) {
+    lo[q] = 0.0f;
+    hi[q] = 0.0f;
+    dq[q] = 0.0f;
+    const int k = 4 * wave + q;
+    if (k < nb) {
+      const int j = j0 + k, c = j / a.CB - c_lo;
+      const float2 *src = a.lohi + ((size_t)h * N + j) * B + RPL * lane;
+      const float2 kv = *(const float2 *)(a.kbar + ((size_t)g * N + j) * 128 + 2 * lane);
 #pragma unroll
-        for (int e = 0; e < RPL; ++e) {
-          const float2 v = src[e];
-          const float wv = w[c][RPL * lane + e];
-          lo[q] += v.x * wv;
-          hi[q] += v.y * wv;
-        }
+      for (int e = 0; e < RPL; ++e) {
+        const float2 v = src[e];
+        const float wv = w[c][RPL * lane + e];
+        lo[q] += v.x * wv;
+        hi[q] += v.y * wv;
       }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float sl = wave_sum(lo[q]), sh = wave_sum(hi[q]);
-      if (lane == 0 && k0 + q < nb) {
-        a.lo[(size_t)h * N + j0 + k0 + q] = sl;
-        a.hi[(size_t)h * N + j0 + k0 + q] = sh;
-      }
+      dq[q] = qv.x * kv.x + qv.y * kv.y;
     }
   }
-  // pooled-estimate logits of the range's blocks: one wave per block, two columns per lane
-  const float2 qv = *(const float2 *)(a.qlast + (size_t)h * 128 + 2 * lane);
-  for (int k = wave; k < nb; k += NWV) {
-    const float2 kv = *(const float2 *)(a.kbar + ((size_t)g * N + j0 + k) * 128 + 2 * lane);
-    const float d = wave_sum(qv.x * kv.x + qv.y * kv.y);
-    if (lane == 0) a.pe[(size_t)h * N + j0 + k] = a.sigma * d;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float sl = wave_sum(lo[q]), sh = wave_sum(hi[q]), d = wave_sum(dq[q]);
+    const int k = 4 * wave + q;
+    if (lane == 0 && k < nb) {
+      a.lo[(size_t)h * N + j0 + k] = sl;
+      a.hi[(size_t)h * N + j0 + k] = sh;
+      a.pe[(size_t)h * N + j0 + k] = a.sigma * d;
+    }
   }
 }
 
