@@ -36,6 +36,7 @@ import argparse
 import csv
 import hashlib
 import json
+import re
 import os
 import platform
 import sys
@@ -83,6 +84,20 @@ def attn_source_hash() -> str:
     return hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
 
 
+# the kernels of one fp_index call (name prefixes) and the sources they are built from
+INDEX_KERNELS = ("k_ig_stream<", "k_ig_rows<", "k_ig_merge<", "k_ig_finalize<", "k_pool_q<", "k_qa_rows",
+                 "k_jobs<", "k_scan_sort", "k_rank_jobs<")
+INDEX_SRCS = [os.path.join(ROOT, "dynamic_block_sparse_flexprefill_amd", "csrc", f)
+              for f in ("ig_stats.hip", "ig_finalize.hip", "ig_qa.hip", "csr_jobs.hip", "fp_select.hpp", "fp_common.hpp")]
+
+
+def index_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in INDEX_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
 def traffic_file(name: str) -> str:
     return os.path.join(ROOT, "profiles", f"traffic_{name}.json")
 
@@ -107,8 +122,22 @@ def _counter(csv_path: str, name_part: str) -> float:
     return sum(vals) / len(vals)
 
 
+def _counters_by_kernel(csv_path: str, prefixes) -> dict:
+    """Mean counter value per dispatch of every kernel whose name (after its namespace) starts with
+    one of the prefixes, keyed by the kernel's full name."""
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        m = re.search(r"\b(k_[a-z0-9_]+)(<|\()", r["Kernel_Name"])
+        short = m.group(1) + m.group(2) if m else ""
+        if any(short.startswith(p) for p in prefixes):
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in per.items()}
+
+
 def traffic_from(d: str, config: str):
-    """Combine the four counter passes in directory d into profiles/traffic_<config>.json."""
+    """Combine the four counter passes in directory d into profiles/traffic_<config>.json: HBM
+    bytes per launch of the attention kernel and per call of fp_index (the sum over its kernels of
+    each kernel's mean per dispatch)."""
     f = lambda stem: os.path.join(d, f"{stem}_counter_collection.csv")
     copy_kib = COPY_BYTES / 1024.0
     fetch_factor = copy_kib / _counter(f("copy_FETCH_SIZE"), "copyBuffer")
@@ -117,10 +146,18 @@ def traffic_from(d: str, config: str):
     kname = ATTN_KERNEL[gen.CONFIGS[config].int8]
     fetch = _counter(f("bench_FETCH_SIZE"), kname)
     write = _counter(f("bench_WRITE_SIZE"), kname)
+    fi = _counters_by_kernel(f("bench_FETCH_SIZE"), INDEX_KERNELS)
+    wi = _counters_by_kernel(f("bench_WRITE_SIZE"), INDEX_KERNELS)
+    if not fi or set(fi) != set(wi):
+        raise RuntimeError("the index kernels differ between the two counter passes")
+    index_rec = {"source_sha256": index_source_hash(),
+                 "kernels": {k: {"fetch_size_kib": fi[k], "write_size_kib": wi[k]} for k in sorted(fi)},
+                 "bytes_per_call": sum(fi.values()) * 1024 * fetch_factor + sum(wi.values()) * 1024 * write_factor}
     rec = {"config": config, "kernel": kname, "attn_source_sha256": attn_source_hash(),
            "fetch_size_kib": fetch, "write_size_kib": write,
            "fetch_factor": fetch_factor, "write_factor": write_factor,
            "bytes_per_launch": fetch * 1024 * fetch_factor + write * 1024 * write_factor,
+           "index": index_rec,
            "commands": [
                f"rocprofv3 --pmc {c} --output-format csv -d D -o copy_{c} -- python3 bench.py --copy-calibration"
                for c in ("FETCH_SIZE", "WRITE_SIZE")] + [
@@ -140,6 +177,27 @@ def measured_traffic(config: str):
     if rec.get("attn_source_sha256") != attn_source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_index_traffic(config: str):
+    """HBM bytes per fp_index call from the counter passes, or None if stale or absent."""
+    try:
+        rec = json.load(open(traffic_file(config)))["index"]
+    except (OSError, ValueError, KeyError, TypeError):
+        return None
+    if rec.get("source_sha256") != index_source_hash():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def index_roofline(rec: dict, config: str) -> dict:
+    """The index stage against HBM on its algorithmic bytes, with the measured bytes per call (and
+    the rate on them) where counter passes of the current index sources exist."""
+    r = dict(bound="hbm", kernel="fp_index (all kernels)", **rec["index"])
+    t = measured_index_traffic(config)
+    r["traffic"] = t
+    r["achieved_on_traffic"] = None if t is None else round(t / (rec["stages_ms"]["index_median"] * 1e-3) / 1e9, 1)
+    return r
 
 
 def log(*a):
@@ -447,7 +505,7 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "kernel": ATTN_KERNEL[c.int8].rstrip("<") + " (fp_attn)",
                      "achieved": main_rec["attn"]["achieved"], "peak": main_rec["attn"]["peak"], "unit": "TFLOP/s",
                      "frac": main_rec["attn"]["frac"], "traffic": measured_traffic(c.name)},
-        "roofline_index": dict(bound="hbm", kernel="fp_index (all kernels)", **main_rec["index"]),
+        "roofline_index": index_roofline(main_rec, c.name),
         "stages_ms": main_rec["stages_ms"],
         "status_after_timing": status,
         "density": main_rec["density"],

@@ -36,9 +36,14 @@ def test_traffic_from_counter_passes(tmp_path, monkeypatch):
     _counters(tmp_path / "copy_FETCH_SIZE_counter_collection.csv", [("__amd_rocclr_copyBuffer", kib / 2)] * 3)
     _counters(tmp_path / "copy_WRITE_SIZE_counter_collection.csv", [("__amd_rocclr_copyBuffer", kib)] * 3)
     attn = "void fp::(anonymous namespace)::k_attn_dl<768, false>(fp::AttnArgs, int)"
+    st = "void fp::(anonymous namespace)::k_ig_stream<128, 768, 1, false>(fp::(anonymous namespace)::StreamArgs)"
+    qa = "void fp::(anonymous namespace)::k_qa_rows16<128, false, false, false>(fp::(anonymous namespace)::QaArgs)"
+    sort = "fp::(anonymous namespace)::k_scan_sort(fp::(anonymous namespace)::ScanJob, int)"
+    other = "void at::native::vectorized_elementwise_kernel<4, at::native::FillFunctor<int> >(int)"
     _counters(tmp_path / "bench_FETCH_SIZE_counter_collection.csv",
-              [(attn, 1000.0), (attn, 1200.0), ("void fp::k_ig_stream<128, 768, 1, false>(args)", 5.0)])
-    _counters(tmp_path / "bench_WRITE_SIZE_counter_collection.csv", [(attn, 300.0), (attn, 300.0)])
+              [(attn, 1000.0), (attn, 1200.0), (st, 5.0), (st, 7.0), (qa, 10.0), (sort, 1.0), (other, 99.0)])
+    _counters(tmp_path / "bench_WRITE_SIZE_counter_collection.csv",
+              [(attn, 300.0), (attn, 300.0), (st, 2.0), (qa, 4.0), (sort, 0.5), (other, 99.0)])
     out = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "traffic_file", lambda name: str(out))
     bench.traffic_from(str(tmp_path), "3b-128k")
@@ -48,8 +53,14 @@ def test_traffic_from_counter_passes(tmp_path, monkeypatch):
     # per launch: the mean over the kernel's dispatches, each counter scaled by its factor
     assert rec["bytes_per_launch"] == pytest.approx(1100.0 * 1024 * 2.0 + 300.0 * 1024 * 1.0)
     assert bench.measured_traffic("3b-128k") == pytest.approx(rec["bytes_per_launch"])
+    # per index call: each index kernel's mean per dispatch, summed over the kernels (not the fill)
+    assert sorted(rec["index"]["kernels"]) == sorted([st, qa, sort])
+    assert rec["index"]["bytes_per_call"] == pytest.approx((6.0 + 10.0 + 1.0) * 1024 * 2.0 + (2.0 + 4.0 + 0.5) * 1024)
+    assert bench.measured_index_traffic("3b-128k") == pytest.approx(rec["index"]["bytes_per_call"])
     monkeypatch.setattr(bench, "attn_source_hash", lambda: "0" * 64)
     assert bench.measured_traffic("3b-128k") is None
+    monkeypatch.setattr(bench, "index_source_hash", lambda: "0" * 64)
+    assert bench.measured_index_traffic("3b-128k") is None
 
 
 def test_traffic_needs_a_dispatch_of_the_kernel(tmp_path):
