@@ -10,10 +10,9 @@
 // normalises attention scores block-wise to avoid overflow).
 //
 // W8A8 (explainer sections 3.3 and 4.2): Q.K^T on the int8 matrix cores with
-// int32 accumulation, scaled by sigma * sQ[t] * sK[k]; P.V in bf16 with the
-// int8 values of V (exact in bf16) and sV folded into P.  The int8 V codes are
-// widened to bf16 once per call (k_widen_v8), so the chunk stream stages V
-// exactly as in the bf16 form.
+// int32 accumulation, scaled by sigma * sQ[t] * sK[k]; P.V in bf16 against V
+// taken as bf16(sV[k] * v8[k]), formed once per call (k_widen_v8), so the chunk
+// stream stages V and runs P.V exactly as in the bf16 form.
 //
 // Kernel layout.  The explainer's section 2.2 notes that grouped-query heads
 // re-fetch the same K/V blocks; section 3.2 schedules sparse attention from a
@@ -208,18 +207,19 @@ __device__ __forceinline__ void dl_issue8_2(const uint8_t *ka, const uint8_t *va
   }
 }
 
-// fp_attn_i8: the int8 V codes widened to bf16 once per call (exact: |v| <= 127), in the key-major
-// layout the chunk stream stages from; the value scales stay separate (folded into P).  Thread t
-// converts the 16 codes at byte 16 t.
-__global__ void __launch_bounds__(256) k_widen_v8(const uint8_t *v8, uint16_t *vw, size_t n16) {
+// fp_attn_i8: the int8 V codes times their per-token scale, rounded to bf16 once per call, in the
+// key-major layout the chunk stream stages from; P.V then runs exactly as in the bf16 form.  Thread
+// t converts the 16 codes at byte 16 t (all of one token's row: 128 codes are 8 threads).
+__global__ void __launch_bounds__(256) k_widen_v8(const uint8_t *v8, const float *sv, uint16_t *vw, size_t n16) {
   const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= n16) return;
   const u32x4 in = *(const u32x4 *)(v8 + 16 * t);
+  const float sc = sv[t >> 3];
   uint32_t w[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const uint32_t word = in[k >> 1] >> (16 * (k & 1));
-    w[k] = pack_bf16x2((float)(int8_t)(word & 0xffu), (float)(int8_t)((word >> 8) & 0xffu));
+    w[k] = pack_bf16x2(sc * (float)(int8_t)(word & 0xffu), sc * (float)(int8_t)((word >> 8) & 0xffu));
   }
   u32x4 *o = (u32x4 *)(vw + 16 * t);
   o[0] = u32x4{w[0], w[1], w[2], w[3]};
@@ -486,12 +486,14 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
       if (run_a || run_b) {
         const bool diag = key0 + kChunkDl - 1 > qtok0;
         const uint32_t kp = opaque(lds_addr(kbuf[buf]) + kl);
+        // int8 K rows: KL<true>::Stride bytes each
+        const uint32_t kp8 = I8 ? opaque(lds_addr(kbuf[buf]) + (lane & 31) * KL<true>::Stride + 16 * hf) : 0u;
         uint32_t vp[4];
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) vp[dt] = opaque(lds_addr(vbuf[buf]) + vl[dt]);
-        const float *sks = sbuf[buf], *svs = sbuf[buf] + kChunkDl;
+        const float *sks = sbuf[buf];
         bool piped = false;
-        if constexpr (!I8 && !PAIR && NT <= 768) {
+        if constexpr (!PAIR && NT <= 768) {
           if (!diag) {
             // Every key of the chunk precedes the wave's first query: no tile is masked or
             // skipped, and the four tiles run software-pipelined with P.V one tile behind.
@@ -502,10 +504,26 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             piped = true;
             auto qk = [&](int kb) {
               f32x16 acc = {};
+              if constexpr (!I8) {
 #pragma unroll
-              for (int s = 0; s < 8; ++s)
-                acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s),
-                                qf[s], acc);
+                for (int s = 0; s < 8; ++s)
+                  acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s),
+                                  qf[s], acc);
+              } else {
+                // int32 tile on the int8 matrix cores (K rows of KL<true>::Stride bytes), times
+                // the key scales of its rows
+                i32x16 ia = {};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                  ia = mfma_i8(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp8 + kb * KL<true>::Stride + 32 * s),
+                               qf[s], ia);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const f32x4 s4 = *(const f32x4 *)(sks + kb + 8 * q + 4 * hf);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) acc[4 * q + e] = (float)ia[4 * q + e] * s4[e];
+                }
+              }
               return acc;
             };
             // softmax weights of one tile (bf16 pairs), first against the current reference
@@ -671,18 +689,13 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
               for (int s2 = 0; s2 < 2; ++s2)
                 o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
           } else {
-            // weights (summed into l) times the value scales, then P.V as in the bf16 form
+            // weights (summed into l), then P.V as in the bf16 form (the value scales are in the
+            // widened V)
             float pv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               pv[r] = fast_exp2(fmaf(x[r], qsc, -m));
               l += pv[r];
-            }
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 s4 = *(const f32x4 *)(svs + kb + 8 * q + 4 * hf);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) pv[4 * q + e] *= s4[e];
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2)
@@ -923,7 +936,7 @@ hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, c
   if (i8) {   // the chunk stream reads V from its bf16 widening
     if (!vw) return hipErrorInvalidValue;
     const size_t n16 = (size_t)p.Hkv * p.S * 128 / 16;
-    hipLaunchKernelGGL(k_widen_v8, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st, (const uint8_t *)V, vw, n16);
+    hipLaunchKernelGGL(k_widen_v8, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, st, (const uint8_t *)V, sV, vw, n16);
     a.V = (const uint8_t *)vw;
   }
   a.sQ = sQ; a.sK = sK; a.sV = sV;

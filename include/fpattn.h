@@ -326,8 +326,8 @@ int fp_attn_split(const fp_shape *shape, const void *Q, const void *K, const voi
 
 /*
  * W8A8 block-sparse attention ([E] 3.3, 4.2; [R] 3.3).  Scores use the exact
- * int8 dot product scaled by sigma * sQ * sK; P.V uses bf16 P against the
- * int8 values of V (exact in bf16) with the per-token scale sV folded into P.
+ * int8 dot product scaled by sigma * sQ * sK; P.V uses bf16 P against V taken
+ * as bf16(sV * v8), rounded once per call.
  *   V8: device int8 [Hkv, S, d], sV: device fp32 [Hkv, S]; O: device bf16.
  *   ws: at least fp_workspace_bytes(shape, 1) bytes (the call first widens V8
  *   to bf16 in it).
