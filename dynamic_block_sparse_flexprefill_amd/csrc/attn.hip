@@ -616,6 +616,131 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
             pv(kChunkDl - 32, pp);
           }
         }
+        if constexpr (PAIR && NT <= 512) {
+          // Two 64-key blocks: the halves that have work for this wave run pipelined (two or four
+          // tiles) when all their keys precede the wave's first query.  (Up to 8 waves: the two
+          // pipelined bodies need more than the 12-wave register budget.)
+          if ((run_a || run_b) && (!run_a || key0 + 63 <= qtok0) && (!run_b || key2 + 63 <= qtok0)) {
+            piped = true;
+            auto qk = [&](int kb) {
+              f32x16 acc = {};
+              if constexpr (!I8) {
+#pragma unroll
+                for (int s = 0; s < 8; ++s)
+                  acc = mfma_bf16(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp + kb * dl::KRow + 32 * s),
+                                  qf[s], acc);
+              } else {
+                // int32 tile on the int8 matrix cores (K rows of KL<true>::Stride bytes), times
+                // the key scales of its rows
+                i32x16 ia = {};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                  ia = mfma_i8(*(const __attribute__((address_space(3))) u32x4 *)(size_t)(kp8 + kb * KL<true>::Stride + 32 * s),
+                               qf[s], ia);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const f32x4 s4 = *(const f32x4 *)(sks + kb + 8 * q + 4 * hf);
+#pragma unroll
+                  for (int e = 0; e < 4; ++e) acc[4 * q + e] = (float)ia[4 * q + e] * s4[e];
+                }
+              }
+              return acc;
+            };
+            // softmax weights of one tile (bf16 pairs), first against the current reference
+            // maximum m with no maximum pass: a score above m + kRescaleDl gives a weight above
+            // 2^kRescaleDl, so the tile's sum reaching that bound (or infinity, as while m is
+            // unset) is the only case that can need a new maximum.  Only then is the tile's
+            // maximum taken and, where it exceeds m + kRescaleDl, m raised and the weights redone;
+            // m therefore moves exactly as under a maximum pass of every tile.
+            auto weights = [&](const f32x16 &sc, u32x4 pf[2], float &alpha, bool ilv) {
+              auto eval = [&]() {
+                float lt = 0.0f;
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                  for (int w = 0; w < 4; ++w) {
+                    const uint32_t pw = pack_bf16x2(fast_exp2(fmaf(sc[8 * s2 + 2 * w], qsc, -m)),
+                                                    fast_exp2(fmaf(sc[8 * s2 + 2 * w + 1], qsc, -m)));
+                    pf[s2][w] = pw;
+                    lt = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pw),
+                                                         __builtin_bit_cast(bf16x2_t, 0x3f803f80u), lt, false);
+                  }
+                return lt;
+              };
+              float lt = eval();
+              if (ilv) {
+                // one basic block holds this tile's products, the previous tile's P.V products and
+                // this tile's weights: the products each follow their operand reads (one ahead),
+                // and the weights fill the P.V products' read waits
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int s = 0; s < 7; ++s) {
+                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                  __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int s = 0; s < 7; ++s) {
+                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                  __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              }
+              bool grew = false;
+              if (__any(!(lt < kRescaleSumDl))) {
+                float mx = fmaxf(sc[0], sc[1]);
+#pragma unroll
+                for (int r = 2; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+                mx = fmaxf(mx, fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]))) * qsc;
+                const bool grow = mx > m + kRescaleDl;
+                if (__any(grow)) {
+                  const float mnew = grow ? mx : m;
+                  alpha = fast_exp2(m - mnew);           // exactly 1 where the maximum stays
+                  m = mnew;
+                  l *= alpha;
+                  lt = eval();
+                  grew = true;
+                }
+              }
+              l += lt;
+              return grew;
+            };
+            auto pv = [&](int kb, const u32x4 pf[2]) {
+#pragma unroll
+              for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+                  o[dt] = mfma_bf16(tr_pair(vp[dt] + (kb + 16 * s2) * 256), pf[s2], o[dt]);
+            };
+            auto run_tiles = [&](int t0, auto ntl) {
+              constexpr int NTL = decltype(ntl)::value;
+              u32x4 pp[2];
+              float alpha;
+              if (weights(qk(32 * t0), pp, alpha, false)) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+              }
+#pragma unroll
+              for (int kt = 1; kt < NTL; ++kt) {
+                const f32x16 sc = qk(32 * (t0 + kt));
+                pv(32 * (t0 + kt - 1), pp);
+                u32x4 pn[2];
+                if (weights(sc, pn, alpha, true)) {
+#pragma unroll
+                  for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+                }
+                pp[0] = pn[0];
+                pp[1] = pn[1];
+              }
+              pv(32 * (t0 + NTL - 1), pp);
+            };
+            if (run_a && run_b) run_tiles(0, std::integral_constant<int, 4>{});
+            else run_tiles(run_a ? 0 : 2, std::integral_constant<int, 2>{});
+          }
+        }
 #pragma unroll 1
         for (int kt = 0; kt < (piped ? 0 : kChunkDl / 32); ++kt) {
           const int kb = kt * 32;                  // LDS row of the tile
