@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.fp_strerror.restype = ctypes.c_char_p
         L.fp_strerror.argtypes = [ctypes.c_int]
         L.fp_workspace_bytes.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        L.fp_batch_workspace_bytes.argtypes = [sp, ctypes.c_int, ctypes.POINTER(ctypes.c_int32), ctypes.c_int,
+                                               ctypes.POINTER(ctypes.c_size_t)]
         L.fp_csr_capacity.restype = ctypes.c_int64
         L.fp_csr_capacity.argtypes = [sp]
         L.fp_job_capacity.restype = ctypes.c_int64
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         L.fp_index_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, f, f, op, _P, ctypes.c_size_t, _P]
         L.fp_attn_i8_batch.argtypes = [sp, ctypes.c_int, lp, _P, _P, _P, _P, _P, _P, op, _P, _P,
                                        ctypes.c_size_t, _P]
-        for name in ("fp_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
+        for name in ("fp_workspace_bytes", "fp_batch_workspace_bytes", "fp_index", "fp_index_i8", "fp_build_jobs", "fp_attn",
                      "fp_attn_i8", "fp_probe_qk_i8", "fp_index_static", "fp_index_shared", "fp_block_uses", "fp_attn_split_workspace_bytes", "fp_attn_split", "fp_qkv_project", "fp_index_pooled", "fp_index_batch", "fp_attn_batch",
                      "fp_index_i8_batch", "fp_attn_i8_batch"):
             getattr(L, name).restype = ctypes.c_int
@@ -116,6 +118,18 @@ def workspace_bytes(shape: FpShape, variant: int = 1) -> int:
     rc = lib().fp_workspace_bytes(ctypes.byref(shape), variant, ctypes.byref(n))
     if rc:
         raise FpError(rc, "fp_workspace_bytes")
+    return n.value
+
+
+def batch_workspace_bytes(shape: FpShape, seqlens, variant: int = 1) -> int:
+    """fp_batch_workspace_bytes: the workspace with which every run of equal-length sequences of a
+    batch runs as one call (shape.S is ignored)."""
+    lens = [int(S) for S in seqlens]
+    n = ctypes.c_size_t(0)
+    rc = lib().fp_batch_workspace_bytes(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens), variant,
+                                        ctypes.byref(n))
+    if rc:
+        raise FpError(rc, "fp_batch_workspace_bytes")
     return n.value
 
 
@@ -195,15 +209,16 @@ class Index:
 
 
 class Workspace:
-    """A device byte buffer sized by fp_workspace_bytes for a shape."""
+    """A device byte buffer sized by fp_workspace_bytes for a shape, or with seqlens given, by
+    fp_batch_workspace_bytes for a batch of sequences of those lengths."""
 
-    def __init__(self, shape: FpShape, device):
-        self.nbytes = workspace_bytes(shape, 1)
+    def __init__(self, shape: FpShape, device, seqlens=None):
+        self.nbytes = workspace_bytes(shape, 1) if seqlens is None else batch_workspace_bytes(shape, seqlens, 1)
         self.buf = torch.empty(max(self.nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def _ws(shape, ws, device):
-    return Workspace(shape, device) if ws is None else ws
+def _ws(shape, ws, device, seqlens=None):
+    return Workspace(shape, device, seqlens) if ws is None else ws
 
 
 def index(Q: torch.Tensor, K: torch.Tensor, b: int, gamma: float, tau: float, *, stats: bool = False,
@@ -457,17 +472,21 @@ def unpack(t: torch.Tensor, seqlens, H: int, d: int = 128) -> list:
 
 
 def index_batch(Q: torch.Tensor, K: torch.Tensor, seqlens, b: int, Hq: int, Hkv: int, gamma: float,
-                tau: float, *, d: int = 128, stats: bool = False, ws: Optional[Workspace] = None,
-                stream=None) -> list:
+                tau: float, *, d: int = 128, stats: bool = False, outs: Optional[list] = None,
+                ws: Optional[Workspace] = None, stream=None) -> list:
     """fp_index_batch: one Index per sequence of a ragged batch; Q (K) holds the sequences'
-    [Hq, S_s, d] ([Hkv, S_s, d]) bf16 blocks one after another, as 1-D tensors."""
+    [Hq, S_s, d] ([Hkv, S_s, d]) bf16 blocks one after another, as 1-D tensors.  outs: the
+    sequences' Index objects to write (e.g. with capacities of the caller's choice)."""
     lens = [int(S) for S in seqlens]
     tot = sum(lens)
     _check(Q, "Q", torch.bfloat16, (Hq * tot * d,))
     _check(K, "K", torch.bfloat16, (Hkv * tot * d,))
-    outs = [Index.empty(shape_of(S, b, Hq, Hkv, d), Q.device, stats=stats) for S in lens]
-    shape = shape_of(max(lens), b, Hq, Hkv, d)     # S is ignored; the longest sizes the workspace
-    ws = _ws(shape, ws, Q.device)
+    if outs is None:
+        outs = [Index.empty(shape_of(S, b, Hq, Hkv, d), Q.device, stats=stats) for S in lens]
+    elif len(outs) != len(lens):
+        raise TypeError("one Index per sequence is needed")
+    shape = shape_of(max(lens), b, Hq, Hkv, d)     # S is ignored
+    ws = _ws(shape, ws, Q.device, lens)
     arr = (FpIndexOut * len(lens))(*[o.c_struct() for o in outs])
     rc = lib().fp_index_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens), _ptr(Q),
                               _ptr(K), gamma, tau, arr, _ptr(ws.buf), ws.nbytes, _stream(stream))
@@ -491,7 +510,7 @@ def attn_batch(Q, K, V, seqlens, idxs: list, *, out: Optional[torch.Tensor] = No
     O = torch.empty_like(Q) if out is None else out
     _check(O, "O", torch.bfloat16, (Hq * tot * d,))
     shape = shape_of(max(lens), b, Hq, Hkv, d)
-    ws = _ws(shape, ws, Q.device)
+    ws = _ws(shape, ws, Q.device, lens)
     arr = (FpIndexOut * len(lens))(*[ix.c_struct() for ix in idxs])
     rc = lib().fp_attn_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens), _ptr(Q),
                              _ptr(K), _ptr(V), arr, _ptr(O), _ptr(ws.buf), ws.nbytes, _stream(stream))
@@ -501,7 +520,8 @@ def attn_batch(Q, K, V, seqlens, idxs: list, *, out: Optional[torch.Tensor] = No
 
 
 def index_i8_batch(Q8, sQ, K8, sK, seqlens, b: int, Hq: int, Hkv: int, gamma: float, tau: float, *,
-                   d: int = 128, stats: bool = False, ws: Optional[Workspace] = None, stream=None) -> list:
+                   d: int = 128, stats: bool = False, outs: Optional[list] = None, ws: Optional[Workspace] = None,
+                   stream=None) -> list:
     """fp_index_i8_batch: index_batch for W8A8 inputs; Q8 / K8 int8 and their per-token scales
     sQ / sK fp32, each packed sequence after sequence as 1-D tensors."""
     lens = [int(S) for S in seqlens]
@@ -510,9 +530,12 @@ def index_i8_batch(Q8, sQ, K8, sK, seqlens, b: int, Hq: int, Hkv: int, gamma: fl
     _check(K8, "K8", torch.int8, (Hkv * tot * d,))
     _check(sQ, "sQ", torch.float32, (Hq * tot,))
     _check(sK, "sK", torch.float32, (Hkv * tot,))
-    outs = [Index.empty(shape_of(S, b, Hq, Hkv, d), Q8.device, stats=stats) for S in lens]
+    if outs is None:
+        outs = [Index.empty(shape_of(S, b, Hq, Hkv, d), Q8.device, stats=stats) for S in lens]
+    elif len(outs) != len(lens):
+        raise TypeError("one Index per sequence is needed")
     shape = shape_of(max(lens), b, Hq, Hkv, d)
-    ws = _ws(shape, ws, Q8.device)
+    ws = _ws(shape, ws, Q8.device, lens)
     arr = (FpIndexOut * len(lens))(*[o.c_struct() for o in outs])
     rc = lib().fp_index_i8_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens),
                                  _ptr(Q8), _ptr(sQ), _ptr(K8), _ptr(sK), gamma, tau, arr, _ptr(ws.buf),
@@ -540,7 +563,7 @@ def attn_i8_batch(Q8, sQ, K8, sK, V8, sV, seqlens, idxs: list, *, out: Optional[
     O = torch.empty(Hq * tot * d, dtype=torch.bfloat16, device=Q8.device) if out is None else out
     _check(O, "O", torch.bfloat16, (Hq * tot * d,))
     shape = shape_of(max(lens), b, Hq, Hkv, d)
-    ws = _ws(shape, ws, Q8.device)
+    ws = _ws(shape, ws, Q8.device, lens)
     arr = (FpIndexOut * len(lens))(*[ix.c_struct() for ix in idxs])
     rc = lib().fp_attn_i8_batch(ctypes.byref(shape), len(lens), (ctypes.c_int32 * len(lens))(*lens),
                                 _ptr(Q8), _ptr(sQ), _ptr(K8), _ptr(sK), _ptr(V8), _ptr(sV), arr, _ptr(O),

@@ -892,8 +892,10 @@ __global__ void __launch_bounds__(NT) k_attn_dl(AttnArgs a, const int4 *utab, in
 }
 
 // Unit table {job, first job-list entry, entry count, rotated start chunk} and a zeroed claim counter.
+// The rotation hashes the job's index within its sequence (jps jobs per sequence), so a sequence run
+// side by side with others visits its chunks in the same order as when run alone.
 __global__ void k_attn_prep(const int32_t *job_order, const int32_t *job_ptr, int nunits, int parts,
-                            int nck, int4 *utab, unsigned int *ctr) {
+                            int nck, int jps, int4 *utab, unsigned int *ctr) {
   const int u = blockIdx.x * blockDim.x + threadIdx.x;
   if (u == 0) ctr[0] = 0u;
   if (u >= nunits) return;
@@ -901,7 +903,7 @@ __global__ void k_attn_prep(const int32_t *job_order, const int32_t *job_ptr, in
   const int p0 = job_ptr[job], n = job_ptr[job + 1] - p0;
   const int total = nck > 0 ? n * nck : (n + 1) >> 1;    // chunks (nck = 0: two 64-key blocks each)
   // chunks start at a per-job offset so that workgroups do not all fetch the same (sink) blocks at once
-  const int rot = total > 0 ? (int)(((unsigned)job * 2654435761u) % (unsigned)total) : 0;
+  const int rot = total > 0 ? (int)(((unsigned)(job % jps) * 2654435761u) % (unsigned)total) : 0;
   utab[u] = int4{job, p0, n, rot};
 }
 
@@ -1018,9 +1020,7 @@ hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4
   const int jobs = p.Hkv * p.N;
   const int nsplit = SPLIT ? std::min(split[0], jobs) : 0, nseg = SPLIT ? split[1] : 1;
   const int nunits = (jobs + nsplit * (nseg - 1)) * a.parts;
-  int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_dl<NT, I8, PAIR, SPLIT>, NT, 0) != hipSuccess)
-    per_cu = 0;
+  const int per_cu = occupancy_per_cu((const void *)k_attn_dl<NT, I8, PAIR, SPLIT>, NT);
   const int cus = cu_count();
   const int grid = std::max(1, std::min(nunits, std::max(1, per_cu) * std::max(1, cus)));
   if (SPLIT)
@@ -1028,7 +1028,7 @@ hipError_t run_attn_dl(const Plan &p, const AttnArgs &a, unsigned int *ctr, int4
                        nunits, a.parts, p.B / kChunkDl, nsplit, nseg, utab, ctr);
   else
     hipLaunchKernelGGL(k_attn_prep, dim3((nunits + 255) / 256), dim3(256), 0, st, a.job_order, a.job_ptr,
-                       nunits, a.parts, p.B / kChunkDl, utab, ctr);
+                       nunits, a.parts, p.B / kChunkDl, p.seq_groups * p.N, utab, ctr);
   hipLaunchKernelGGL((k_attn_dl<NT, I8, PAIR, SPLIT>), dim3(grid), dim3(NT), 0, st, a, (const int4 *)utab, nunits,
                      ctr);
   if (SPLIT && nsplit > 0) {

@@ -274,9 +274,11 @@ __device__ void scan_counts(const ScanJob &s, int32_t *status) {
 
 // Job order by decreasing work, ties by lower job index: every job has the
 // unique key (work << 32) | ~job.  Step 1 sorts each KV group's N keys in LDS
-// (one workgroup per group, bitonic); step 2 places every job at its global
-// rank, i.e. its position in its own group plus, for each other group, the
-// number of larger keys there (binary search).
+// (one workgroup per group, bitonic); step 2 places every job at its rank,
+// i.e. its position in its own group plus, for each other group of the same
+// sequence, the number of larger keys there (binary search).  With several
+// sequences side by side (gps groups each), each sequence's jobs are ranked
+// among themselves and fill that sequence's gps * N slots of the order.
 constexpr int kSortThreads = 1024;
 constexpr int kSortMax = 16384;
 __device__ __forceinline__ unsigned long long job_key(const int32_t *jwork, int job) {
@@ -325,7 +327,7 @@ __global__ void __launch_bounds__(kScanThreads) k_scan_sort(ScanJob s0, ScanJob 
 // kRankLdsKeys) and searches there.
 constexpr int kRankLdsKeys = 16384;       // 128 KiB of keys
 template <bool LDS>
-__global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, int32_t *order) {
+__global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, int gps, int32_t *order) {
   extern __shared__ unsigned long long skeys[];
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (LDS) {
@@ -335,9 +337,10 @@ __global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, in
   if (e >= Hkv * N) return;
   const unsigned long long *src = LDS ? skeys : sorted;
   const int g = e / N, k = e % N;
+  const int s0 = g / gps * gps;                              // the sequence's first group
   const unsigned long long key = src[e];
   int rank = k;
-  for (int o = 0; o < Hkv; ++o) {
+  for (int o = s0; o < s0 + gps; ++o) {
     if (o == g) continue;
     const unsigned long long *l = src + (size_t)o * N;      // descending
     int lo = 0, hi = N;                                      // count of entries > key
@@ -347,7 +350,7 @@ __global__ void k_rank_jobs(const unsigned long long *sorted, int N, int Hkv, in
     }
     rank += lo;
   }
-  order[rank] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
+  order[(size_t)s0 * N + rank] = (int32_t)(0xffffffffu - (uint32_t)(key & 0xffffffffull));
 }
 
 template <int GM, bool WRITE>
@@ -385,7 +388,7 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   int P = 1;
   while (P < p.N) P <<= 1;
   const size_t slds = sizeof(unsigned long long) * P;
-  e = hipFuncSetAttribute((const void *)k_scan_sort, hipFuncAttributeMaxDynamicSharedMemorySize, (int)slds);
+  e = ensure_dyn_lds((const void *)k_scan_sort, slds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_scan_sort, dim3(nscan + p.Hkv), dim3(kScanThreads), slds, st, sj, sr, nscan,
                      io->status, w.jwork, p.N, w.jkeys);
@@ -398,13 +401,13 @@ hipError_t build(const Plan &p, const fp_index_out *io, const Work &w, hipStream
   if (e != hipSuccess) return e;
   if (jobs <= kRankLdsKeys) {
     const size_t lds = sizeof(unsigned long long) * jobs;
-    e = hipFuncSetAttribute((const void *)k_rank_jobs<true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    e = ensure_dyn_lds((const void *)k_rank_jobs<true>, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_rank_jobs<true>, dim3((jobs + 1023) / 1024), dim3(1024), lds, st, w.jkeys, p.N, p.Hkv,
-                       io->job_order);
+                       p.seq_groups, io->job_order);
   } else {
     hipLaunchKernelGGL(k_rank_jobs<false>, dim3((jobs + 255) / 256), dim3(256), 0, st, w.jkeys, p.N, p.Hkv,
-                       io->job_order);
+                       p.seq_groups, io->job_order);
   }
   return hipGetLastError();
 }
@@ -462,6 +465,86 @@ hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hip
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return build(p, io, w, st, false);
+}
+
+// ---------------------------------------------------------------------------
+// Equal-length sequences run side by side.  A batch of k sequences of one length is one call with
+// k * Hq query heads and k * Hkv KV heads: every quantity is per head or per KV group, and the job
+// order and the attention's chunk rotation are taken per sequence (Plan::seq_groups).  These two
+// kernels move between that folded form and the caller's per-sequence outputs; one workgroup per
+// sequence.
+
+// Index outputs of the folded call -> each sequence's fp_index_out, with that output's own
+// capacities: row and job offsets rebased to the sequence and clamped to its capacity, columns and
+// job entries copied up to it, the overflow bits set in its status word as a call of its own would.
+__global__ void __launch_bounds__(1024) k_split_index(FoldArgs a) {
+  const int t = a.t0 + blockIdx.x;                           // the sequence within the folded call
+  const fp_index_out &o = a.seq[blockIdx.x];
+  const int nr = a.Hq * a.N, nj = a.Hkv * a.N;
+  const size_t rb = (size_t)t * nr, jb = (size_t)t * nj;
+  const int r0 = a.f.row_ptr[rb], rtot = a.f.row_ptr[rb + nr] - r0;
+  const int j0 = a.f.job_ptr[jb], jtot = a.f.job_ptr[jb + nj] - j0;
+  for (int r = threadIdx.x; r <= nr; r += blockDim.x)
+    o.row_ptr[r] = (int32_t)min((int64_t)(a.f.row_ptr[rb + r] - r0), o.col_cap);
+  const int nc = (int)min((int64_t)rtot, o.col_cap);
+  for (int q = threadIdx.x; q < nc; q += blockDim.x) o.col_idx[q] = a.f.col_idx[r0 + q];
+  for (int j = threadIdx.x; j <= nj; j += blockDim.x)
+    o.job_ptr[j] = (int32_t)min((int64_t)(a.f.job_ptr[jb + j] - j0), o.job_cap);
+  const int ne = (int)min((int64_t)jtot, o.job_cap);
+  for (int q = threadIdx.x; q < ne; q += blockDim.x) {
+    o.job_blk[q] = a.f.job_blk[j0 + q];
+    o.job_mask[q] = a.f.job_mask[j0 + q];
+  }
+  for (int q = threadIdx.x; q < nj; q += blockDim.x) o.job_order[q] = a.f.job_order[jb + q] - (int32_t)jb;
+  for (int h = threadIdx.x; h < a.Hq; h += blockDim.x) {
+    o.pattern[h] = a.f.pattern[(size_t)t * a.Hq + h];
+    o.jsd[h] = a.f.jsd[(size_t)t * a.Hq + h];
+  }
+  if (o.stats && a.f.stats) {
+    const size_t HNf = (size_t)a.k * nr;                       // folded [3][k * Hq][N]
+    for (int e = threadIdx.x; e < 3 * nr; e += blockDim.x) {
+      const int c = e / nr, q = e - c * nr;
+      o.stats[e] = a.f.stats[c * HNf + rb + q];
+    }
+  }
+  if (threadIdx.x == 0)
+    o.status[0] = a.f.status[0] | (rtot > o.col_cap ? (int32_t)FP_STATUS_CSR_OVERFLOW : 0) |
+                  (jtot > o.job_cap ? (int32_t)FP_STATUS_JOB_OVERFLOW : 0);
+}
+
+// Each sequence's job list -> the folded one: job offsets shifted by the entries of the sequences
+// before it, entries copied after theirs, and the orders interleaved (position q * k + t holds
+// sequence t's q-th job), which keeps every sequence's longest jobs first.  Launches cover
+// consecutive groups of sequences in order; a group starts from the offset the previous one wrote
+// (the folded job_ptr at its first sequence).
+__global__ void __launch_bounds__(1024) k_merge_jobs(FoldArgs a) {
+  const int t = a.t0 + blockIdx.x;
+  const fp_index_out &in = a.seq[blockIdx.x];
+  const int nj = a.Hkv * a.N;
+  // offsets are kept within a sequence's worst case (the merged list has room for exactly that
+  // much per sequence), whatever the input holds
+  const int cap = (int)((int64_t)nj * (a.N + 1) / 2);
+  auto clampj = [&](int v) { return min(max(v, 0), cap); };
+  int off = a.t0 == 0 ? 0 : a.f.job_ptr[(size_t)a.t0 * nj];
+  for (int u = 0; u < (int)blockIdx.x; ++u) off += clampj(a.seq[u].job_ptr[nj]);
+  const int tot = clampj(in.job_ptr[nj]);
+  for (int j = threadIdx.x; j <= nj; j += blockDim.x) a.f.job_ptr[(size_t)t * nj + j] = off + clampj(in.job_ptr[j]);
+  for (int q = threadIdx.x; q < tot; q += blockDim.x) {
+    a.f.job_blk[off + q] = in.job_blk[q];
+    a.f.job_mask[off + q] = in.job_mask[q];
+  }
+  for (int q = threadIdx.x; q < nj; q += blockDim.x)
+    a.f.job_order[(size_t)q * a.k + t] = in.job_order[q] + t * nj;
+}
+
+hipError_t launch_split_index(const FoldArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_split_index, dim3(a.n), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_jobs(const FoldArgs &a, hipStream_t st) {
+  hipLaunchKernelGGL(k_merge_jobs, dim3(a.n), dim3(1024), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace fp

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "fp_internal.hpp"
@@ -27,6 +28,7 @@ int make_plan(const fp_shape *s, Plan *p) {
   memset(p, 0, sizeof(*p));
   p->S = s->S; p->B = s->b; p->Hq = s->Hq; p->Hkv = s->Hkv; p->d = s->d;
   p->N = N; p->G = G;
+  p->seq_groups = s->Hkv;
   p->nw32 = (N + 31) / 32;
   p->nch = stats_chunks(s->b, G, N);
   size_t o = 0;
@@ -141,6 +143,18 @@ int64_t fp_job_capacity(const fp_shape *shape) {
   return (int64_t)p.Hkv * p.N * (p.N + 1) / 2;
 }
 
+// The index launches for a validated plan and workspace.
+static int index_launch(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K, const float *sK,
+                        float gamma, float tau, const fp_index_out *out, void *ws, hipStream_t st, bool share,
+                        const float *qbar_in) {
+  Work w = carve(p, ws);
+  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, st, out->status));   // also clears the status word
+  FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, true));
+  FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st, qbar_in));
+  FP_LAUNCH(launch_rows_and_jobs(p, out, w, st, share));
+  return FP_OK;
+}
+
 static int index_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
                         const void *K, const float *sK, float gamma, float tau,
                         fp_index_out *out, void *ws, size_t ws_bytes, void *stream,
@@ -152,13 +166,7 @@ static int index_common(const fp_shape *shape, bool i8, const void *Q, const flo
   if ((rc = check_params(gamma, tau))) return rc;
   if ((rc = check_out(p, out, true))) return rc;
   if (!ws || ws_bytes < p.total) return ws ? FP_EWORKSPACE : FP_EINVAL;
-  hipStream_t st = (hipStream_t)stream;
-  Work w = carve(p, ws);
-  FP_LAUNCH(launch_ig_stats(p, i8, Q, sQ, K, sK, w, st, out->status));   // also clears the status word
-  FP_LAUNCH(launch_ig_finalize(p, i8, Q, sQ, gamma, tau, out, w, st, true));
-  FP_LAUNCH(launch_ig_qa(p, i8, Q, sQ, gamma, out->pattern, w, st, qbar_in));
-  FP_LAUNCH(launch_rows_and_jobs(p, out, w, st, share));
-  return FP_OK;
+  return index_launch(p, i8, Q, sQ, K, sK, gamma, tau, out, ws, (hipStream_t)stream, share, qbar_in);
 }
 
 int fp_index(const fp_shape *shape, const void *Q, const void *K, float gamma, float tau,
@@ -258,6 +266,15 @@ int fp_build_jobs(const fp_shape *shape, fp_index_out *io, void *ws, size_t ws_b
   return FP_OK;
 }
 
+// The attention launches for a validated plan and workspace.
+static int attn_launch(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K, const float *sK,
+                       const void *V, const float *sV, const fp_index_out *csr, void *O, void *ws, hipStream_t st) {
+  const Work w = carve(p, ws);
+  FP_LAUNCH(launch_attn(p, i8, Q, sQ, K, sK, V, sV, csr, O, w.bar + 32, w.utab, st, 0, 1, nullptr,
+                        i8 ? (uint16_t *)((char *)ws + p.off_vw) : nullptr));
+  return FP_OK;
+}
+
 static int attn_common(const fp_shape *shape, bool i8, const void *Q, const float *sQ,
                        const void *K, const float *sK, const void *V, const float *sV,
                        const fp_index_out *csr, void *O, void *ws, size_t ws_bytes,
@@ -271,10 +288,7 @@ static int attn_common(const fp_shape *shape, bool i8, const void *Q, const floa
     return FP_EINVAL;
   const size_t need = i8 ? p.total_i8 : p.total;
   if (!ws || ws_bytes < need) return ws ? FP_EWORKSPACE : FP_EINVAL;
-  const Work w = carve(p, ws);
-  FP_LAUNCH(launch_attn(p, i8, Q, sQ, K, sK, V, sV, csr, O, w.bar + 32, w.utab, (hipStream_t)stream, 0, 1,
-                        nullptr, i8 ? (uint16_t *)((char *)ws + p.off_vw) : nullptr));
-  return FP_OK;
+  return attn_launch(p, i8, Q, sQ, K, sK, V, sV, csr, O, ws, (hipStream_t)stream);
 }
 
 int fp_attn(const fp_shape *shape, const void *Q, const void *K, const void *V,
@@ -354,6 +368,74 @@ static int batch_check(const fp_shape *shape, int nseq, const int32_t *seqlens, 
   return ws_bytes < need ? FP_EWORKSPACE : FP_OK;
 }
 
+// Runs of equal-length sequences (up to kFoldRun of them, each of at most kFoldMaxN key blocks) run
+// as one call with their heads side by side, when the workspace holds that call's layout: a batch
+// of short sequences is otherwise a chain of small launches per sequence.  Longer sequences gain
+// nothing from it and would need folded capacities of Hq * N^2 / 2 entries each.
+constexpr int kFoldMaxN = 256;
+
+// The plan of k sequences of length S side by side (job order and chunk rotation per sequence).
+static int fold_plan(const fp_shape *shape, int S, int k, Plan *p) {
+  fp_shape f = *shape;
+  f.S = S;
+  f.Hq = shape->Hq * k;
+  f.Hkv = shape->Hkv * k;
+  const int rc = make_plan(&f, p);
+  if (rc) return rc;
+  p->seq_groups = shape->Hkv;
+  return FP_OK;
+}
+
+// Workspace of a folded index call: its own workspace, then the folded outputs with room for every
+// sequence's worst case (so the folded call itself never overflows).
+struct FoldIndexLayout {
+  size_t row_ptr, col_idx, job_ptr, job_blk, job_mask, job_order, pattern, jsd, stats, status, total;
+};
+static FoldIndexLayout fold_index_layout(const Plan &pf, int k, bool stats) {
+  const size_t N = pf.N, nr = (size_t)pf.Hq * N, nj = (size_t)pf.Hkv * N;
+  const size_t ccap = nr * (N + 1) / 2, jcap = nj * (N + 1) / 2;   // k sequences' worst cases
+  FoldIndexLayout L;
+  size_t o = pf.total;
+  L.row_ptr = o;   o = align_up(o + sizeof(int32_t) * (nr + 1));
+  L.col_idx = o;   o = align_up(o + sizeof(int32_t) * ccap);
+  L.job_ptr = o;   o = align_up(o + sizeof(int32_t) * (nj + 1));
+  L.job_blk = o;   o = align_up(o + sizeof(int32_t) * jcap);
+  L.job_mask = o;  o = align_up(o + sizeof(uint32_t) * jcap);
+  L.job_order = o; o = align_up(o + sizeof(int32_t) * nj);
+  L.pattern = o;   o = align_up(o + pf.Hq);
+  L.jsd = o;       o = align_up(o + sizeof(float) * pf.Hq);
+  L.stats = o;     o = align_up(o + (stats ? sizeof(float) * 3 * nr : 0));
+  L.status = o;    o = align_up(o + sizeof(int32_t));
+  L.total = o;
+  (void)k;
+  return L;
+}
+
+// Workspace of a folded attention call: its own workspace (with the int8 V widening for W8A8), then
+// the merged job list.
+struct FoldAttnLayout {
+  size_t job_ptr, job_blk, job_mask, job_order, total;
+};
+static FoldAttnLayout fold_attn_layout(const Plan &pf, bool i8) {
+  const size_t N = pf.N, nj = (size_t)pf.Hkv * N, jcap = nj * (N + 1) / 2;
+  FoldAttnLayout L;
+  size_t o = i8 ? pf.total_i8 : pf.total;
+  L.job_ptr = o;   o = align_up(o + sizeof(int32_t) * (nj + 1));
+  L.job_blk = o;   o = align_up(o + sizeof(int32_t) * jcap);
+  L.job_mask = o;  o = align_up(o + sizeof(uint32_t) * jcap);
+  L.job_order = o; o = align_up(o + sizeof(int32_t) * nj);
+  L.total = o;
+  return L;
+}
+
+// The run of equal-length sequences that starts at s: its length (1 if it is not folded).
+static int fold_run(const fp_shape *shape, int nseq, const int32_t *seqlens, int s) {
+  if (seqlens[s] / shape->b > kFoldMaxN) return 1;
+  int e = s + 1;
+  while (e < nseq && e - s < kFoldRun && seqlens[e] == seqlens[s]) ++e;
+  return e - s;
+}
+
 // Sequence s's tensors follow sequence s - 1's: element bytes 2 (bf16) or 1 (int8), and the
 // int8 forms' per-token scales likewise, one fp32 per head and token.
 static int index_batch_common(const fp_shape *shape, bool i8, int nseq, const int32_t *seqlens,
@@ -363,17 +445,51 @@ static int index_batch_common(const fp_shape *shape, bool i8, int nseq, const in
   int rc = check_params(gamma, tau);
   if (rc || (rc = batch_check(shape, nseq, seqlens, ws_bytes, outs, true))) return rc;
   const size_t eb = i8 ? 1 : 2;
+  hipStream_t st = (hipStream_t)stream;
   const uint8_t *q = (const uint8_t *)Q, *k = (const uint8_t *)K;
-  for (int s = 0; s < nseq; ++s) {
+  for (int s = 0; s < nseq;) {
     fp_shape one = *shape;
     one.S = seqlens[s];
-    if ((rc = index_common(&one, i8, q, sQ, k, sK, gamma, tau, outs + s, ws, ws_bytes, stream))) return rc;
-    q += (size_t)one.Hq * one.S * one.d * eb;
-    k += (size_t)one.Hkv * one.S * one.d * eb;
-    if (i8) {
-      sQ += (size_t)one.Hq * one.S;
-      sK += (size_t)one.Hkv * one.S;
+    int run = fold_run(shape, nseq, seqlens, s);
+    Plan pf;
+    FoldIndexLayout L{};
+    bool stats = false;
+    for (int t = s; t < s + run; ++t) stats = stats || outs[t].stats != nullptr;
+    if (run >= 2 && (rc = fold_plan(shape, one.S, run, &pf)) == FP_OK) L = fold_index_layout(pf, run, stats);
+    if (run >= 2 && rc == FP_OK && ws_bytes >= L.total) {
+      char *b = (char *)ws;
+      FoldArgs fa{};
+      fa.k = run; fa.Hq = shape->Hq; fa.Hkv = shape->Hkv; fa.N = pf.N;
+      fp_index_out &f = fa.f;
+      f.row_ptr = (int32_t *)(b + L.row_ptr);
+      f.col_idx = (int32_t *)(b + L.col_idx);
+      f.col_cap = (int64_t)pf.Hq * pf.N * (pf.N + 1) / 2;
+      f.job_ptr = (int32_t *)(b + L.job_ptr);
+      f.job_blk = (int32_t *)(b + L.job_blk);
+      f.job_mask = (uint32_t *)(b + L.job_mask);
+      f.job_cap = (int64_t)pf.Hkv * pf.N * (pf.N + 1) / 2;
+      f.job_order = (int32_t *)(b + L.job_order);
+      f.pattern = (uint8_t *)(b + L.pattern);
+      f.jsd = (float *)(b + L.jsd);
+      f.stats = stats ? (float *)(b + L.stats) : nullptr;
+      f.status = (int32_t *)(b + L.status);
+      if ((rc = index_launch(pf, i8, q, sQ, k, sK, gamma, tau, &f, ws, st, false, nullptr))) return rc;
+      for (fa.t0 = 0; fa.t0 < run; fa.t0 += kFoldArgs) {
+        fa.n = std::min(kFoldArgs, run - fa.t0);
+        for (int t = 0; t < fa.n; ++t) fa.seq[t] = outs[s + fa.t0 + t];
+        FP_LAUNCH(launch_split_index(fa, st));
+      }
+    } else {
+      run = 1;
+      if ((rc = index_common(&one, i8, q, sQ, k, sK, gamma, tau, outs + s, ws, ws_bytes, stream))) return rc;
     }
+    q += (size_t)run * one.Hq * one.S * one.d * eb;
+    k += (size_t)run * one.Hkv * one.S * one.d * eb;
+    if (i8) {
+      sQ += (size_t)run * one.Hq * one.S;
+      sK += (size_t)run * one.Hkv * one.S;
+    }
+    s += run;
   }
   return FP_OK;
 }
@@ -385,13 +501,35 @@ static int attn_batch_common(const fp_shape *shape, bool i8, int nseq, const int
   int rc = batch_check(shape, nseq, seqlens, ws_bytes, csrs, false, i8);
   if (rc) return rc;
   const size_t eb = i8 ? 1 : 2;
+  hipStream_t st = (hipStream_t)stream;
   const uint8_t *q = (const uint8_t *)Q, *k = (const uint8_t *)K, *v = (const uint8_t *)V;
   uint8_t *o = (uint8_t *)O;
-  for (int s = 0; s < nseq; ++s) {
+  for (int s = 0; s < nseq;) {
     fp_shape one = *shape;
     one.S = seqlens[s];
-    if ((rc = attn_common(&one, i8, q, sQ, k, sK, v, sV, csrs + s, o, ws, ws_bytes, stream))) return rc;
-    const size_t qn = (size_t)one.Hq * one.S, kn = (size_t)one.Hkv * one.S;
+    int run = fold_run(shape, nseq, seqlens, s);
+    Plan pf;
+    FoldAttnLayout L{};
+    if (run >= 2 && (rc = fold_plan(shape, one.S, run, &pf)) == FP_OK) L = fold_attn_layout(pf, i8);
+    if (run >= 2 && rc == FP_OK && ws_bytes >= L.total) {
+      char *b = (char *)ws;
+      FoldArgs fa{};
+      fa.k = run; fa.Hq = shape->Hq; fa.Hkv = shape->Hkv; fa.N = pf.N;
+      fa.f.job_ptr = (int32_t *)(b + L.job_ptr);
+      fa.f.job_blk = (int32_t *)(b + L.job_blk);
+      fa.f.job_mask = (uint32_t *)(b + L.job_mask);
+      fa.f.job_order = (int32_t *)(b + L.job_order);
+      for (fa.t0 = 0; fa.t0 < run; fa.t0 += kFoldArgs) {   // in order: each group continues the last
+        fa.n = std::min(kFoldArgs, run - fa.t0);
+        for (int t = 0; t < fa.n; ++t) fa.seq[t] = csrs[s + fa.t0 + t];
+        FP_LAUNCH(launch_merge_jobs(fa, st));
+      }
+      if ((rc = attn_launch(pf, i8, q, sQ, k, sK, v, sV, &fa.f, o, ws, st))) return rc;
+    } else {
+      run = 1;
+      if ((rc = attn_common(&one, i8, q, sQ, k, sK, v, sV, csrs + s, o, ws, ws_bytes, stream))) return rc;
+    }
+    const size_t qn = (size_t)run * one.Hq * one.S, kn = (size_t)run * one.Hkv * one.S;
     q += qn * one.d * eb;
     o += qn * one.d * 2;                          // bf16 output
     k += kn * one.d * eb;
@@ -401,7 +539,32 @@ static int attn_batch_common(const fp_shape *shape, bool i8, int nseq, const int
       sK += kn;
       sV += kn;
     }
+    s += run;
   }
+  return FP_OK;
+}
+
+int fp_batch_workspace_bytes(const fp_shape *shape, int nseq, const int32_t *seqlens, int variant, size_t *bytes) {
+  if (!shape || !bytes || nseq < 1 || !seqlens || (variant != 0 && variant != 1)) return FP_EINVAL;
+  size_t need = 0;
+  for (int s = 0; s < nseq;) {
+    fp_shape one = *shape;
+    one.S = seqlens[s];
+    Plan p;
+    int rc = make_plan(&one, &p);
+    if (rc) return rc;
+    size_t t = variant == 1 ? p.total_i8 : p.total;
+    const int run = fold_run(shape, nseq, seqlens, s);
+    if (run >= 2) {
+      Plan pf;
+      if ((rc = fold_plan(shape, one.S, run, &pf))) return rc;
+      const size_t fi = fold_index_layout(pf, run, true).total, fa = fold_attn_layout(pf, variant == 1).total;
+      t = std::max(t, std::max(fi, fa));
+    }
+    need = std::max(need, t);
+    s += run;
+  }
+  *bytes = need;
   return FP_OK;
 }
 

@@ -13,6 +13,9 @@ namespace fp {
 // Everything the launchers need about one problem, derived from fp_shape.
 struct Plan {
   int S, B, Hq, Hkv, d, N, G;
+  int seq_groups;    // KV groups per sequence: Hkv, or fewer when several equal-length sequences
+                     // run as one call with their heads side by side (job order and chunk
+                     // rotation are then taken per sequence)
   int nw32;          // 32-bit words per row bitmask: ceil(N / 32)
   int nch;           // key-block chunks of the statistics (stats_chunks)
   // workspace layout (byte offsets from the workspace base)
@@ -88,9 +91,26 @@ hipError_t launch_block_uses(const Plan &p, const fp_index_out *jobs, int32_t *u
 hipError_t launch_jobs(const Plan &p, const fp_index_out *io, const Work &w, hipStream_t st);
 // status[0] = 0 and, when bar is not NULL, bar[0] = 0
 hipError_t launch_status_init(int32_t *status, unsigned int *bar, hipStream_t st);
+
+// Equal-length sequences run as one call (side by side): the folded call's outputs f (in the
+// workspace, k sequences) and the own outputs seq[0..n) of its sequences t0 .. t0 + n - 1 (the
+// caller's, passed by value, at most kFoldArgs per launch).
+constexpr int kFoldRun = 64;        // sequences per folded call
+constexpr int kFoldArgs = 24;       // sequences per split or merge launch (kernel arguments)
+struct FoldArgs {
+  fp_index_out f;
+  fp_index_out seq[kFoldArgs];
+  int k, t0, n, Hq, Hkv, N;         // Hq, Hkv: one sequence's heads
+};
+// Folded index outputs -> each sequence's fp_index_out (rebased, clamped to its capacities).
+hipError_t launch_split_index(const FoldArgs &a, hipStream_t st);
+// Each sequence's job list -> the folded job list (job fields of f).
+hipError_t launch_merge_jobs(const FoldArgs &a, hipStream_t st);
 // Block-sparse attention over the CSR rows.
 // compute units of the current device (cached; 0 if the query fails)
 int cu_count();
+hipError_t ensure_dyn_lds(const void *fn, size_t bytes);
+int occupancy_per_cu(const void *fn, int threads);
 // nseg > 1: split-KV schedule of fp_attn_split (bf16, b >= 128): the nsplit longest jobs in nseg
 // segments each, partial rows in `part`, merged by a combine kernel.
 hipError_t launch_attn(const Plan &p, bool i8, const void *Q, const float *sQ, const void *K,

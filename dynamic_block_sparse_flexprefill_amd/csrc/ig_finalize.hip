@@ -184,7 +184,7 @@ hipError_t launch_ig_finalize(const Plan &p, bool i8, const void *Q, const float
   a.sel = w.sel;
   const size_t lds = sizeof(float) * (3 * (size_t)p.N + 128 + kFinRowGroups * 128) + sizeof(uint32_t) * 2 * p.nw32;
   const void *fn = i8 ? (const void *)k_ig_finalize<true> : (const void *)k_ig_finalize<false>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = ensure_dyn_lds(fn, lds);
   if (e != hipSuccess) return e;
   if (i8)
     hipLaunchKernelGGL(k_ig_finalize<true>, dim3(p.Hq), dim3(kFinThreads), lds, st, a);

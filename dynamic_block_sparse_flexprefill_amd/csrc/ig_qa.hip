@@ -299,7 +299,7 @@ template <int B, bool I8, bool WIDE, bool PRE>
 hipError_t launch_qa16(const Plan &p, const QaArgs &a, hipStream_t st) {
   const size_t lds = sizeof(float) * ((size_t)16 * p.N + 16 * 128) + sizeof(uint32_t) * 8 * p.nw32;
   const void *fn = (const void *)k_qa_rows16<B, I8, WIDE, PRE>;
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = ensure_dyn_lds(fn, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_qa_rows16<B, I8, WIDE, PRE>), dim3((p.N + 15) / 16, p.Hq), dim3(kQa16Threads), lds, st, a);
   return hipGetLastError();
@@ -333,7 +333,7 @@ hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, 
       return run_qa16<256, false, true>(p, a, st);
     }
     const size_t lds = sizeof(float) * ((size_t)a.R * p.N + a.R * 128) + sizeof(uint32_t) * 4 * p.nw32;
-    hipError_t e = hipFuncSetAttribute((const void *)k_qa_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = ensure_dyn_lds((const void *)k_qa_rows, lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_qa_rows, dim3((p.N + a.R - 1) / a.R, p.Hq), dim3(kQaThreads), lds, st, a);
     return hipGetLastError();
@@ -355,7 +355,7 @@ hipError_t launch_ig_qa(const Plan &p, bool i8, const void *Q, const float *sQ, 
   else e = i8 ? run_pool<256, true>(p, pa, st) : run_pool<256, false>(p, pa, st);
   if (e != hipSuccess) return e;
   const size_t lds = sizeof(float) * ((size_t)a.R * p.N + a.R * 128) + sizeof(uint32_t) * 4 * p.nw32;
-  e = hipFuncSetAttribute((const void *)k_qa_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  e = ensure_dyn_lds((const void *)k_qa_rows, lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_qa_rows, dim3((p.N + a.R - 1) / a.R, p.Hq), dim3(kQaThreads), lds, st, a);
   return hipGetLastError();

@@ -36,6 +36,9 @@
 // up to 128 keys, two units in flight (the next one loads while the current
 // one is used), one barrier per unit.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
@@ -685,6 +688,39 @@ hipError_t probe_b(const Plan &p, const int8_t *Q8, const int8_t *K8, int h, int
 int stats_chunks(int B, int G, int N) {
   const int cb = chunk_blocks(B, tile_slots(G * B / 32));
   return (N + cb - 1) / cb;
+}
+
+// A kernel's dynamic-LDS limit raised to at least `bytes` on the current device.  The runtime call
+// is made only when the limit has to grow, so repeated launches of one shape do no host work for
+// it (a batch of short sequences is bound by the host's launch rate).
+hipError_t ensure_dyn_lds(const void *fn, size_t bytes) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, size_t> set;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  size_t &cur = set[{dev, fn}];
+  if (bytes <= cur) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e == hipSuccess) cur = bytes;
+  return e;
+}
+
+// Resident workgroups per compute unit of a kernel launched with `threads` threads and no dynamic
+// LDS, on the current device (queried once per kernel and device; 0 if the query fails).
+int occupancy_per_cu(const void *fn, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, int> seen;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = seen.find({dev, fn});
+  if (it != seen.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess) n = 0;
+  seen[{dev, fn}] = n;
+  return n;
 }
 
 int cu_count() {

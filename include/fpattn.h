@@ -347,8 +347,16 @@ int fp_attn_i8(const fp_shape *shape, const int8_t *Q8, const float *sQ,
  * since every quantity is per head or per KV group.)
  *   outs / csrs: host array of nseq index outputs, one per sequence, each
  *                sized for its own S_s as in fp_index.
- *   ws: one workspace of at least fp_workspace_bytes of the longest sequence;
- *       the sequences run in order on the stream and reuse it.
+ *   ws: at least fp_workspace_bytes of the longest sequence.  The sequences
+ *       run in order on the stream and reuse it.  A run of up to 64
+ *       consecutive sequences of one length S with S/b <= 256 runs as one
+ *       call with its heads side by side (every quantity is per head or per
+ *       KV group) when ws holds that call's layout; fp_batch_workspace_bytes
+ *       gives the size that allows it for every run.  The outputs are the same
+ *       bit for bit either way: job order and chunk order are taken per
+ *       sequence, and each sequence's outputs keep its own capacities.
+ *   csrs (attention): each as written by fp_index / fp_build_jobs for its
+ *       sequence.
  * Every sequence is checked before anything is enqueued (FP_EINVAL,
  * FP_EUNSUPPORTED, FP_EWORKSPACE as for one sequence); FP_EHIP if a launch
  * fails, after the earlier sequences have been enqueued.  Each sequence's
@@ -361,6 +369,17 @@ int fp_attn_batch(const fp_shape *shape, int nseq, const int32_t *seqlens,
                   const void *Q, const void *K, const void *V,
                   const fp_index_out *csrs, void *O,
                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Workspace bytes with which every run of equal-length sequences of a batch
+ * (see above) runs as one call: seqlens as for the batch calls (host array),
+ * shape->S ignored; variant 0 for fp_index_batch, fp_attn_batch and
+ * fp_index_i8_batch, 1 for fp_attn_i8_batch (or for all four).  Host only.
+ * Returns FP_EINVAL (null pointers, nseq < 1, variant not 0 or 1) or the
+ * shape errors of fp_workspace_bytes.
+ */
+int fp_batch_workspace_bytes(const fp_shape *shape, int nseq, const int32_t *seqlens, int variant,
+                             size_t *bytes);
 
 /*
  * The same for W8A8 inputs (as fp_index_i8 / fp_attn_i8): Q8, K8, V8 packed

@@ -31,7 +31,8 @@ def test_header_declares_expected_entry_points():
               "fp_workspace_bytes", "fp_csr_capacity", "fp_job_capacity", "fp_strerror",
               "fp_version", "fp_probe_qk_i8", "fp_index_batch", "fp_attn_batch",
               "fp_index_i8_batch", "fp_attn_i8_batch", "fp_index_static", "fp_index_shared",
-              "fp_index_pooled", "fp_qkv_project", "fp_attn_split", "fp_block_uses"):
+              "fp_index_pooled", "fp_qkv_project", "fp_attn_split", "fp_block_uses",
+              "fp_batch_workspace_bytes"):
         assert n in names
 
 
@@ -157,6 +158,29 @@ def test_workspace_grows_with_shape():
     # variant 1 adds fp_attn_i8's bf16 widening of V8 (Hkv x S x d), 256-byte aligned
     b1 = fpa.workspace_bytes(fpa.shape_of(131072, 128, 24, 8), 1)
     assert b1 == b + 2 * 8 * 131072 * 128
+
+
+def test_batch_workspace_bytes():
+    """Distinct lengths need the longest sequence's workspace; a run of equal short lengths runs as
+    one call and needs more; equal long sequences (more than 256 key blocks) are not folded."""
+    sh = fpa.shape_of(4096, 128, 6, 2)
+    one = lambda S, v: fpa.workspace_bytes(fpa.shape_of(S, 128, 6, 2), v)
+    for v in (0, 1):
+        assert fpa.batch_workspace_bytes(sh, [2048, 1024, 512], v) == max(one(S, v) for S in (2048, 1024, 512))
+        assert fpa.batch_workspace_bytes(sh, [1024] * 4, v) > one(1024, v)
+        assert fpa.batch_workspace_bytes(sh, [1024] * 4, v) > fpa.batch_workspace_bytes(sh, [1024] * 2, v)
+        long_ = 128 * 300
+        assert fpa.batch_workspace_bytes(sh, [long_] * 3, v) == one(long_, v)
+    assert fpa.batch_workspace_bytes(sh, [1024] * 4, 1) >= fpa.batch_workspace_bytes(sh, [1024] * 4, 0)
+    L = fpa.lib()
+    n = ctypes.c_size_t(0)
+    lens = (ctypes.c_int32 * 2)(1024, 1024)
+    assert L.fp_batch_workspace_bytes(ctypes.byref(sh), 0, lens, 0, ctypes.byref(n)) == fpa.FP_EINVAL
+    assert L.fp_batch_workspace_bytes(ctypes.byref(sh), 2, None, 0, ctypes.byref(n)) == fpa.FP_EINVAL
+    assert L.fp_batch_workspace_bytes(ctypes.byref(sh), 2, lens, 2, ctypes.byref(n)) == fpa.FP_EINVAL
+    assert L.fp_batch_workspace_bytes(ctypes.byref(sh), 2, lens, 0, None) == fpa.FP_EINVAL
+    bad = (ctypes.c_int32 * 2)(1000, 1000)          # not a multiple of b
+    assert L.fp_batch_workspace_bytes(ctypes.byref(sh), 2, bad, 0, ctypes.byref(n)) == fpa.FP_EINVAL
 
 
 @no_gpu_only

@@ -330,6 +330,118 @@ def test_ragged_batch_i8():
         assert mx <= MAXABS and rms <= RMS
 
 
+INDEX_FIELDS = ("row_ptr", "col_idx", "job_ptr", "job_blk", "job_mask", "job_order", "pattern", "jsd", "stats",
+                "status")
+
+
+def _index_equal(a, b, upto=None):
+    """Every field of two Index results equal (col_idx / job arrays up to their written length)."""
+    nnz = min(a.nnz, a.col_idx.numel()) if upto is None else upto
+    njob = min(int(a.job_ptr[-1].item()), a.job_blk.numel())
+    assert nnz == min(b.nnz, b.col_idx.numel()) and njob == min(int(b.job_ptr[-1].item()), b.job_blk.numel())
+    lens = {"col_idx": nnz, "job_blk": njob, "job_mask": njob}
+    for f in INDEX_FIELDS:
+        x, y = getattr(a, f), getattr(b, f)
+        if x is None and y is None:
+            continue
+        n = lens.get(f, x.numel())
+        assert torch.equal(x.flatten()[:n], y.flatten()[:n]), f
+
+
+@pytest.mark.parametrize("i8", [False, True], ids=["bf16", "i8"])
+def test_batch_runs_of_equal_lengths_match_single_calls(i8):
+    """Runs of equal-length sequences run as one call with their heads side by side; every
+    sequence's index (statistics included) and attention output equal those of a call of its own,
+    bit for bit, and so does attention over indices from single calls."""
+    lens = [1024, 1024, 1024, 384, 2048, 2048, 256]
+    say(f"batch with runs of equal lengths vs single calls ({'i8' if i8 else 'bf16'}): S = {lens}")
+    cs = [cfg(S=S, Hq=6, Hkv=2) for S in lens]
+    Ls = [gen.make(c, seed=11 + k) for k, c in enumerate(cs)]
+    c0 = cs[0]
+    singles, Os = [], []
+    if i8:
+        ts = [P.layer_i8_on_device(L) for L in Ls]
+        for c, t in zip(cs, ts):
+            ix = fpa.index_i8(t["q8"], t["sq"], t["k8"], t["sk"], c.b, c.gamma, c.tau, stats=True)
+            singles.append(ix)
+            Os.append(fpa.attn_i8(t["q8"], t["sq"], t["k8"], t["sk"], t["v8"], t["sv"], ix))
+        pack = lambda name: torch.cat([t[name].reshape(-1) for t in ts])
+        Q8, sQ, K8, sK, V8, sV = (pack(n) for n in ("q8", "sq", "k8", "sk", "v8", "sv"))
+        idxs = fpa.index_i8_batch(Q8, sQ, K8, sK, lens, c0.b, c0.Hq, c0.Hkv, c0.gamma, c0.tau, stats=True)
+        O = fpa.attn_i8_batch(Q8, sQ, K8, sK, V8, sV, lens, idxs)
+        O2 = fpa.attn_i8_batch(Q8, sQ, K8, sK, V8, sV, lens, singles)
+    else:
+        for c, L in zip(cs, Ls):
+            Qd, Kd, Vd = P.layer_on_device(L)
+            ix = fpa.index(Qd, Kd, c.b, c.gamma, c.tau, stats=True)
+            singles.append(ix)
+            Os.append(fpa.attn(Qd, Kd, Vd, ix))
+        pack = lambda name: torch.cat([P.dev_bf16(getattr(L, name), "cuda").reshape(-1) for L in Ls])
+        Q, K, V = pack("q"), pack("k"), pack("v")
+        idxs = fpa.index_batch(Q, K, lens, c0.b, c0.Hq, c0.Hkv, c0.gamma, c0.tau, stats=True)
+        O = fpa.attn_batch(Q, K, V, lens, idxs)
+        O2 = fpa.attn_batch(Q, K, V, lens, singles)
+    torch.cuda.synchronize()
+    for s, (a, b_) in enumerate(zip(idxs, singles)):
+        _index_equal(a, b_)
+    for Ob in (O, O2):
+        for s, (x, y) in enumerate(zip(fpa.unpack(Ob, lens, c0.Hq), Os)):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), s
+
+
+def test_batch_long_run_matches_single_calls():
+    """A run of 30 equal-length sequences (its outputs split, and its job lists merged, by
+    launches of 24 and 6 sequences) and a run of 3: every index and output equals a call of its
+    own, bit for bit."""
+    lens = [256] * 30 + [512] * 3
+    say(f"batch with a run of 30 sequences, S = 256, then 3 of S = 512")
+    cs = [cfg(S=S, Hq=4, Hkv=2) for S in lens]
+    Ls = [gen.make(c, seed=40 + k) for k, c in enumerate(cs)]
+    c0 = cs[0]
+    singles, Os = [], []
+    for c, L in zip(cs, Ls):
+        Qd, Kd, Vd = P.layer_on_device(L)
+        ix = fpa.index(Qd, Kd, c.b, c.gamma, c.tau)
+        singles.append(ix)
+        Os.append(fpa.attn(Qd, Kd, Vd, ix))
+    pack = lambda name: torch.cat([P.dev_bf16(getattr(L, name), "cuda").reshape(-1) for L in Ls])
+    Q, K, V = pack("q"), pack("k"), pack("v")
+    idxs = fpa.index_batch(Q, K, lens, c0.b, c0.Hq, c0.Hkv, c0.gamma, c0.tau)
+    O = fpa.attn_batch(Q, K, V, lens, idxs)
+    O2 = fpa.attn_batch(Q, K, V, lens, singles)
+    torch.cuda.synchronize()
+    for a, b_ in zip(idxs, singles):
+        _index_equal(a, b_)
+    for Ob in (O, O2):
+        for s_, (x, y) in enumerate(zip(fpa.unpack(Ob, lens, c0.Hq), Os)):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), s_
+
+
+def test_batch_run_keeps_each_sequences_capacity():
+    """One sequence of a run of equal lengths with a column capacity too small for its rows: its
+    status word reports the overflow and its outputs equal those of a call of its own with that
+    capacity; the others are complete."""
+    lens = [1024] * 3
+    say("batch run with one small capacity")
+    cs = [cfg(S=S, Hq=4, Hkv=2) for S in lens]
+    Ls = [gen.make(c, seed=23 + k) for k, c in enumerate(cs)]
+    c0 = cs[0]
+    sh = fpa.shape_of(1024, c0.b, c0.Hq, c0.Hkv)
+    small = c0.Hq * c0.N + 5
+    outs = [fpa.Index.empty(sh, "cuda", col_cap=(small if k == 1 else None)) for k in range(3)]
+    pack = lambda name: torch.cat([P.dev_bf16(getattr(L, name), "cuda").reshape(-1) for L in Ls])
+    idxs = fpa.index_batch(pack("q"), pack("k"), lens, c0.b, c0.Hq, c0.Hkv, c0.gamma, c0.tau, outs=outs)
+    ref = []
+    for k, L in enumerate(Ls):
+        Qd, Kd, _ = P.layer_on_device(L)
+        out = fpa.Index.empty(sh, "cuda", col_cap=(small if k == 1 else None))
+        ref.append(fpa.index(Qd, Kd, c0.b, c0.gamma, c0.tau, out=out))
+    torch.cuda.synchronize()
+    assert [int(ix.status.item()) for ix in idxs] == [0, fpa.FP_STATUS_CSR_OVERFLOW, 0]
+    for a, b_ in zip(idxs, ref):
+        _index_equal(a, b_)
+
+
 def test_index_deterministic_and_end_to_end():
     say("index + attn determinism, tiny")
     c = cfg()
