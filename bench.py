@@ -372,6 +372,44 @@ def split_kv_records(c, T, idx, steps, warmup, dev):
     return out
 
 
+def short_prompt_batch_record(steps, warmup, dev, nseq=32, S=4096):
+    """A batch of nseq prompts of S tokens (3B shape, seeds 100 ..): fp_index_batch + fp_attn_batch
+    with the batch workspace (the run of equal lengths folded into one call) against a workspace of
+    one sequence (a call per sequence), outputs allocated once, and the folded outputs checked
+    against the per-sequence ones bit for bit."""
+    import torch
+    import gen
+    import dynamic_block_sparse_flexprefill_amd as fpa
+    c = gen.CONFIGS["3b-32k"].with_(S=S)
+    Ls = [gen.make(c, seed=100 + s) for s in range(nseq)]
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    Q, K, V = (up(np.concatenate([getattr(L, n).reshape(-1) for L in Ls])) for n in ("q", "k", "v"))
+    del Ls
+    lens = [S] * nseq
+    sh = fpa.shape_of(S, c.b, c.Hq, c.Hkv)
+    rec = {"workload": f"{nseq} prompts of {S} tokens, Llama-3.2-3B-shaped layers (b={c.b}, Hq={c.Hq}, "
+                       f"Hkv={c.Hkv}, d=128), packed one after another"}
+    res = {}
+    for label, ws in (("per_sequence", fpa.Workspace(sh, dev)), ("folded", fpa.Workspace(sh, dev, lens))):
+        outs = [fpa.Index.empty(sh, dev) for _ in lens]
+        O = torch.empty_like(Q)
+        ti = time_call(lambda: fpa.index_batch(Q, K, lens, c.b, c.Hq, c.Hkv, c.gamma, c.tau, outs=outs, ws=ws),
+                       steps, warmup)
+        ta = time_call(lambda: fpa.attn_batch(Q, K, V, lens, outs, out=O, ws=ws), steps, warmup)
+        torch.cuda.synchronize()
+        nnz = sum(ix.nnz for ix in outs)
+        flops, _ = attn_flops(c.with_(Hq=c.Hq * nseq, Hkv=c.Hkv * nseq), nnz)
+        rec[label] = {"index_ms": round(ti, 4), "attn_ms": round(ta, 4), "ms_per_batch": round(ti + ta, 4),
+                      "attn_tflops": round(flops / (ta * 1e-3) / 1e12, 1)}
+        res[label] = (outs, O)
+    (oa, Oa), (ob, Ob) = res["per_sequence"], res["folded"]
+    same = torch.equal(Oa.view(torch.int16), Ob.view(torch.int16))
+    for a, b_ in zip(oa, ob):
+        same = same and torch.equal(a.row_ptr, b_.row_ptr) and torch.equal(a.job_order, b_.job_order)
+    rec["folded_equals_per_sequence"] = bool(same)
+    return rec
+
+
 def time_call(fn, steps: int, warmup: int) -> float:
     """Median ms of fn() over `steps` calls timed with events on the current stream."""
     import torch
@@ -521,6 +559,7 @@ def main(argv=None):
         "split_kv": None,
         "projection": None,
         "index_with_upstream_qbar": None,
+        "short_prompt_batch": None,
     }
 
     if not args.no_cpu:
@@ -563,6 +602,10 @@ def main(argv=None):
             log(f"[bench] QKV projection with the fused epilogue at {c.name}'s shape (D = 3072)")
             rec["projection"] = projection_records(c, args.steps, args.warmup, dev)
             log(f"[bench]   {rec['projection']}")
+            torch.cuda.empty_cache()
+            log("[bench] a batch of 32 prompts of 4096 tokens, folded and per sequence")
+            rec["short_prompt_batch"] = short_prompt_batch_record(args.steps, args.warmup, dev)
+            log(f"[bench]   {rec['short_prompt_batch']}")
         for name in EXTRA_CONFIGS:
             if name == c.name:
                 continue
