@@ -17,6 +17,11 @@
 // words of the rows, popcounts give the counts, OR gives the union.  Counts
 // are turned into offsets by one scan launch (rows and jobs side by side),
 // then a second pass over the same words writes columns and job entries.
+//
+// Equal-length sequences of a batch can run as one call with their heads side
+// by side; the job order is then ranked per sequence, and the split and merge
+// kernels at the end of this file move between that folded form and each
+// sequence's own outputs.
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 
