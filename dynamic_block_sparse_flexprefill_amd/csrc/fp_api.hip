@@ -375,6 +375,8 @@ static int batch_check(const fp_shape *shape, int nseq, const int32_t *seqlens, 
 constexpr int kFoldMaxN = 256;
 
 // The plan of k sequences of length S side by side (job order and chunk rotation per sequence).
+// FP_EUNSUPPORTED when the folded call's worst-case column or job count would not fit the 32-bit
+// offsets of its outputs (such runs go one sequence at a time).
 static int fold_plan(const fp_shape *shape, int S, int k, Plan *p) {
   fp_shape f = *shape;
   f.S = S;
@@ -382,6 +384,8 @@ static int fold_plan(const fp_shape *shape, int S, int k, Plan *p) {
   f.Hkv = shape->Hkv * k;
   const int rc = make_plan(&f, p);
   if (rc) return rc;
+  const int64_t worst = (int64_t)p->Hq * p->N * (p->N + 1) / 2;   // columns (jobs: Hkv <= Hq)
+  if (worst > INT32_MAX) return FP_EUNSUPPORTED;
   p->seq_groups = shape->Hkv;
   return FP_OK;
 }
@@ -555,9 +559,8 @@ int fp_batch_workspace_bytes(const fp_shape *shape, int nseq, const int32_t *seq
     if (rc) return rc;
     size_t t = variant == 1 ? p.total_i8 : p.total;
     const int run = fold_run(shape, nseq, seqlens, s);
-    if (run >= 2) {
-      Plan pf;
-      if ((rc = fold_plan(shape, one.S, run, &pf))) return rc;
+    Plan pf;
+    if (run >= 2 && fold_plan(shape, one.S, run, &pf) == FP_OK) {   // (else the run goes one at a time)
       const size_t fi = fold_index_layout(pf, run, true).total, fa = fold_attn_layout(pf, variant == 1).total;
       t = std::max(t, std::max(fi, fa));
     }

@@ -172,6 +172,9 @@ def test_batch_workspace_bytes():
         long_ = 128 * 300
         assert fpa.batch_workspace_bytes(sh, [long_] * 3, v) == one(long_, v)
     assert fpa.batch_workspace_bytes(sh, [1024] * 4, 1) >= fpa.batch_workspace_bytes(sh, [1024] * 4, 0)
+    # a run whose folded worst case would not fit 32-bit offsets is not folded
+    big = fpa.shape_of(32768, 128, 1024, 1024)
+    assert fpa.batch_workspace_bytes(big, [32768] * 64, 0) == fpa.workspace_bytes(big, 0)
     L = fpa.lib()
     n = ctypes.c_size_t(0)
     lens = (ctypes.c_int32 * 2)(1024, 1024)
