@@ -8,7 +8,9 @@
 // then a butterfly), so results are reproducible run to run.  Two methods:
 //  * greedy: the maxima are extracted in exactly that order (value descending,
 //    lowest index among equal values) until the running sum reaches gamma*T
-//    -- used when that takes at most kGreedySteps extractions;
+//    -- used when that takes at most kGreedySteps extractions (half as many
+//    for rows of more than 1024 values, whose extraction steps cost twice as
+//    much);
 //  * bisection: the cut value theta = x_(k*) is the largest t with
 //    sum_{x >= t} x >= gamma * T, found by bisection over the bit patterns of
 //    non-negative floats (ordered like the values); everything above theta
@@ -100,10 +102,11 @@ __device__ __forceinline__ void wave_select_vals(const float (&v)[VPL], int n, f
     return;
   }
   // greedy extraction
+  constexpr int steps = VPL > 16 ? kGreedySteps / 2 : kGreedySteps;
   uint32_t taken = 0u;
   float cum = 0.0f;
   bool done = false;
-  for (int step = 0; step < kGreedySteps && step < n; ++step) {
+  for (int step = 0; step < steps && step < n; ++step) {
     float bv = -1.0f;
     int bk = -1;
 #pragma unroll

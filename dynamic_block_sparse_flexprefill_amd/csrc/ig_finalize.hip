@@ -14,6 +14,8 @@
 // cumulative threshold gamma); the rows are expanded later.
 //
 // One workgroup per query head; every per-head vector of length N lives in LDS.
+#include <float.h>
+
 #include "fp_common.hpp"
 #include "fp_internal.hpp"
 #include "fp_select.hpp"
@@ -137,11 +139,22 @@ __global__ void __launch_bounds__(kFinThreads) k_ig_finalize(FinArgs a) {
     const float v = lo[j] + hi[j];
     vv[j] = v;
     sv[j] = lo[N - 1 - j] + (j <= N - 2 ? hi[N - 2 - j] : 0.0f);
-    const double pd = p, vd = v, m = 0.5 * (pd + vd);
-    if (pd > 0.0) dpart += pd * log(pd / m);
-    if (vd > 0.0) dpart += vd * log(vd / m);
+    // x log2(x / m) in fp32 with the hardware log2 (error about 1e-7 of the term's weight x, far
+    // below the divergence's use against tau), summed in double; a ratio below the smallest normal
+    // float contributes less than 1e-36 and is left out
+    const float m = 0.5f * (p + v);
+    float term = 0.0f;
+    if (p > 0.0f) {
+      const float r = __fdividef(p, m);
+      if (r >= FLT_MIN) term += p * __log2f(r);
+    }
+    if (v > 0.0f) {
+      const float r = __fdividef(v, m);
+      if (r >= FLT_MIN) term += v * __log2f(r);
+    }
+    dpart += (double)term;
   }
-  const double D = 0.5 * block_sum(dpart, redd);
+  const double D = 0.5 * 0.6931471805599453 * block_sum(dpart, redd);   // natural log: ln 2 * log2
   const bool qa = D < (double)a.tau;
   if (tid == 0) {
     a.jsd[h] = (float)D;
