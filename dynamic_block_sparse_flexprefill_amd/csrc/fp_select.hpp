@@ -8,9 +8,10 @@
 // then a butterfly), so results are reproducible run to run.  Two methods:
 //  * greedy: the maxima are extracted in exactly that order (value descending,
 //    lowest index among equal values) until the running sum reaches gamma*T
-//    -- used when that takes at most kGreedySteps extractions (half as many
-//    for rows of more than 1024 values, whose extraction steps cost twice as
-//    much);
+//    -- used when that takes at most GS extractions (by default kGreedySteps,
+//    half as many for rows of more than 1024 values, whose extraction steps
+//    cost twice as much; callers whose rows rarely finish in few steps pass
+//    fewer);
 //  * bisection: the cut value theta = x_(k*) is the largest t with
 //    sum_{x >= t} x >= gamma * T, found by bisection over the bit patterns of
 //    non-negative floats (ordered like the values); everything above theta
@@ -81,7 +82,7 @@ constexpr int kGreedySteps = 24;
 // so the selection does not depend on which VPL serves a row.
 // wave_select_vals takes the values already in registers: v[k] = element lane + 64 k, or -1 for
 // the slots past n.
-template <int VPL>
+template <int VPL, int GS = (VPL > 16 ? kGreedySteps / 2 : kGreedySteps)>
 __device__ __forceinline__ void wave_select_vals(const float (&v)[VPL], int n, float gamma, uint32_t *words) {
   static_assert(VPL >= 1 && VPL <= 32, "one bit of `taken` per slot");
   const int lane = threadIdx.x & 63;
@@ -102,7 +103,7 @@ __device__ __forceinline__ void wave_select_vals(const float (&v)[VPL], int n, f
     return;
   }
   // greedy extraction
-  constexpr int steps = VPL > 16 ? kGreedySteps / 2 : kGreedySteps;
+  constexpr int steps = GS;
   uint32_t taken = 0u;
   float cum = 0.0f;
   bool done = false;
