@@ -515,7 +515,8 @@ __global__ void __launch_bounds__(kMergeThreads) k_ig_rows(MergeArgs a) {
     if (row < a.Hq * B) {
       const int h = row / B, r = row % B;
       const float2 *p = a.ml + (size_t)h * a.nch * B + r;
-#pragma unroll 4
+      // (loads of up to 32 chunk pairs in flight: 8.3 -> 6.3 us at 128K against 4)
+#pragma unroll 32
       for (int c = part; c < a.nch; c += kRowSplit) {
         const float2 v = p[(size_t)c * B];
         const float Mn = fmaxf(M, v.x);
