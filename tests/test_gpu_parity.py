@@ -417,6 +417,40 @@ def test_batch_long_run_matches_single_calls():
             assert torch.equal(x.view(torch.int16), y.view(torch.int16)), s_
 
 
+@pytest.mark.parametrize("b,Hq,Hkv,lens", [
+    (64, 4, 2, [16384, 16384, 2048]),           # a run at the folding limit of 256 key blocks
+    (64, 6, 2, [16448, 16448, 1024, 1024]),     # 257 blocks go one at a time, then a run of two
+    (256, 8, 8, [4096, 4096, 4096]),            # G = 1
+    (128, 16, 1, [2048, 2048]),                 # G = 16, G * b = 2048
+], ids=["b64-limit", "b64-over-limit", "b256-G1", "b128-G16"])
+def test_batch_runs_at_other_shapes_match_single_calls(b, Hq, Hkv, lens):
+    """Folded runs at 64- and 256-token blocks, at the 256-block folding limit and one block past
+    it, and with one and sixteen query heads per KV head: every index and attention output equals
+    a call of its own, bit for bit."""
+    say(f"batch vs single calls: b = {b}, Hq = {Hq}, Hkv = {Hkv}, S = {lens}")
+    cs = [cfg(S=S, b=b, Hq=Hq, Hkv=Hkv) for S in lens]
+    Ls = [gen.make(c, seed=70 + k) for k, c in enumerate(cs)]
+    c0 = cs[0]
+    singles, Os = [], []
+    for c, L in zip(cs, Ls):
+        Qd, Kd, Vd = P.layer_on_device(L)
+        ix = fpa.index(Qd, Kd, c.b, c.gamma, c.tau, stats=True)
+        singles.append(ix)
+        Os.append(fpa.attn(Qd, Kd, Vd, ix))
+    pack = lambda name: torch.cat([P.dev_bf16(getattr(L, name), "cuda").reshape(-1) for L in Ls])
+    Q, K, V = pack("q"), pack("k"), pack("v")
+    idxs = fpa.index_batch(Q, K, lens, b, Hq, Hkv, c0.gamma, c0.tau, stats=True)
+    O = fpa.attn_batch(Q, K, V, lens, idxs)
+    O2 = fpa.attn_batch(Q, K, V, lens, singles)
+    torch.cuda.synchronize()
+    for a, b_ in zip(idxs, singles):
+        assert int(a.status.item()) == 0
+        _index_equal(a, b_)
+    for Ob in (O, O2):
+        for s_, (x, y) in enumerate(zip(fpa.unpack(Ob, lens, Hq), Os)):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), s_
+
+
 def test_batch_run_keeps_each_sequences_capacity():
     """One sequence of a run of equal lengths with a column capacity too small for its rows: its
     status word reports the overflow and its outputs equal those of a call of its own with that
