@@ -295,7 +295,9 @@ int fp_block_uses(const fp_shape *shape, const fp_index_out *jobs, int32_t *uses
  *   O: device bf16 [Hq, S, d], every element written.
  * For query token t of block i of head h: O[h,t] = sum over keys k <= t whose
  * block is in J(h,i) of softmax_k(sigma * Q[h,t] . K[g,k]) * V[g,k]; fp32
- * softmax and accumulation, one rounding to bf16 at the end.
+ * softmax and accumulation, one rounding to bf16 at the end.  fp_index always
+ * keeps block i; a row of a caller's CSR (fp_build_jobs) may leave it out, and
+ * an empty row, which has no keys to attend to, gives O = 0 for its block.
  * Errors: FP_EINVAL, FP_EUNSUPPORTED, FP_EWORKSPACE, FP_EHIP.
  */
 int fp_attn(const fp_shape *shape, const void *Q, const void *K, const void *V,

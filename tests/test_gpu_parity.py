@@ -145,6 +145,62 @@ def test_attn_gamma_one_is_dense_causal():
     assert mx <= MAXABS and rms <= RMS, (mx, rms)
 
 
+def _irregular_csr(c, seed):
+    """Random causal rows: about 15% empty, 25% without their diagonal block, the rest random
+    subsets that keep it; entry counts odd and even."""
+    rng = np.random.default_rng(seed)
+    N = c.N
+    rp = np.zeros(c.Hq * N + 1, dtype=np.int32)
+    cols, empty = [], []
+    for h in range(c.Hq):
+        for i in range(N):
+            u = rng.random()
+            if u < 0.15:
+                sel = []
+            elif u < 0.40 and i > 0:
+                sel = sorted(rng.choice(i, size=int(rng.integers(1, i + 1)), replace=False).tolist())
+            else:
+                sel = sorted(set(rng.choice(i + 1, size=int(rng.integers(1, i + 2)), replace=False).tolist()) | {i})
+            if not sel:
+                empty.append((h, i))
+            cols.extend(sel)
+            rp[h * N + i + 1] = len(cols)
+    return rp, np.array(cols, dtype=np.int32), empty
+
+
+@pytest.mark.parametrize("b,Hq,Hkv", [(128, 6, 2), (64, 6, 2), (256, 4, 2)], ids=["b128-G3", "b64-G3", "b256-G2"])
+def test_attn_on_irregular_csr(b, Hq, Hkv):
+    """A caller's CSR through fp_build_jobs with empty rows (also beside heads of the same group
+    that have entries), rows without their diagonal block and odd entry counts (single-block
+    chunks at b = 64): rows with entries match the oracle, and an empty row's output is zero,
+    as fp_attn defines it."""
+    say(f"attn on an irregular CSR b={b} Hq={Hq} Hkv={Hkv}")
+    c = cfg(S=2048, b=b, Hq=Hq, Hkv=Hkv)
+    L = gen.make(c, seed=5)
+    rp, ci, empty = _irregular_csr(c, 7)
+    assert empty
+    sh = fpa.shape_of(c.S, c.b, c.Hq, c.Hkv)
+    idx = fpa.build_jobs(sh, P.dev(rp), P.dev(ci))
+    torch.cuda.synchronize()
+    assert int(idx.status.item()) == 0
+    P.check_jobs(idx, c.G)
+    Qd, Kd, Vd = P.layer_on_device(L)
+    O = fpa.attn(Qd, Kd, Vd, idx)
+    torch.cuda.synchronize()
+    Q, K, V = L.f32("q"), L.f32("k"), L.f32("v")
+    rows = [(h, i) for h in range(c.Hq) for i in range(c.N) if (h, i) not in set(empty)]
+    res = oracle.attn.attn(Q, K, V, rp, ci, c.b, rows=rows)
+    Oref = np.zeros((c.Hq, c.S, c.d))
+    for (h, i), o in res.items():
+        Oref[h, i * c.b:(i + 1) * c.b] = o
+    Of = O.float().cpu()
+    for h, i in empty:
+        assert torch.count_nonzero(Of[h, i * c.b:(i + 1) * c.b]) == 0, (h, i)
+    mx, rms = P.attn_errors(O, Oref)
+    say(f"  maxabs={mx:.3e} rms={rms:.3e}, {len(empty)} empty rows")
+    assert mx <= MAXABS and rms <= RMS, (mx, rms)
+
+
 @pytest.mark.parametrize("b,Hq,Hkv", [(128, 2, 2), (128, 4, 2), (128, 6, 2), (64, 4, 2), (64, 6, 2)],
                          ids=["G1", "G2", "G3", "b64-G2", "b64-G3"])
 def test_attn_score_spike(b, Hq, Hkv):
