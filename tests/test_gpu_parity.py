@@ -168,13 +168,14 @@ def _irregular_csr(c, seed):
     return rp, np.array(cols, dtype=np.int32), empty
 
 
+@pytest.mark.parametrize("i8", [False, True], ids=["bf16", "i8"])
 @pytest.mark.parametrize("b,Hq,Hkv", [(128, 6, 2), (64, 6, 2), (256, 4, 2)], ids=["b128-G3", "b64-G3", "b256-G2"])
-def test_attn_on_irregular_csr(b, Hq, Hkv):
+def test_attn_on_irregular_csr(b, Hq, Hkv, i8):
     """A caller's CSR through fp_build_jobs with empty rows (also beside heads of the same group
     that have entries), rows without their diagonal block and odd entry counts (single-block
     chunks at b = 64): rows with entries match the oracle, and an empty row's output is zero,
     as fp_attn defines it."""
-    say(f"attn on an irregular CSR b={b} Hq={Hq} Hkv={Hkv}")
+    say(f"attn on an irregular CSR b={b} Hq={Hq} Hkv={Hkv} {'i8' if i8 else 'bf16'}")
     c = cfg(S=2048, b=b, Hq=Hq, Hkv=Hkv)
     L = gen.make(c, seed=5)
     rp, ci, empty = _irregular_csr(c, 7)
@@ -184,12 +185,18 @@ def test_attn_on_irregular_csr(b, Hq, Hkv):
     torch.cuda.synchronize()
     assert int(idx.status.item()) == 0
     P.check_jobs(idx, c.G)
-    Qd, Kd, Vd = P.layer_on_device(L)
-    O = fpa.attn(Qd, Kd, Vd, idx)
-    torch.cuda.synchronize()
-    Q, K, V = L.f32("q"), L.f32("k"), L.f32("v")
     rows = [(h, i) for h in range(c.Hq) for i in range(c.N) if (h, i) not in set(empty)]
-    res = oracle.attn.attn(Q, K, V, rp, ci, c.b, rows=rows)
+    if i8:
+        t = P.layer_i8_on_device(L)
+        O = fpa.attn_i8(t["q8"], t["sq"], t["k8"], t["sk"], t["v8"], t["sv"], idx)
+        d = L.int8()
+        res = oracle.attn.attn_i8(d["q8"], d["sq"], d["k8"], d["sk"], d["v8"], d["sv"], rp, ci, c.b, rows=rows)
+    else:
+        Qd, Kd, Vd = P.layer_on_device(L)
+        O = fpa.attn(Qd, Kd, Vd, idx)
+        Q, K, V = L.f32("q"), L.f32("k"), L.f32("v")
+        res = oracle.attn.attn(Q, K, V, rp, ci, c.b, rows=rows)
+    torch.cuda.synchronize()
     Oref = np.zeros((c.Hq, c.S, c.d))
     for (h, i), o in res.items():
         Oref[h, i * c.b:(i + 1) * c.b] = o
